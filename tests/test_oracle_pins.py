@@ -1,0 +1,322 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: hand-worked
+examples (tests/golden/*.txt), closed forms, exact invariants, special cases
+that reduce to plain sums, and brute force with numpy on tiny shapes.  Each is
+chosen so that a plausible slip (a dropped term, a wrong rounding mode, a
+wrong bit position, a transposed operand) fails at least one of them.
+
+Pages: "BitNet Embeddings GGUF Conversion Implementation" s1, s3, s4.5;
+"BitNet Inference Framework", "Quantization and Encoding", "Data Layout",
+"Quantization (W1.58A8)"; "gguf-gemv", "Requirements".
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import read_golden
+from ternary_weight_amd import inputs
+
+
+def _w1():
+    g = read_golden("i2s_w1.txt")
+    period = np.array([float(v) for v in g["period"]], dtype=np.float32)
+    row0 = np.tile(period, 16)
+    return np.stack([row0, -row0]), g
+
+
+def _fields(packed_codes: np.ndarray) -> np.ndarray:
+    """All 2-bit fields of a byte array, most significant first."""
+    b = packed_codes.astype(np.uint8)
+    return np.stack([(b >> 6) & 3, (b >> 4) & 3, (b >> 2) & 3, b & 3], axis=-1)
+
+
+# ---------------------------------------------------------------- packing ---
+
+def test_w1_worked_example_bytes():
+    W, g = _w1()
+    packed, scale = oracle.i2s_pack(W)
+    assert scale == float(g["scale"][0])
+    assert len(packed) == int(g["total_bytes"][0])
+    row0 = bytes.fromhex("".join(g["row0_period_bytes"])) * 4
+    row1 = bytes.fromhex("".join(g["row1_period_bytes"])) * 4
+    assert packed[:32].tobytes() == row0
+    assert packed[32:64].tobytes() == row1
+    assert packed[64:].tobytes() == bytes.fromhex("".join(g["tail_bytes"]))
+    # The other in-block order would start differently.
+    assert packed[:2].tobytes() != bytes.fromhex("".join(g["contiguous_order_row0_first_bytes"]))
+
+
+@pytest.mark.parametrize("p", range(128))
+def test_one_hot_family(p):
+    # One weight of 1, the rest 0: mean|w| = 1/128, scale = 128; the hot
+    # element gets code 2, all others code 1 (byte 0x55).  The hot field sits
+    # in byte p % 32 at field p // 32 (c0 = bits 7:6 ... c3 = bits 1:0).
+    w = np.zeros((1, 128), dtype=np.float32)
+    w[0, p] = 1.0
+    packed, scale = oracle.i2s_pack(w)
+    assert scale == 128.0
+    expect = np.full(32, 0x55, dtype=np.uint8)
+    expect[p % 32] = (0x95, 0x65, 0x59, 0x56)[p // 32]
+    assert np.array_equal(packed[:32], expect)
+    assert packed[32:].tobytes() == bytes([0x00, 0x00, 0x00, 0x43])
+
+
+def test_block_and_row_placement():
+    # One-hot at (n, k) in a multi-block, multi-row tensor: the hot byte is at
+    # n*K/4 + (k//128)*32 + k%32.
+    N, K = 3, 384
+    for n, k in [(0, 0), (1, 200), (2, 383), (2, 128 + 95)]:
+        w = np.zeros((N, K), dtype=np.float32)
+        w[n, k] = -3.0
+        packed, scale = oracle.i2s_pack(w)
+        assert scale == np.float32(1.0 / (3.0 / (N * K)))
+        hot = n * K // 4 + (k // 128) * 32 + k % 32
+        fields = _fields(packed[: N * K // 4])
+        assert fields[hot, (k % 128) // 32] == 0  # -1 -> code 0
+        mask = np.ones_like(fields, dtype=bool)
+        mask[hot, (k % 128) // 32] = False
+        assert np.all(fields[mask] == 1)
+
+
+def test_all_zero_weight():
+    packed, scale = oracle.i2s_pack(np.zeros((4, 256), dtype=np.float32))
+    assert scale == 1.0
+    assert np.all(packed[:-4] == 0x55)
+
+
+def test_negation_swaps_codes_keeps_scale():
+    W = inputs.weight(9, 0, 0, 16, 512)
+    p1, s1 = oracle.i2s_pack(W)
+    p2, s2 = oracle.i2s_pack(-W)
+    assert s1 == s2
+    assert np.array_equal(_fields(p2[:-4]), 2 - _fields(p1[:-4]))
+
+
+@pytest.mark.parametrize("e", [-3, 1, 5])
+def test_power_of_two_scaling(e):
+    W = inputs.weight(9, 0, 1, 8, 256)
+    p1, s1 = oracle.i2s_pack(W)
+    p2, s2 = oracle.i2s_pack(W * np.float32(2.0 ** e))
+    assert np.array_equal(p1[:-4], p2[:-4])
+    assert s2 == s1 * 2.0 ** (-e)
+
+
+def test_round_trip_and_no_code3():
+    W = inputs.weight(9, 1, 0, 24, 640)
+    packed, scale = oracle.i2s_pack(W)
+    assert not np.any(_fields(packed[:-4]) == 3)
+    q, s = oracle.i2s_unpack(packed, 640, 24)
+    assert s == scale
+    assert set(np.unique(q)) <= {-1, 0, 1}
+    # Independent numpy decision (f32 multiply by the stored scale, half-even).
+    expect = np.clip(np.rint(W * np.float32(scale)), -1, 1).astype(np.int8)
+    assert np.array_equal(q, expect)
+
+
+def test_zero_fraction_matches_closed_form():
+    # For W ~ N(0, s^2) the zero code fraction is P(|z| < 0.5*sqrt(2/pi)),
+    # i.e. erf(1/(2*sqrt(pi))) ~= 0.31006, independent of s.
+    W = inputs.weight(9, 2, 0, 1024, 1024)
+    packed, _ = oracle.i2s_pack(W)
+    f = _fields(packed[:-4]).ravel()
+    zero = np.mean(f == 1)
+    assert abs(zero - math.erf(1 / (2 * math.sqrt(math.pi)))) < 0.0015
+    assert abs(np.mean(f == 0) - np.mean(f == 2)) < 0.003
+
+
+def test_pack_rejects_bad_input():
+    with pytest.raises(oracle.OracleError):
+        oracle.i2s_pack(np.zeros((2, 100), dtype=np.float32))
+    w = np.ones((1, 128), dtype=np.float32)
+    w[0, 5] = np.inf
+    with pytest.raises(oracle.OracleError):
+        oracle.i2s_pack(w)
+
+
+def test_unpack_rejects_code3():
+    packed = np.full(36, 0x55, dtype=np.uint8)
+    packed[7] = 0x57  # field c3 = 3
+    with pytest.raises(oracle.OracleError):
+        oracle.i2s_unpack(packed, 128, 1)
+
+
+# ----------------------------------------------------------- quantization ---
+
+def _x1():
+    g = read_golden("quant_x1.txt")
+    x = np.tile(np.array([1, -1], dtype=np.float32), 64)[None, :]
+    nw = np.tile(np.array([float(v) for v in g["norm_period"]], dtype=np.float32), 16)
+    return x, nw, g
+
+
+def test_x1_worked_example():
+    x, nw, g = _x1()
+    q, factor = oracle.quant(x, nw, 0.0)
+    assert np.array_equal(q[0], np.tile(np.array([int(v) for v in g["q_period"]]), 16))
+    assert factor[0] == float(g["factor"][0])
+
+
+def test_constant_row_closed_form():
+    # x = c everywhere, norm_w = 1: mean(x^2) = c^2, xhat = c/sqrt(c^2+eps) for
+    # every k, so every code is sign(c)*127 and factor = |c|/(127*sqrt(c^2+eps)).
+    # c = 1, eps = 3 gives factor exactly 1/254: catches eps outside the root,
+    # sum instead of mean, or a missing norm.
+    K = 256
+    q, f = oracle.quant(np.ones((1, K), np.float32), np.ones(K, np.float32), 3.0)
+    assert np.all(q == 127) and f[0] == 1.0 / 254.0
+    q, f = oracle.quant(np.full((1, K), -2.0, np.float32), np.ones(K, np.float32), 0.0)
+    assert np.all(q == -127) and f[0] == 1.0 / 127.0
+
+
+def test_absmax_taken_after_norm_weight():
+    # x = 1, norm_w = [2, 1, 1, ...], eps = 0: xhat = [2, 1, ...], absmax 2,
+    # codes 127 and 63.5 -> 64 (half to even); factor = 2/127.
+    K = 128
+    nw = np.ones(K, np.float32)
+    nw[0] = 2.0
+    q, f = oracle.quant(np.ones((1, K), np.float32), nw, 0.0)
+    assert q[0, 0] == 127 and np.all(q[0, 1:] == 64)
+    assert f[0] == 2.0 / 127.0
+
+
+def test_zero_row():
+    x = inputs.activations(9, 0, 0, 3, 128)
+    x[1] = 0.0
+    q, f = oracle.quant(x, inputs.norm_weight(9, 0, 0, 128), 1e-6)
+    assert np.all(q[1] == 0) and f[1] == 0.0
+    assert f[0] > 0 and f[2] > 0
+
+
+def test_quant_rounding_bound_and_peak():
+    M, K = 6, 1024
+    x = inputs.activations(9, 0, 1, M, K)
+    nw = inputs.norm_weight(9, 0, 1, K)
+    q, f = oracle.quant(x, nw, 1e-6)
+    # Independent double-precision normalisation for the bound check.
+    xd = x.astype(np.float64)
+    xhat = xd / np.sqrt(np.mean(xd * xd, axis=1, keepdims=True) + 1e-6) * nw.astype(np.float64)
+    step = f[:, None]  # = absmax/127: the quantization step
+    assert np.all(np.abs(xhat - q * step) <= 0.5 * step * (1 + 1e-12))
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    assert np.array_equal(np.abs(q).argmax(axis=1), np.abs(xhat).argmax(axis=1))
+    assert np.allclose(f, np.abs(xhat).max(axis=1) / 127, rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("e", [-4, 3])
+def test_quant_scale_invariance(e):
+    # RMSNorm removes a power-of-two scale of x exactly (eps = 0); scaling
+    # norm_w by 2^e keeps the codes and multiplies the factor by 2^e.
+    M, K = 4, 512
+    x = inputs.activations(9, 1, 0, M, K)
+    nw = inputs.norm_weight(9, 1, 0, K)
+    q0, f0 = oracle.quant(x, nw, 0.0)
+    q1, f1 = oracle.quant(x * np.float32(2.0 ** e), nw, 0.0)
+    assert np.array_equal(q0, q1) and np.array_equal(f0, f1)
+    q2, f2 = oracle.quant(x, nw * np.float32(2.0 ** e), 0.0)
+    assert np.array_equal(q0, q2) and np.array_equal(f2, f0 * 2.0 ** e)
+
+
+# ------------------------------------------------------- integer product ---
+
+def test_w1_x1_accumulator_and_output():
+    W, _ = _w1()
+    x, nw, g = _x1()
+    packed, scale = oracle.i2s_pack(W)
+    q, f = oracle.quant(x, nw, 0.0)
+    acc = oracle.matmul_i32(q, packed, 128, 2)
+    assert acc.tolist() == [[int(v) for v in g["acc"]]]
+    # Row-sum identity: sum q*code - sum q equals the ternary product.
+    codes = oracle.i2s_unpack(packed, 128, 2)[0].astype(np.int64) + 1
+    assert int(q[0].astype(np.int64) @ codes[0]) - int(q[0].astype(np.int64).sum()) == acc[0, 0]
+    y = oracle.epilogue(acc, f, scale)
+    assert y.tolist() == [[float(v) for v in g["y"]]]
+    assert oracle.bitlinear(x, nw, packed, 2, 0.0).tolist() == [[float(v) for v in g["y"]]]
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (3, 256, 5), (4, 128, 8), (2, 384, 3)])
+def test_matmul_brute_force(M, K, N):
+    W = inputs.weight(9, 3, N, N, K)
+    packed, _ = oracle.i2s_pack(W)
+    qw, _ = oracle.i2s_unpack(packed, K, N)
+    xq = inputs.rng(9, 3, N, 7).integers(-127, 128, size=(M, K)).astype(np.int8)
+    acc = oracle.matmul_i32(xq, packed, K, N)
+    assert np.array_equal(acc, xq.astype(np.int64) @ qw.astype(np.int64).T)
+
+
+def test_matmul_special_cases():
+    K = 256
+    xq = inputs.rng(9, 4, 0, 7).integers(-127, 128, size=(5, K)).astype(np.int8)
+    # All-(+1) weights: the product is the row sum of the activations.
+    packed, scale = oracle.i2s_pack(np.ones((2, K), np.float32))
+    assert scale == 1.0
+    acc = oracle.matmul_i32(xq, packed, K, 2)
+    assert np.array_equal(acc[:, 0], xq.astype(np.int64).sum(axis=1))
+    # One-hot weight row: the product picks one activation column.
+    w = np.zeros((1, K), np.float32)
+    w[0, 77] = 0.5
+    packed, _ = oracle.i2s_pack(w)
+    assert np.array_equal(oracle.matmul_i32(xq, packed, K, 1)[:, 0], xq[:, 77])
+
+
+def test_matmul_extreme_magnitude():
+    # Largest possible |acc| at K = 1024: all codes 127 times all +1 weights.
+    K = 1024
+    xq = np.full((1, K), 127, np.int8)
+    packed, _ = oracle.i2s_pack(np.ones((1, K), np.float32))
+    assert oracle.matmul_i32(xq, packed, K, 1)[0, 0] == 127 * K
+
+
+# -------------------------------------------------------------- whole path ---
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 3), (4, 256, 8), (3, 384, 5)])
+def test_path_equals_float64_dequantized_product(M, K, N):
+    W = inputs.weight(9, 5, K, N, K)
+    x = inputs.activations(9, 5, K, M, K)
+    nw = inputs.norm_weight(9, 5, K, K)
+    packed, scale = oracle.i2s_pack(W)
+    y = oracle.bitlinear(x, nw, packed, N, 1e-6)
+    q, f = oracle.quant(x, nw, 1e-6)
+    qw, _ = oracle.i2s_unpack(packed, K, N)
+    ref = (q.astype(np.float64) * f[:, None]) @ (qw.astype(np.float64) / scale).T
+    assert np.allclose(y, ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 1e-7
+
+
+def test_grid_exact_case():
+    # x alternates +-1 (r = 1 at eps = 0) and norm_w holds integers with max
+    # 127, so xhat is already on the int8 grid (factor 1): the path must equal
+    # the float64 product of xhat with the dequantized weights.
+    K, N = 256, 6
+    x = np.tile(np.array([1, -1], np.float32), K // 2)[None, :]
+    nw = inputs.rng(9, 6, 0, 7).integers(0, 128, size=K).astype(np.float32)
+    nw[3] = 127.0
+    W = inputs.weight(9, 6, 0, N, K)
+    packed, scale = oracle.i2s_pack(W)
+    qw, _ = oracle.i2s_unpack(packed, K, N)
+    xhat = (x[0] * nw).astype(np.float64)
+    ref = (qw.astype(np.float64) @ xhat) / scale
+    y = oracle.bitlinear(x, nw, packed, N, 0.0)
+    assert np.allclose(y[0], ref.astype(np.float32), rtol=0, atol=0)
+
+
+def test_row_separability_and_weight_symmetries():
+    M, K, N = 9, 256, 12
+    x = inputs.activations(9, 7, 0, M, K)
+    nw = inputs.norm_weight(9, 7, 0, K)
+    W = inputs.weight(9, 7, 0, N, K)
+    packed, _ = oracle.i2s_pack(W)
+    y = oracle.bitlinear(x, nw, packed, N, 1e-6)
+    rows = [0, 4, 8, 4]
+    assert np.array_equal(oracle.bitlinear(x[rows], nw, packed, N, 1e-6), y[rows])
+    p_neg, _ = oracle.i2s_pack(-W)
+    assert np.array_equal(oracle.bitlinear(x, nw, p_neg, N, 1e-6), -y)
+    p_big, _ = oracle.i2s_pack(W * np.float32(8.0))
+    assert np.array_equal(oracle.bitlinear(x, nw, p_big, N, 1e-6), y * np.float32(8.0))
+
+
+def test_path_rejects_ragged_k():
+    assert oracle.packed_bytes(100, 4) == 0
+    assert oracle.packed_bytes(128, 4) == 4 * 32 + 4
