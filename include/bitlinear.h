@@ -1,0 +1,183 @@
+/*
+ * bitlinear.h — C ABI of libbitlinear.so: the BitLinear forward path with
+ * I2_S ternary weights on AMD Instinct MI355X (gfx950).
+ *
+ * The path, per projection ("BitNet Embeddings GGUF Conversion
+ * Implementation", s1 "Background" and s4.5 "load_tensors"):
+ *
+ *     y = ( Q8( RMSNorm(x) * norm_w ) x ternary(W)^T ) * (absmax/127) / w_scale
+ *
+ * RMSNorm(x) = x / sqrt(mean(x^2) + eps); Q8 is per-token absmax int8
+ * quantization ("BitNet Inference Framework", "Quantization (W1.58A8)");
+ * ternary(W) is the absmean ternary weight stored in I2_S ("BitNet Inference
+ * Framework", "Quantization and Encoding" and "Data Layout"); there is no bias
+ * ("BitNet Inference Framework", "Architectural Details").
+ *
+ * Conventions shared by every call:
+ *  - All functions are extern "C", never throw, and return bl_status
+ *    (0 = BL_OK, negative = error) unless stated otherwise.
+ *  - Every argument check runs on the host before any HIP call, so an error
+ *    return means nothing was enqueued.
+ *  - The caller owns every buffer passed in.  The library never frees caller
+ *    memory and never keeps a caller pointer after the call returns (group
+ *    handles excepted, see bl_group_create).
+ *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *    GPU calls only enqueue work on it and return without synchronising;
+ *    faults during execution surface at the caller's next synchronisation.
+ *  - Matrices are row-major.  x is [M][K] float32, y is [M][N] float32,
+ *    the weight is [N][K] (output x input) before packing.
+ *  - K must be a positive multiple of 128 (the I2_S block; "gguf-gemv",
+ *    "Requirements") and at most bl_k_max(); N >= 1; M >= 0 (M == 0 is a
+ *    no-op returning BL_OK).
+ *  - Device pointers must be 16-byte aligned.
+ *
+ * I2_S layout (the in-block order is a reading; the pages give only the byte
+ * formula):  row n of the weight occupies bytes [n*K/4, (n+1)*K/4).  Each
+ * 128-value block along K is 32 bytes; byte j (0..31) of block b holds the
+ * codes of elements 128b+j, 128b+32+j, 128b+64+j, 128b+96+j in bits 7:6, 5:4,
+ * 3:2 and 1:0.  Codes are 0, 1, 2 for -1, 0, +1.  The tensor-wide float32
+ * scale (1/mean|W|) follows at byte N*K/4, little-endian; dequantized
+ * w = (code - 1) / scale.
+ */
+#ifndef TERNARY_BITLINEAR_H
+#define TERNARY_BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bl_status;
+
+#define BL_OK 0
+#define BL_ERR_INVALID_ARGUMENT (-1) /* null pointer, bad size, eps < 0 or not finite, short buffer */
+#define BL_ERR_UNSUPPORTED (-2)      /* K % 128 != 0, K > bl_k_max(), or a size that overflows */
+#define BL_ERR_MISALIGNED (-3)       /* a device pointer not 16-byte aligned */
+#define BL_ERR_NONFINITE (-4)        /* non-finite weight given to i2s_pack */
+#define BL_ERR_HIP (-5)              /* the HIP runtime reported an error */
+#define BL_ERR_NOMEM (-6)            /* device or host allocation failed */
+#define BL_ERR_INTERNAL (-7)         /* unexpected internal failure */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* bl_status_string(bl_status s);
+
+/* Largest K the GPU calls accept. */
+int64_t bl_k_max(void);
+
+/* Size in bytes of an I2_S buffer for a [N][K] weight: N*K/4 + 4.
+ * Returns 0 if K <= 0, N <= 0, K % 128 != 0, or the size overflows. */
+size_t i2s_packed_bytes(int64_t K, int64_t N);
+
+/*
+ * i2s_pack — absmean ternary quantization and I2_S packing, on the HOST
+ * ("BitNet Embeddings GGUF Conversion Implementation", s3 "I2_S Ternary
+ * Packing"; "BitNet Inference Framework", "Quantization and Encoding",
+ * "Data Layout").
+ *   w            host, [N][K] float32, finite.
+ *   packed       host output, at least i2s_packed_bytes(K, N) bytes; fully
+ *                written (codes, then the scale).
+ *   packed_bytes size of the packed buffer.
+ *   w_scale_out  host output (may be NULL): the scale also stored at the tail.
+ * scale = (float)(1 / mean|w|) with the mean accumulated in double in memory
+ * order; code = clamp(rne((float)w * scale), -1, 1) + 1 with a float32
+ * multiply; an all-zero w gives scale 1 and all codes 1.
+ * Errors: BL_ERR_INVALID_ARGUMENT (nulls, short buffer), BL_ERR_UNSUPPORTED
+ * (K % 128), BL_ERR_NONFINITE (inf or NaN in w; packed left unspecified).
+ */
+bl_status i2s_pack(const float* w, int64_t K, int64_t N, uint8_t* packed, size_t packed_bytes,
+                   float* w_scale_out);
+
+/*
+ * bitlinear_forward — the whole path for one projection on the GPU
+ * ("BitNet Embeddings GGUF Conversion Implementation", s1 and s4.5;
+ * "BitNet Inference Framework", "Quantization (W1.58A8)").
+ *   x        device [M][K] float32.
+ *   norm_w   device [K] float32, the projection's norm weight, used as given.
+ *   packed_w device I2_S buffer of i2s_packed_bytes(K, N) bytes.
+ *   w_scale  the float32 scale stored at the tail of packed_w (passed by
+ *            value so that no device-to-host read is needed).
+ *   eps      RMSNorm epsilon, finite and >= 0.
+ *   y        device [M][N] float32 output, fully overwritten.
+ * Per row: codes = rne(x*norm_w * 127/max|x*norm_w|) (RMSNorm's scalar cancels
+ * in the codes), factor = max|RMSNorm(x)*norm_w| / 127, an all-zero row gives
+ * zero codes and factor 0; y = (sum_k code*ternary) * factor / w_scale.
+ * M <= 16 takes the weight-streaming decode kernel, larger M the tiled MFMA
+ * kernel; both share the same integer result.  Uses a library-owned
+ * workspace (M*K + 8*M bytes) per (device, stream); the workspace is grown
+ * with hipMalloc when needed, which is not allowed while the stream is being
+ * captured into a graph (BL_ERR_UNSUPPORTED).
+ */
+bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* packed_w,
+                            float w_scale, int64_t M, int64_t K, int64_t N, float eps, float* y,
+                            void* stream);
+
+/*
+ * bitlinear_quant — the first stage of bitlinear_forward alone (same kernel):
+ * fused RMSNorm + per-token absmax int8 quantization.
+ *   xq       device [M][K] int8 output, codes in [-127, 127].
+ *   x_factor device [M] float32 output, absmax/127 of the normalised row.
+ */
+bl_status bitlinear_quant(const float* x, const float* norm_w, int64_t M, int64_t K, float eps,
+                          int8_t* xq, float* x_factor, void* stream);
+
+/*
+ * bitlinear_matmul_i32 — the integer product of bitlinear_forward alone, on
+ * caller-supplied int8 activations, with the same main loops as the forward
+ * (M <= 16 decode kernel, else the MFMA kernel) and a raw int32 epilogue:
+ *   acc[m][n] = sum_k xq[m][k] * (code[n][k] - 1), exact.
+ *   xq  device [M][K] int8, values in [-127, 127].
+ *   acc device [M][N] int32 output.
+ * Uses the same library workspace as bitlinear_forward (8*M bytes).
+ */
+bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_t M, int64_t K,
+                               int64_t N, int32_t* acc, void* stream);
+
+/*
+ * Grouped execution: many independent projections (for example the seven of
+ * a layer, or of many layers) run as one launch per stage.  Results are
+ * bit-identical to separate bitlinear_forward calls on the same inputs.
+ */
+typedef struct bl_desc {
+    const float* x;          /* device [M][K] */
+    const float* norm_w;     /* device [K] */
+    const uint8_t* packed_w; /* device, I2_S */
+    float w_scale;
+    float eps;
+    int64_t M, K, N;
+    float* y;                /* device [M][N] */
+} bl_desc;
+
+typedef struct bl_group bl_group;
+
+/*
+ * bl_group_create — validates every descriptor (same rules as
+ * bitlinear_forward), copies the table to the current device, and allocates
+ * the group's own workspace and launch tables.  Blocking; may call hipMalloc.
+ * The group keeps the descriptors' device pointers: the caller keeps those
+ * buffers alive until bl_group_destroy.  Outputs must not alias each other or
+ * any input.  count >= 1.
+ */
+bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out);
+
+/* Both stages for every descriptor, enqueued on stream (quant, then matmul). */
+bl_status bl_group_forward(bl_group* g, void* stream);
+/* Stage 1 only: RMSNorm + int8 quantization of every descriptor's x into the
+ * group's workspace. */
+bl_status bl_group_quant(bl_group* g, void* stream);
+/* Stage 2 only: integer product + epilogue for every descriptor, reading the
+ * workspace written by the last bl_group_quant on the same stream. */
+bl_status bl_group_matmul(bl_group* g, void* stream);
+/* Frees the group (synchronises the device first). NULL is a no-op. */
+bl_status bl_group_destroy(bl_group* g);
+
+/* Frees the per-(device, stream) workspaces of bitlinear_forward and the
+ * hooks (synchronises the device first). */
+bl_status bl_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERNARY_BITLINEAR_H */

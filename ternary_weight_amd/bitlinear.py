@@ -1,0 +1,228 @@
+"""Python binding of libbitlinear.so (the C ABI declared in include/bitlinear.h).
+
+Argument marshalling only: torch tensors are checked for dtype, device and
+layout and passed as raw device pointers with the current HIP stream; every
+step of the path runs in the library's HIP kernels (or, for ``i2s_pack``, in
+its host C++).  Importing this module raises ImportError when the library has
+not been built: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m ternary_weight_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+BL_OK = 0
+BL_ERR_INVALID_ARGUMENT = -1
+BL_ERR_UNSUPPORTED = -2
+BL_ERR_MISALIGNED = -3
+BL_ERR_NONFINITE = -4
+BL_ERR_HIP = -5
+BL_ERR_NOMEM = -6
+BL_ERR_INTERNAL = -7
+
+_p, _i64, _f32, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32
+
+
+class BlDesc(ctypes.Structure):
+    """Mirror of ``bl_desc``."""
+    _fields_ = [("x", _p), ("norm_w", _p), ("packed_w", _p), ("w_scale", _f32), ("eps", _f32),
+                ("M", _i64), ("K", _i64), ("N", _i64), ("y", _p)]
+
+
+_SIGS = {
+    "bl_status_string": ([_i32], ctypes.c_char_p),
+    "bl_k_max": ([], _i64),
+    "i2s_packed_bytes": ([_i64, _i64], ctypes.c_size_t),
+    "i2s_pack": ([_p, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
+    "bitlinear_forward": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
+    "bitlinear_quant": ([_p, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
+    "bitlinear_matmul_i32": ([_p, _p, _i64, _i64, _i64, _p, _p], _i32),
+    "bl_group_create": ([ctypes.POINTER(BlDesc), _i32, ctypes.POINTER(_p)], _i32),
+    "bl_group_forward": ([_p, _p], _i32),
+    "bl_group_quant": ([_p, _p], _i32),
+    "bl_group_matmul": ([_p, _p], _i32),
+    "bl_group_destroy": ([_p], _i32),
+    "bl_release_workspace": ([], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+lib = _lib
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {bl_status_string(status)} ({status})")
+
+
+def bl_status_string(status: int) -> str:
+    return _lib.bl_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != BL_OK:
+        raise BitLinearError(status, what)
+
+
+def bl_k_max() -> int:
+    return int(_lib.bl_k_max())
+
+
+def i2s_packed_bytes(K: int, N: int) -> int:
+    return int(_lib.i2s_packed_bytes(K, N))
+
+
+def i2s_pack(w: np.ndarray) -> tuple[np.ndarray, float]:
+    """Host packing: float32 [N, K] -> (uint8 I2_S buffer, scale)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be [N, K]")
+    N, K = w.shape
+    nbytes = i2s_packed_bytes(K, N)
+    out = np.empty(max(nbytes, 1), dtype=np.uint8)
+    scale = ctypes.c_float(0.0)
+    _check(_lib.i2s_pack(w.ctypes.data, K, N, out.ctypes.data, nbytes, ctypes.byref(scale)),
+           "i2s_pack")
+    return out, float(scale.value)
+
+
+# ---------------------------------------------------------------- device ---
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> int | None:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t, dtype, name: str, shape=None) -> int:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def bitlinear_forward(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y=None,
+                      stream=None):
+    """y[M, N] (float32) = BitLinear(x[M, K]) on the GPU; returns y."""
+    torch = _torch()
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(_lib.bitlinear_forward(
+        _dev(x, torch.float32, "x"), _dev(norm_w, torch.float32, "norm_w", (K,)),
+        _dev(packed_w, torch.uint8, "packed_w"), w_scale, M, K, N, eps,
+        _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)), "bitlinear_forward")
+    return y
+
+
+def bitlinear_quant(x, norm_w, eps: float, xq=None, x_factor=None, stream=None):
+    """(int8 codes [M, K], float32 factor [M]) of the fused RMSNorm + quant kernel."""
+    torch = _torch()
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if x_factor is None:
+        x_factor = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(_lib.bitlinear_quant(
+        _dev(x, torch.float32, "x"), _dev(norm_w, torch.float32, "norm_w", (K,)), M, K, eps,
+        _dev(xq, torch.int8, "xq", (M, K)), _dev(x_factor, torch.float32, "x_factor", (M,)),
+        _stream_handle(stream)), "bitlinear_quant")
+    return xq, x_factor
+
+
+def bitlinear_matmul_i32(xq, packed_w, N: int, acc=None, stream=None):
+    """Exact int32 [M, N] product of int8 codes with the ternary weights."""
+    torch = _torch()
+    M, K = xq.shape
+    if acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    _check(_lib.bitlinear_matmul_i32(
+        _dev(xq, torch.int8, "xq"), _dev(packed_w, torch.uint8, "packed_w"), M, K, N,
+        _dev(acc, torch.int32, "acc", (M, N)), _stream_handle(stream)), "bitlinear_matmul_i32")
+    return acc
+
+
+class Group:
+    """Many independent projections run as one launch per stage.
+
+    ``items`` is a sequence of dicts with keys x, norm_w, packed_w, w_scale,
+    eps, N and y (torch tensors on the GPU where applicable).  The tensors are
+    kept referenced for the group's lifetime.
+    """
+
+    def __init__(self, items):
+        torch = _torch()
+        self._keep = []
+        descs = (BlDesc * len(items))()
+        for i, it in enumerate(items):
+            x, y = it["x"], it["y"]
+            M, K = x.shape
+            descs[i] = BlDesc(_dev(x, torch.float32, "x"),
+                              _dev(it["norm_w"], torch.float32, "norm_w", (K,)),
+                              _dev(it["packed_w"], torch.uint8, "packed_w"),
+                              float(it["w_scale"]), float(it["eps"]), M, K, int(it["N"]),
+                              _dev(y, torch.float32, "y", (M, int(it["N"]))))
+            self._keep.append(it)
+        handle = _p()
+        _check(_lib.bl_group_create(descs, len(items), ctypes.byref(handle)), "bl_group_create")
+        self._h = handle
+
+    def forward(self, stream=None) -> None:
+        _check(_lib.bl_group_forward(self._h, _stream_handle(stream)), "bl_group_forward")
+
+    def quant(self, stream=None) -> None:
+        _check(_lib.bl_group_quant(self._h, _stream_handle(stream)), "bl_group_quant")
+
+    def matmul(self, stream=None) -> None:
+        _check(_lib.bl_group_matmul(self._h, _stream_handle(stream)), "bl_group_matmul")
+
+    def close(self) -> None:
+        if self._h:
+            _check(_lib.bl_group_destroy(self._h), "bl_group_destroy")
+            self._h = _p()
+            self._keep = []
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            if self._h:
+                _lib.bl_group_destroy(self._h)
+        except Exception:
+            pass
+
+
+def bl_release_workspace() -> None:
+    _check(_lib.bl_release_workspace(), "bl_release_workspace")

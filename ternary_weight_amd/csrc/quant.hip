@@ -1,0 +1,206 @@
+// Stage 1 of the BitLinear path: per-projection RMSNorm fused with per-token
+// absmax int8 quantization ("BitNet Embeddings GGUF Conversion
+// Implementation", s1 "Background" and s4.5; "BitNet Inference Framework",
+// "Quantization (W1.58A8)").
+//
+// One wavefront owns one token row.  The row is read once from HBM with
+// coalesced 16-byte loads and kept in VGPRs (K <= 4096), Sum(x^2) and
+// max|x*norm_w| are reduced across the wave, and the int8 codes are written
+// with one coalesced dword per lane per 4 elements.
+//
+// The codes use the identity  xhat*127/max|xhat| = u*127/max|u|  with
+// u = x*norm_w, since RMSNorm multiplies the whole row by one positive scalar;
+// so the codes never see the rsqrt.  The norm only enters the factor
+// absmax(xhat)/127 = r*max|u|/127, computed in double from the fp32 partial
+// sums.  Bound: HBM, 4K bytes read + K bytes written per row (plus the norm
+// weight, an L2 hit).
+#include "kernels.hpp"
+
+namespace bl {
+
+__device__ __forceinline__ int code_f32(float u, float s) {
+  float v = rintf(u * s);  // half to even
+  v = fminf(fmaxf(v, -127.0f), 127.0f);
+  return static_cast<int>(v);
+}
+__device__ __forceinline__ int code_f64(float u, double s) {
+  double v = rint(static_cast<double>(u) * s);
+  v = fmin(fmax(v, -127.0), 127.0);
+  return static_cast<int>(v);
+}
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (static_cast<uint32_t>(a) & 0xffu) | ((static_cast<uint32_t>(b) & 0xffu) << 8) |
+         ((static_cast<uint32_t>(c) & 0xffu) << 16) | ((static_cast<uint32_t>(d) & 0xffu) << 24);
+}
+
+// Per-row finish shared by both variants: the factor and the row sum.
+__device__ __forceinline__ void finish_row(const Prob& P, int m, double ss, float amax, int rs,
+                                           int lane) {
+  rs = wave_sum(rs);
+  if (lane == 0) {
+    double r = 1.0 / sqrt(ss / static_cast<double>(P.K) + static_cast<double>(P.eps));
+    P.factor[m] = static_cast<float>(r * static_cast<double>(amax) / 127.0);
+    if (P.rowsum) P.rowsum[m] = rs;
+  }
+}
+
+// NC: float4 chunks per lane held in registers (K <= 256*NC).
+template <int NC>
+__global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= set.total) return;
+  int m;
+  const Prob& P = prob_at(set, find_prob(set, unit, &m));
+  const int nch = P.K >> 2;
+  const float4* xr = reinterpret_cast<const float4*>(P.x + static_cast<int64_t>(m) * P.K);
+  const float4* wr = reinterpret_cast<const float4*>(P.norm_w);
+
+  float4 u[NC];
+  float ss = 0.f, amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + kWave * i;
+    u[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nch) {
+      const float4 xv = xr[c];
+      const float4 wv = wr[c];
+      ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+      u[i] = make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(u[i].x), fabsf(u[i].y)),
+                               fmaxf(fabsf(u[i].z), fabsf(u[i].w))));
+    }
+  }
+  const double ssd = wave_sum(static_cast<double>(ss));
+  amax = wave_max(amax);
+
+  uint32_t* qrow = reinterpret_cast<uint32_t*>(P.xq + static_cast<int64_t>(m) * P.K);
+  int rs = 0;
+  if (amax > 0.f && amax >= 1e-30f) {
+    const float s = 127.0f / amax;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      if (c < nch) {
+        const int a = code_f32(u[i].x, s), b = code_f32(u[i].y, s);
+        const int cc = code_f32(u[i].z, s), d = code_f32(u[i].w, s);
+        rs += a + b + cc + d;
+        qrow[c] = pack4(a, b, cc, d);
+      }
+    }
+  } else if (amax > 0.f) {  // tiny row: 127/amax would overflow fp32
+    const double s = 127.0 / static_cast<double>(amax);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      if (c < nch) {
+        const int a = code_f64(u[i].x, s), b = code_f64(u[i].y, s);
+        const int cc = code_f64(u[i].z, s), d = code_f64(u[i].w, s);
+        rs += a + b + cc + d;
+        qrow[c] = pack4(a, b, cc, d);
+      }
+    }
+  } else {  // all-zero row: zero codes, factor 0
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      if (c < nch) qrow[c] = 0u;
+    }
+  }
+  finish_row(P, m, ssd, amax, rs, lane);
+}
+
+// Rows longer than the register budget: two streaming passes over the row.
+__global__ __launch_bounds__(256) void quant_stream_kernel(ProbSet set) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= set.total) return;
+  int m;
+  const Prob& P = prob_at(set, find_prob(set, unit, &m));
+  const int nch = P.K >> 2;
+  const float4* xr = reinterpret_cast<const float4*>(P.x + static_cast<int64_t>(m) * P.K);
+  const float4* wr = reinterpret_cast<const float4*>(P.norm_w);
+
+  double ss = 0.0;
+  float amax = 0.f;
+  for (int c = lane; c < nch; c += kWave) {
+    const float4 xv = xr[c];
+    const float4 wv = wr[c];
+    ss += static_cast<double>(xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xv.x * wv.x), fabsf(xv.y * wv.y)),
+                             fmaxf(fabsf(xv.z * wv.z), fabsf(xv.w * wv.w))));
+  }
+  ss = wave_sum(ss);
+  amax = wave_max(amax);
+
+  uint32_t* qrow = reinterpret_cast<uint32_t*>(P.xq + static_cast<int64_t>(m) * P.K);
+  int rs = 0;
+  const bool tiny = amax < 1e-30f;
+  const float s = amax > 0.f && !tiny ? 127.0f / amax : 0.f;
+  const double sd = amax > 0.f ? 127.0 / static_cast<double>(amax) : 0.0;
+  for (int c = lane; c < nch; c += kWave) {
+    const float4 xv = xr[c];
+    const float4 wv = wr[c];
+    const float4 u = make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
+    int a = 0, b = 0, cc = 0, d = 0;
+    if (amax > 0.f) {
+      if (!tiny) {
+        a = code_f32(u.x, s); b = code_f32(u.y, s); cc = code_f32(u.z, s); d = code_f32(u.w, s);
+      } else {
+        a = code_f64(u.x, sd); b = code_f64(u.y, sd); cc = code_f64(u.z, sd); d = code_f64(u.w, sd);
+      }
+    }
+    rs += a + b + cc + d;
+    qrow[c] = pack4(a, b, cc, d);
+  }
+  finish_row(P, m, ss, amax, rs, lane);
+}
+
+// Row sums of int8 codes supplied by the caller (raw-integer hook only).
+__global__ __launch_bounds__(256) void rowsum_kernel(Prob P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= P.M) return;
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(P.xq + static_cast<int64_t>(m) * P.K);
+  int rs = 0;
+  for (int c = lane; c < (P.K >> 2); c += kWave) {
+    const uint32_t d = row[c];
+    rs += static_cast<int8_t>(d & 0xff) + static_cast<int8_t>((d >> 8) & 0xff) +
+          static_cast<int8_t>((d >> 16) & 0xff) + static_cast<int8_t>(d >> 24);
+  }
+  rs = wave_sum(rs);
+  if (lane == 0) P.rowsum[m] = rs;
+}
+
+hipError_t launch_quant(const ProbSet& set, int max_k, hipStream_t stream) {
+  if (set.total <= 0) return hipSuccess;
+  const dim3 grid((set.total + 3) / 4), block(256);
+  const int nc = (max_k + 255) / 256;
+  if (max_k > kQuantRegK)
+    hipLaunchKernelGGL(quant_stream_kernel, grid, block, 0, stream, set);
+  else if (nc <= 1)
+    hipLaunchKernelGGL(quant_reg_kernel<1>, grid, block, 0, stream, set);
+  else if (nc <= 2)
+    hipLaunchKernelGGL(quant_reg_kernel<2>, grid, block, 0, stream, set);
+  else if (nc <= 3)
+    hipLaunchKernelGGL(quant_reg_kernel<3>, grid, block, 0, stream, set);
+  else if (nc <= 4)
+    hipLaunchKernelGGL(quant_reg_kernel<4>, grid, block, 0, stream, set);
+  else if (nc <= 6)
+    hipLaunchKernelGGL(quant_reg_kernel<6>, grid, block, 0, stream, set);
+  else if (nc <= 8)
+    hipLaunchKernelGGL(quant_reg_kernel<8>, grid, block, 0, stream, set);
+  else if (nc <= 12)
+    hipLaunchKernelGGL(quant_reg_kernel<12>, grid, block, 0, stream, set);
+  else
+    hipLaunchKernelGGL(quant_reg_kernel<16>, grid, block, 0, stream, set);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowsum(const Prob& p, hipStream_t stream) {
+  if (p.M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rowsum_kernel, dim3((p.M + 3) / 4), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace bl

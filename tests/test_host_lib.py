@@ -1,0 +1,164 @@
+"""Host-side checks of libbitlinear.so that need no GPU.
+
+* the library loads and exports every function include/bitlinear.h declares;
+* the host packer i2s_pack is byte-identical to the oracle's packing on the
+  hand-worked examples and on every projection shape of the workloads;
+* every invalid argument is rejected with the documented status code before
+  any HIP call (no call here passes a pointer that survives validation,
+  except with M == 0, which must return BL_OK without touching the device).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import ROOT
+from ternary_weight_amd import bitlinear as bl
+from ternary_weight_amd import inputs
+
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_symbols_exported():
+    names = _declared_functions()
+    assert "bitlinear_forward" in names and "i2s_pack" in names
+    lib = ctypes.CDLL(bl.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in bitlinear.h but not exported"
+    assert set(names) == set(bl.EXPORTED)
+
+
+def test_status_strings():
+    assert bl.bl_status_string(0) == "BL_OK"
+    assert bl.bl_status_string(-2) == "BL_ERR_UNSUPPORTED"
+    assert bl.bl_status_string(-99) == "BL_ERR_UNKNOWN"
+    assert bl.bl_k_max() >= 4096
+
+
+def test_packed_bytes():
+    assert bl.i2s_packed_bytes(1024, 3072) == 3072 * 256 + 4
+    assert bl.i2s_packed_bytes(100, 4) == 0
+    assert bl.i2s_packed_bytes(0, 4) == 0
+    assert bl.i2s_packed_bytes(128, 0) == 0
+
+
+def test_pack_matches_oracle_on_worked_examples():
+    pat = np.array([0.5, -0.5, 0.125, -0.125, 0.375, -0.0625, 0.1875, -0.125], np.float32)
+    W = np.stack([np.tile(pat, 16), -np.tile(pat, 16)])
+    assert np.array_equal(bl.i2s_pack(W)[0], oracle.i2s_pack(W)[0])
+    for p in (0, 31, 32, 95, 127):
+        w = np.zeros((1, 128), np.float32)
+        w[0, p] = 1.0
+        assert np.array_equal(bl.i2s_pack(w)[0], oracle.i2s_pack(w)[0])
+    z = np.zeros((3, 256), np.float32)
+    assert np.array_equal(bl.i2s_pack(z)[0], oracle.i2s_pack(z)[0])
+
+
+SHAPES = sorted({(N, K) for w in inputs.WORKLOADS.values() for (_, K, N) in w.projs})
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_pack_matches_oracle_on_workload_shapes(N, K):
+    W = inputs.weight(8, 0, K + N, N, K)
+    p_lib, s_lib = bl.i2s_pack(W)
+    p_ref, s_ref = oracle.i2s_pack(W)
+    assert s_lib == s_ref
+    assert np.array_equal(p_lib, p_ref)
+
+
+def test_pack_matches_oracle_multithreaded_and_ties():
+    # Large enough for the threaded path; values on exact .5 ties after
+    # scaling exercise half-to-even in both implementations.
+    N, K = 1024, 1280
+    W = inputs.weight(8, 1, 0, N, K)
+    W[::7, ::5] = 0.0
+    p_lib, s_lib = bl.i2s_pack(W)
+    p_ref, s_ref = oracle.i2s_pack(W)
+    assert s_lib == s_ref and np.array_equal(p_lib, p_ref)
+    ties = np.tile(np.array([0.5, -0.5, 1.5, -1.5, 2.5, 0.25, -0.25, 1.0], np.float32), 16)
+    W2 = np.stack([ties, ties * 2, -ties])
+    assert np.array_equal(bl.i2s_pack(W2)[0], oracle.i2s_pack(W2)[0])
+
+
+def test_pack_errors():
+    lib = bl.lib
+    w = np.ones((2, 128), np.float32)
+    out = np.zeros(2 * 32 + 4, np.uint8)
+    assert lib.i2s_pack(None, 128, 2, out.ctypes.data, out.size, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.i2s_pack(w.ctypes.data, 128, 2, None, out.size, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.i2s_pack(w.ctypes.data, 100, 2, out.ctypes.data, out.size, None) == bl.BL_ERR_UNSUPPORTED
+    assert lib.i2s_pack(w.ctypes.data, 128, 2, out.ctypes.data, out.size - 1, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.i2s_pack(w.ctypes.data, 128, 0, out.ctypes.data, out.size, None) == bl.BL_ERR_INVALID_ARGUMENT
+    w[1, 3] = np.nan
+    assert lib.i2s_pack(w.ctypes.data, 128, 2, out.ctypes.data, out.size, None) == bl.BL_ERR_NONFINITE
+    assert lib.i2s_pack(w.ctypes.data, 128, 2, out.ctypes.data, out.size, None) == bl.BL_ERR_NONFINITE
+
+
+# Fake device addresses: only ever used in calls that must fail validation
+# (or have M == 0, which returns before any HIP call).
+A, MIS = 0x10000, 0x10004
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, A, A, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # null x
+    ((A, 0, A, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # null norm_w
+    ((A, A, 0, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # null weights
+    ((A, A, A, 1.0, 4, 128, 8, 1e-6, 0), bl.BL_ERR_INVALID_ARGUMENT),        # null y
+    ((A, A, A, 1.0, -1, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),       # M < 0
+    ((A, A, A, 1.0, 4, 0, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),          # K = 0
+    ((A, A, A, 1.0, 4, 128, 0, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # N = 0
+    ((A, A, A, 1.0, 4, 192, 8, 1e-6, A), bl.BL_ERR_UNSUPPORTED),             # K % 128
+    ((A, A, A, 1.0, 4, 1 << 20, 8, 1e-6, A), bl.BL_ERR_UNSUPPORTED),         # K > K max
+    ((A, A, A, 1.0, 4, 128, 8, -1.0, A), bl.BL_ERR_INVALID_ARGUMENT),        # eps < 0
+    ((A, A, A, 1.0, 4, 128, 8, float("nan"), A), bl.BL_ERR_INVALID_ARGUMENT),
+    ((A, A, A, 0.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # scale 0
+    ((A, A, A, float("inf"), 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),
+    ((MIS, A, A, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_MISALIGNED),
+    ((A, MIS, A, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_MISALIGNED),
+    ((A, A, MIS, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_MISALIGNED),
+    ((A, A, A, 1.0, 4, 128, 8, 1e-6, MIS), bl.BL_ERR_MISALIGNED),
+    ((A, A, A, 1.0, 0, 128, 8, 1e-6, A), bl.BL_OK),                          # M = 0: no-op
+    ((0, A, A, 1.0, 0, 128, 8, 1e-6, 0), bl.BL_OK),                          # M = 0, no x/y
+])
+def test_forward_validation(args, code):
+    assert bl.lib.bitlinear_forward(*args, None) == code
+
+
+def test_quant_and_matmul_validation():
+    q, mm = bl.lib.bitlinear_quant, bl.lib.bitlinear_matmul_i32
+    assert q(0, A, 4, 128, 1e-6, A, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert q(A, A, 4, 100, 1e-6, A, A, None) == bl.BL_ERR_UNSUPPORTED
+    assert q(A, A, 4, 128, -1.0, A, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert q(A, A, 4, 128, 1e-6, MIS, A, None) == bl.BL_ERR_MISALIGNED
+    assert q(A, A, 4, 128, 1e-6, A, MIS, None) == bl.BL_ERR_MISALIGNED
+    assert q(A, A, 0, 128, 1e-6, A, A, None) == bl.BL_OK
+    assert mm(0, A, 4, 128, 8, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert mm(A, A, 4, 256 + 64, 8, A, None) == bl.BL_ERR_UNSUPPORTED
+    assert mm(A, MIS, 4, 128, 8, A, None) == bl.BL_ERR_MISALIGNED
+    assert mm(A, A, 4, 128, 8, MIS, None) == bl.BL_ERR_MISALIGNED
+    assert mm(A, A, 0, 128, 8, A, None) == bl.BL_OK
+
+
+def test_group_validation():
+    lib = bl.lib
+    h = ctypes.c_void_p()
+    d = (bl.BlDesc * 2)()
+    d[0] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, A)
+    d[1] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 200, 8, A)  # K % 128
+    assert lib.bl_group_create(d, 2, ctypes.byref(h)) == bl.BL_ERR_UNSUPPORTED
+    assert not h.value
+    d[1] = bl.BlDesc(A, A, MIS, 1.0, 1e-6, 4, 128, 8, A)
+    assert lib.bl_group_create(d, 2, ctypes.byref(h)) == bl.BL_ERR_MISALIGNED
+    assert lib.bl_group_create(d, 0, ctypes.byref(h)) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_group_create(d, 2, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_group_forward(None, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_group_destroy(None) == bl.BL_OK
