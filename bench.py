@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Throughput of the BitLinear forward path on one MI355X.
+
+Headline (the line's "value"): decode, M = 1, through the seven BitLinears of
+a Qwen3-0.6B-shaped layer (q 1024->2048, k/v 1024->1024, o 2048->1024,
+gate/up 1024->3072, down 3072->1024), in weight GB/s (packed I2_S bytes
+streamed per second).  One layer is 3.93 MB, far below a kernel launch and
+below the 256 MB MALL, so the step runs R distinct seeded copies of the layer
+(R * 3.93 MB >= 1 GiB) as one grouped launch per stage: the weights come from
+HBM, not from a cache, and launch latency is amortised.  A step is the whole
+path for every copy: fused RMSNorm + int8 quantization, then the ternary
+product with the scale epilogue.
+
+Secondary ("prefill"): the 28-layer Qwen3-0.6B projection stack at
+M = 16384 tokens (196 BitLinears, 14.4 T int8-equivalent operations), in
+int8-equivalent TOPS.
+
+Also reported: the dominant kernel's roofline fraction (HIP events around
+each launch in the timed region), and the plain CPU oracle timed on a
+bounded sample of the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-prefill] [--skip-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from ternary_weight_amd import inputs  # noqa: E402
+
+METRIC = "ternary GEMM int8-eq TOPS (prefill) + GEMV weight GB/s (M=1), Qwen3-0.6B shapes"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+DECODE_BYTES_TARGET = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--replicas", type=int, default=0, help="decode layer copies (0 = enough for 1 GiB)")
+    ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------ input prep ---
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def make_projections(workload: int, layers: int, projs, pack) -> list:
+    """Seeded weights and norm weights of every (layer, proj), packed; in parallel."""
+    def one(job):
+        layer, pi, K, N = job
+        packed, scale = pack(inputs.weight(workload, layer, pi, N, K))
+        return dict(layer=layer, proj=pi, K=K, N=N, packed=packed, scale=scale,
+                    norm_w=inputs.norm_weight(workload, layer, pi, K))
+    jobs = [(layer, pi, K, N) for layer in range(layers) for pi, (_, K, N) in enumerate(projs)]
+    with cf.ThreadPoolExecutor(_threads()) as ex:
+        return list(ex.map(one, jobs))
+
+
+class Arena:
+    """Sub-allocates 256-byte-aligned views from one device buffer."""
+
+    def __init__(self, torch, nbytes: int, device):
+        self.torch = torch
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.off = 0
+
+    @staticmethod
+    def size(nbytes: int) -> int:
+        return (nbytes + 255) // 256 * 256
+
+    def take(self, nbytes: int, dtype, shape):
+        view = self.buf[self.off:self.off + nbytes].view(dtype).view(shape)
+        self.off += self.size(nbytes)
+        return view
+
+
+# -------------------------------------------------------------- timing ---
+
+def run_timed(torch, group, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` steps; events bracket each stage."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        group.forward()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        group.quant()
+        e[1].record(stream)
+        group.matmul()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    quant_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    mm_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    return wall * 1e3 / steps, float(np.mean(quant_ms)), float(np.mean(mm_ms)), float(np.median(mm_ms))
+
+
+def traffic_from_profiles(kernel_tag: str, source: str):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, or None.
+
+    The summary names the kernel source's sha256; a changed kernel makes the
+    counters stale and the figure is dropped.
+    """
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b):
+        return None
+    src = open(os.path.join(ROOT, "ternary_weight_amd", "csrc", source), "rb").read()
+    if hashlib.sha256(src).hexdigest() != m_sha.group(1):
+        return None
+    return float(m_b.group(1))
+
+
+# ------------------------------------------------------------- workloads ---
+
+def bench_decode(torch, bl, args):
+    w = inputs.WORKLOADS[2]
+    layer_bytes = sum(N * K // 4 for _, K, N in w.projs)
+    R = args.replicas or math.ceil(DECODE_BYTES_TARGET / layer_bytes)
+    t0 = time.time()
+    projs = make_projections(2, R, w.projs, bl.i2s_pack)
+    log(f"decode: {len(projs)} BitLinears prepared in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda")
+    sz = Arena.size
+    total = sum(sz(len(p["packed"])) + sz(4 * p["K"]) * 2 + sz(4 * p["N"]) for p in projs)
+    arena = Arena(torch, total, dev)
+    items = []
+    for p in projs:
+        K, N = p["K"], p["N"]
+        pw = arena.take(len(p["packed"]), torch.uint8, (len(p["packed"]),))
+        pw.copy_(torch.from_numpy(p["packed"]))
+        nw = arena.take(4 * K, torch.float32, (K,))
+        nw.copy_(torch.from_numpy(p["norm_w"]))
+        x = arena.take(4 * K, torch.float32, (1, K))
+        x.copy_(torch.from_numpy(inputs.activations(2, p["layer"], p["proj"], 1, K)))
+        y = arena.take(4 * N, torch.float32, (1, N))
+        items.append(dict(x=x, norm_w=nw, packed_w=pw, w_scale=p["scale"], eps=inputs.EPS, N=N, y=y))
+    group = bl.Group(items)
+    ms, quant_ms, mm_ms, mm_med = run_timed(torch, group, args.steps, args.warmup)
+    group.close()
+    weight_bytes = sum(N * K // 4 for p in projs for K, N in [(p["K"], p["N"])])
+    # Algorithmic bytes of one decode-kernel launch: packed weights, int8
+    # activations, factor + row sum, fp32 outputs.
+    mm_bytes = sum(p["N"] * p["K"] // 4 + p["K"] + 8 + 4 * p["N"] for p in projs)
+    achieved = mm_bytes / (mm_ms * 1e-3) / 1e9
+    return dict(R=R, projs=projs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, mm_med=mm_med,
+                weight_bytes=weight_bytes, mm_bytes=mm_bytes, achieved=achieved,
+                value=weight_bytes / (ms * 1e-3) / 1e9)
+
+
+def bench_prefill(torch, bl, args):
+    w = inputs.WORKLOADS[4]
+    t0 = time.time()
+    projs = make_projections(4, w.layers, w.projs, bl.i2s_pack)
+    log(f"prefill: {len(projs)} BitLinears prepared in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda")
+    xs = {}
+    for _, K, _ in w.projs:
+        if K not in xs:
+            xs[K] = torch.from_numpy(inputs.activations(4, 0, K, w.M, K)).to(dev)
+    items = []
+    for p in projs:
+        items.append(dict(x=xs[p["K"]], norm_w=torch.from_numpy(p["norm_w"]).to(dev),
+                          packed_w=torch.from_numpy(p["packed"]).to(dev), w_scale=p["scale"],
+                          eps=inputs.EPS, N=p["N"],
+                          y=torch.empty((w.M, p["N"]), dtype=torch.float32, device=dev)))
+    group = bl.Group(items)
+    ms, quant_ms, mm_ms, mm_med = run_timed(torch, group, max(3, args.steps // 2), max(1, args.warmup // 2))
+    group.close()
+    ops = sum(2 * w.M * p["N"] * p["K"] for p in projs)
+    return dict(projs=projs, xs=xs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, ops=ops, M=w.M,
+                tops=ops / (ms * 1e-3) / 1e12, mm_tops=ops / (mm_ms * 1e-3) / 1e12)
+
+
+def cpu_baseline_decode(projs, seconds: float):
+    """The oracle, single-threaded, over the first BitLinears of the decode step."""
+    import oracle
+    done_bytes, t_used, n = 0, 0.0, 0
+    for p in projs:
+        x = inputs.activations(2, p["layer"], p["proj"], 1, p["K"])
+        t0 = time.perf_counter()
+        oracle.bitlinear(x, p["norm_w"], p["packed"], p["N"], inputs.EPS)
+        t_used += time.perf_counter() - t0
+        done_bytes += p["N"] * p["K"] // 4
+        n += 1
+        if t_used >= seconds:
+            break
+    return dict(value=done_bytes / t_used / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"first {n} of {len(projs)} M=1 BitLinears of the decode step "
+                       f"({done_bytes / 1e6:.0f} MB of packed weights, {t_used:.1f} s)")
+
+
+def cpu_baseline_prefill(pre, seconds: float):
+    """The oracle on sampled token rows of the prefill stack (rows are independent)."""
+    import oracle
+    rows = inputs.sample_rows(pre["M"], 2, seed=4)
+    xs_host = {K: x[torch_rows(x, rows)].cpu().numpy() for K, x in pre["xs"].items()}
+    ops, t_used, n = 0, 0.0, 0
+    for p in pre["projs"]:
+        t0 = time.perf_counter()
+        oracle.bitlinear(xs_host[p["K"]], p["norm_w"], p["packed"], p["N"], inputs.EPS)
+        t_used += time.perf_counter() - t0
+        ops += 2 * len(rows) * p["N"] * p["K"]
+        n += 1
+        if t_used >= seconds:
+            break
+    return dict(value=ops / t_used / 1e12, unit="TOPS", cores=1, kind="oracle",
+                sample=f"{len(rows)} sampled token rows through the first {n} of "
+                       f"{len(pre['projs'])} BitLinears ({t_used:.1f} s)")
+
+
+def torch_rows(x, rows):
+    import torch
+    return torch.as_tensor(rows, device=x.device)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards over token rows with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from ternary_weight_amd import bitlinear as bl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    dec = bench_decode(torch, bl, args)
+    log(f"decode: {dec['ms']:.3f} ms/step, {dec['value']:.0f} GB/s weights; "
+        f"quant {dec['quant_ms'] * 1e3:.1f} us, decode kernel {dec['mm_ms'] * 1e3:.1f} us "
+        f"({dec['achieved']:.0f} GB/s algorithmic)")
+    traffic = traffic_from_profiles("gemv_decode_qwen3", "gemv.hip")
+    out = {
+        "metric": METRIC,
+        "value": round(dec["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode M=1 through a Qwen3-0.6B-shaped layer (7 BitLinears), "
+                        f"{dec['R']} distinct seeded layer copies per step (>= 1 GiB of I2_S weights)",
+            "M": 1, "bitlinears": len(dec["projs"]), "layer_copies": dec["R"],
+            "weight_bytes": dec["weight_bytes"], "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "gemv_kernel (decode, M<=16)",
+            "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dec["mm_bytes"],
+            "avg_launch_us": round(dec["mm_ms"] * 1e3, 2),
+        },
+        "stages_us": {"quant": round(dec["quant_ms"] * 1e3, 2), "matmul": round(dec["mm_ms"] * 1e3, 2)},
+    }
+    if not args.skip_cpu:
+        out["cpu_baseline"] = cpu_baseline_decode(dec["projs"], args.cpu_seconds)
+    del dec
+
+    if not args.skip_prefill:
+        pre = bench_prefill(torch, bl, args)
+        log(f"prefill: {pre['ms']:.3f} ms/step, {pre['tops']:.1f} TOPS; MFMA kernel "
+            f"{pre['mm_ms']:.3f} ms ({pre['mm_tops']:.1f} TOPS), quant {pre['quant_ms']:.3f} ms")
+        pf = {
+            "workload": "prefill M=16384 through the 28-layer Qwen3-0.6B projection stack (196 BitLinears)",
+            "value": round(pre["tops"], 2), "unit": "TOPS (int8-equivalent)",
+            "ms_per_step": round(pre["ms"], 4),
+            "roofline": {
+                "bound": "mfma", "kernel": "gemm_kernel (prefill, M>16)",
+                "achieved": round(pre["mm_tops"], 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(pre["mm_tops"] / INT8_PEAK_TOPS, 4),
+                "traffic": traffic_from_profiles("gemm_prefill_qwen3", "gemm.hip"),
+                "algorithmic_ops_per_launch": pre["ops"],
+                "avg_launch_us": round(pre["mm_ms"] * 1e3, 1),
+            },
+            "stages_us": {"quant": round(pre["quant_ms"] * 1e3, 1), "matmul": round(pre["mm_ms"] * 1e3, 1)},
+        }
+        if not args.skip_cpu:
+            pf["cpu_baseline"] = cpu_baseline_prefill(pre, args.cpu_seconds / 2)
+        out["prefill"] = pf
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

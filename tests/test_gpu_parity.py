@@ -135,7 +135,7 @@ def test_matmul_i32_extremes(M):
     K, N = 2048, 96
     ones, _ = oracle.i2s_pack(np.ones((N, K), np.float32))
     xq = np.full((M, K), 127, np.int8)
-    xq[::2] = -127
+    xq[1::2] = -127
     acc = host(bl.bitlinear_matmul_i32(dev(xq), dev(ones), N))
     assert np.array_equal(acc, oracle.matmul_i32(xq, ones, K, N))
     assert acc[0, 0] == 127 * K and (M < 2 or acc[1, 0] == -127 * K)
