@@ -207,6 +207,40 @@ def bench_prefill(torch, bl, args):
                 tops=ops / (ms * 1e-3) / 1e12, mm_tops=ops / (mm_ms * 1e-3) / 1e12)
 
 
+def measure_peaks(torch, bl):
+    """Sustained HBM read / copy bandwidth and int8 MFMA rate of this GPU (probes)."""
+    dev = torch.device("cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    read = {}
+    for blocks in (2048, 4096, 8192, 16384):
+        read[blocks] = nbytes / timed(lambda: bl.probe_read(buf, sink, blocks)) / 1e9
+    half = nbytes // 2
+    src, dst = buf[:half], buf[half:]
+    copy = max(2 * half / timed(lambda: bl.probe_copy(src, dst, b)) / 1e9 for b in (4096, 16384))
+    del buf, src, dst
+    iters, blocks = 4000, 256 * 8
+    t = timed(lambda: bl.probe_mfma_i8(iters, blocks, sink), reps=3)
+    mfma = blocks * 4 * 4 * iters * 32768 / t / 1e12
+    return {"hbm_read_GBps": round(max(read.values()), 1),
+            "hbm_read_by_blocks": {str(k): round(v, 1) for k, v in read.items()},
+            "copy_GBps_read_plus_write": round(copy, 1), "mfma_i8_TOPS": round(mfma, 1)}
+
+
 def cpu_baseline_decode(projs, seconds: float):
     """The oracle, single-threaded, over the first BitLinears of the decode step."""
     import oracle
@@ -262,6 +296,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    peaks = measure_peaks(torch, bl)
+    log(f"measured peaks: {peaks}")
     dec = bench_decode(torch, bl, args)
     log(f"decode: {dec['ms']:.3f} ms/step, {dec['value']:.0f} GB/s weights; "
         f"quant {dec['quant_ms'] * 1e3:.1f} us, decode kernel {dec['mm_ms'] * 1e3:.1f} us "
@@ -295,7 +331,9 @@ def main():
             "avg_launch_us": round(dec["mm_ms"] * 1e3, 2),
         },
         "stages_us": {"quant": round(dec["quant_ms"] * 1e3, 2), "matmul": round(dec["mm_ms"] * 1e3, 2)},
+        "measured_peaks": peaks,
     }
+    out["roofline"]["frac_of_measured"] = round(dec["achieved"] / peaks["hbm_read_GBps"], 4)
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline_decode(dec["projs"], args.cpu_seconds)
     del dec
@@ -315,6 +353,7 @@ def main():
                 "traffic": traffic_from_profiles("gemm_prefill_qwen3", "gemm.hip"),
                 "algorithmic_ops_per_launch": pre["ops"],
                 "avg_launch_us": round(pre["mm_ms"] * 1e3, 1),
+                "frac_of_measured": round(pre["mm_tops"] / peaks["mfma_i8_TOPS"], 4),
             },
             "stages_us": {"quant": round(pre["quant_ms"] * 1e3, 1), "matmul": round(pre["mm_ms"] * 1e3, 1)},
         }

@@ -1,0 +1,41 @@
+/*
+ * bitlinear_probe.h — measurement probes exported by libbitlinear.so.
+ *
+ * Not part of the BitLinear computation: these kernels measure the GPU's own
+ * ceilings so that the BitLinear kernels' throughput can be quoted against
+ * both the published MI355X peaks and what the machine sustains.  Same
+ * conventions as bitlinear.h (status codes, void* stream, asynchronous).
+ */
+#ifndef TERNARY_BITLINEAR_PROBE_H
+#define TERNARY_BITLINEAR_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bitlinear.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Streaming read: every 16-byte word of buf (device, 16-byte aligned,
+ * bytes % 16 == 0) is loaded once by `blocks` workgroups of 256 threads,
+ * eight loads in flight per thread.  sink: device uint32, written only in a
+ * practically impossible case (it keeps the loads from being removed). */
+bl_status bl_probe_read(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
+                        void* stream);
+
+/* Device-to-device copy of `bytes` (16-byte aligned, bytes % 16 == 0) by
+ * `blocks` workgroups of 256 threads: exactly `bytes` read and written. */
+bl_status bl_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* stream);
+
+/* int8 matrix-core throughput: each of `blocks` workgroups of 4 waves runs
+ * 4*iters dependent-chain v_mfma_i32_16x16x64_i8 (32768 int8 operations
+ * each) per wave on register operands.  sink: device int32 (see above). */
+bl_status bl_probe_mfma_i8(int32_t iters, int32_t blocks, int32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERNARY_BITLINEAR_PROBE_H */

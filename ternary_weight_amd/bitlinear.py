@@ -53,6 +53,10 @@ _SIGS = {
     "bl_group_matmul": ([_p, _p], _i32),
     "bl_group_destroy": ([_p], _i32),
     "bl_release_workspace": ([], _i32),
+    # measurement probes (include/bitlinear_probe.h)
+    "bl_probe_read": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
+    "bl_probe_copy": ([_p, _p, ctypes.c_size_t, _i32, _p], _i32),
+    "bl_probe_mfma_i8": ([_i32, _i32, _p, _p], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -226,3 +230,25 @@ class Group:
 
 def bl_release_workspace() -> None:
     _check(_lib.bl_release_workspace(), "bl_release_workspace")
+
+
+def probe_read(buf, sink, blocks: int, stream=None) -> None:
+    """Streaming-read probe over a uint8 device tensor (see bitlinear_probe.h)."""
+    torch = _torch()
+    _check(_lib.bl_probe_read(_dev(buf, torch.uint8, "buf"), buf.numel(),
+                              _dev(sink, torch.int32, "sink"), blocks, _stream_handle(stream)),
+           "bl_probe_read")
+
+
+def probe_copy(src, dst, blocks: int, stream=None) -> None:
+    torch = _torch()
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst sizes differ")
+    _check(_lib.bl_probe_copy(_dev(src, torch.uint8, "src"), _dev(dst, torch.uint8, "dst"),
+                              src.numel(), blocks, _stream_handle(stream)), "bl_probe_copy")
+
+
+def probe_mfma_i8(iters: int, blocks: int, sink, stream=None) -> None:
+    torch = _torch()
+    _check(_lib.bl_probe_mfma_i8(iters, blocks, _dev(sink, torch.int32, "sink"),
+                                 _stream_handle(stream)), "bl_probe_mfma_i8")

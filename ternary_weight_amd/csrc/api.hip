@@ -3,6 +3,8 @@
 // any HIP call; every GPU call only enqueues work on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -27,6 +29,7 @@ bl_status check_shape(int64_t M, int64_t K, int64_t N) {
   if (K % 128 != 0 || K > kKMax) return BL_ERR_UNSUPPORTED;
   if (M > INT32_MAX - 256 || N > INT32_MAX - 256) return BL_ERR_UNSUPPORTED;
   if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BL_ERR_UNSUPPORTED;
+  if (N * (K / 4) > kMaxOffset || M * K > kMaxOffset) return BL_ERR_UNSUPPORTED;
   return BL_OK;
 }
 
@@ -102,11 +105,10 @@ bl_status acquire_ws(hipStream_t stream, size_t bytes, uint8_t** out) {
 inline bl_status from_hip(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
 ProbSet single_set(const Prob& p, int total) {
-  ProbSet s;
+  ProbSet s{};
   s.single = p;
   s.probs = nullptr;
-  s.starts = nullptr;
-  s.count = 0;
+  s.units = nullptr;
   s.total = total;
   return s;
 }
@@ -114,7 +116,13 @@ ProbSet single_set(const Prob& p, int total) {
 // Stage 2 for one problem: the decode kernel for M <= kGemvMaxM, else the
 // tiled MFMA kernel.
 hipError_t launch_matmul_single(const Prob& p, bool raw, hipStream_t stream) {
-  if (p.M <= kGemvMaxM) return launch_gemv(single_set(p, gemv_units(p.N)), raw, stream);
+  if (p.M <= kGemvMaxM) {
+    GemvLaunch L{};
+    L.single = p;
+    L.units = nullptr;
+    L.total = gemv_units(p.N, gemv_bucket(p.K));
+    return launch_gemv(L, raw, gemv_bucket(p.K), p.M, p.K, stream);
+  }
   return launch_gemm(single_set(p, gemm_units(p.M, p.N)), raw, stream);
 }
 
@@ -249,20 +257,22 @@ bl_status bl_release_workspace(void) {
 
 // ---------------------------------------------------------------- groups ---
 
+// One stage of a group: a device problem table and one (problem, local unit)
+// entry per workgroup.
+struct GroupStage {
+  const Prob* probs = nullptr;
+  const int2* units = nullptr;
+  const FatUnit* fat = nullptr;  // decode stages: problem records inline
+  int total = 0;
+  int max_m = 0, max_k = 0;
+};
+
 struct bl_group {
   int device = 0;
-  int count = 0;          // problems with M > 0
-  int max_k = 0;
-  int quant_total = 0, gemv_total = 0, gemm_total = 0;
-  int gemv_count = 0, gemm_count = 0;
-  void* tables = nullptr;     // device: all probs | gemv probs | gemm probs | 3 start arrays
+  GroupStage quant, gemm;
+  std::vector<std::pair<int, GroupStage>> gemv;  // one stage per superblock bucket
+  void* tables = nullptr;     // device: problem tables and unit tables
   void* workspace = nullptr;  // device: per-problem xq, factor, rowsum
-  const Prob* d_all = nullptr;
-  const Prob* d_gemv = nullptr;
-  const Prob* d_gemm = nullptr;
-  const int* d_quant_starts = nullptr;
-  const int* d_gemv_starts = nullptr;
-  const int* d_gemm_starts = nullptr;
 };
 
 namespace {
@@ -273,12 +283,11 @@ bl_status group_current_device(const bl_group* g) {
   return dev == g->device ? BL_OK : BL_ERR_INVALID_ARGUMENT;
 }
 
-ProbSet table_set(const Prob* probs, const int* starts, int count, int total) {
+ProbSet stage_set(const GroupStage& st) {
   ProbSet s{};
-  s.probs = probs;
-  s.starts = starts;
-  s.count = count;
-  s.total = total;
+  s.probs = st.probs;
+  s.units = st.units;
+  s.total = st.total;
   return s;
 }
 
@@ -289,6 +298,27 @@ void free_group(bl_group* g) {
   delete g;
 }
 
+// Host image of one stage before upload.
+struct StageHost {
+  bool fat = false;
+  std::vector<Prob> probs;
+  std::vector<int2> units;
+  std::vector<FatUnit> fat_units;
+  int max_m = 0, max_k = 0;
+  void add(const Prob& p, int nunits) {
+    const int idx = static_cast<int>(probs.size());
+    if (fat) {
+      for (int u = 0; u < nunits; ++u) fat_units.push_back(FatUnit{p, u, 0});
+    } else {
+      probs.push_back(p);
+      for (int u = 0; u < nunits; ++u) units.push_back(int2{idx, u});
+    }
+    max_m = std::max(max_m, p.M);
+    max_k = std::max(max_k, p.K);
+  }
+  size_t nunits() const { return fat ? fat_units.size() : units.size(); }
+};
+
 }  // namespace
 
 extern "C" {
@@ -298,21 +328,20 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
     if (!out) return BL_ERR_INVALID_ARGUMENT;
     *out = nullptr;
     if (!descs || count <= 0) return BL_ERR_INVALID_ARGUMENT;
-    int64_t quant_total = 0, gemv_total = 0, gemm_total = 0;
+    int64_t units_q = 0, units_v = 0, units_m = 0;
     size_t ws_bytes = 0;
-    int max_k = 0;
     for (int32_t i = 0; i < count; ++i) {
       const bl_desc& d = descs[i];
       bl_status st = check_forward(d.x, d.norm_w, d.packed_w, d.w_scale, d.M, d.K, d.N, d.eps, d.y);
       if (st != BL_OK) return st;
       if (d.M == 0) continue;
-      quant_total += d.M;
-      if (d.M <= kGemvMaxM) gemv_total += gemv_units(static_cast<int>(d.N));
-      else gemm_total += gemm_units(static_cast<int>(d.M), static_cast<int>(d.N));
+      units_q += quant_units(static_cast<int>(d.M));
+      if (d.M <= kGemvMaxM)
+        units_v += gemv_units(static_cast<int>(d.N), gemv_bucket(static_cast<int>(d.K)));
+      else units_m += gemm_units(static_cast<int>(d.M), static_cast<int>(d.N));
       ws_bytes += ws_layout(d.M, d.K).bytes;
-      max_k = d.K > max_k ? static_cast<int>(d.K) : max_k;
     }
-    if (quant_total > INT32_MAX / 2 || gemv_total > INT32_MAX / 2 || gemm_total > INT32_MAX / 2)
+    if (units_q > INT32_MAX / 2 || units_v > INT32_MAX / 2 || units_m > INT32_MAX / 2)
       return BL_ERR_UNSUPPORTED;
 
     bl_group* g = new (std::nothrow) bl_group;
@@ -327,8 +356,8 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       return BL_ERR_NOMEM;
     }
 
-    std::vector<Prob> all, gemv, gemm;
-    std::vector<int> qs{0}, vs{0}, ms{0};
+    StageHost hq, hm;
+    std::map<int, StageHost> hv;  // decode problems by superblock bucket
     uint8_t* ws = static_cast<uint8_t*>(g->workspace);
     size_t off = 0;
     for (int32_t i = 0; i < count; ++i) {
@@ -350,62 +379,65 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       p.K = static_cast<int>(d.K);
       p.N = static_cast<int>(d.N);
       off += l.bytes;
-      all.push_back(p);
-      qs.push_back(qs.back() + p.M);
+      hq.add(p, quant_units(p.M));
       if (p.M <= kGemvMaxM) {
-        gemv.push_back(p);
-        vs.push_back(vs.back() + gemv_units(p.N));
-      } else {
-        gemm.push_back(p);
-        ms.push_back(ms.back() + gemm_units(p.M, p.N));
+        StageHost& sh = hv[gemv_bucket(p.K)];
+        sh.fat = true;
+        sh.add(p, gemv_units(p.N, gemv_bucket(p.K)));
       }
+      else hm.add(p, gemm_units(p.M, p.N));
     }
-    g->count = static_cast<int>(all.size());
-    g->gemv_count = static_cast<int>(gemv.size());
-    g->gemm_count = static_cast<int>(gemm.size());
-    g->quant_total = static_cast<int>(quant_total);
-    g->gemv_total = static_cast<int>(gemv_total);
-    g->gemm_total = static_cast<int>(gemm_total);
-    g->max_k = max_k;
 
-    // One device buffer for the problem tables and the prefix sums.
-    const size_t b_all = round_up(all.size() * sizeof(Prob), kAlign);
-    const size_t b_gemv = round_up(gemv.size() * sizeof(Prob), kAlign);
-    const size_t b_gemm = round_up(gemm.size() * sizeof(Prob), kAlign);
-    const size_t b_qs = round_up(qs.size() * sizeof(int), kAlign);
-    const size_t b_vs = round_up(vs.size() * sizeof(int), kAlign);
-    const size_t b_ms = round_up(ms.size() * sizeof(int), kAlign);
-    const size_t total = b_all + b_gemv + b_gemm + b_qs + b_vs + b_ms;
-    std::vector<uint8_t> host(total, 0);
-    size_t o = 0;
-    auto put = [&](const void* src, size_t n, size_t span) {
-      if (n) std::memcpy(host.data() + o, src, n);
-      const size_t at = o;
-      o += span;
-      return at;
-    };
-    const size_t o_all = put(all.data(), all.size() * sizeof(Prob), b_all);
-    const size_t o_gemv = put(gemv.data(), gemv.size() * sizeof(Prob), b_gemv);
-    const size_t o_gemm = put(gemm.data(), gemm.size() * sizeof(Prob), b_gemm);
-    const size_t o_qs = put(qs.data(), qs.size() * sizeof(int), b_qs);
-    const size_t o_vs = put(vs.data(), vs.size() * sizeof(int), b_vs);
-    const size_t o_ms = put(ms.data(), ms.size() * sizeof(int), b_ms);
-    if (hipMalloc(&g->tables, total) != hipSuccess) {
+    // One device buffer for every table.
+    g->gemv.resize(hv.size());
+    std::vector<StageHost*> hosts{&hq, &hm};
+    std::vector<GroupStage*> stages{&g->quant, &g->gemm};
+    size_t bi = 0;
+    for (auto& kv : hv) {
+      g->gemv[bi].first = kv.first;
+      hosts.push_back(&kv.second);
+      stages.push_back(&g->gemv[bi].second);
+      ++bi;
+    }
+    const size_t nst = hosts.size();
+    size_t total = 0;
+    std::vector<std::array<size_t, 3>> offs(nst);
+    for (size_t k = 0; k < nst; ++k) {
+      offs[k][0] = total;
+      total += round_up(hosts[k]->probs.size() * sizeof(Prob), kAlign);
+      offs[k][1] = total;
+      total += round_up(hosts[k]->units.size() * sizeof(int2), kAlign);
+      offs[k][2] = total;
+      total += round_up(hosts[k]->fat_units.size() * sizeof(FatUnit), kAlign);
+    }
+    std::vector<uint8_t> image(std::max<size_t>(total, 1), 0);
+    for (size_t k = 0; k < nst; ++k) {
+      const StageHost& h = *hosts[k];
+      if (!h.probs.empty())
+        std::memcpy(image.data() + offs[k][0], h.probs.data(), h.probs.size() * sizeof(Prob));
+      if (!h.units.empty())
+        std::memcpy(image.data() + offs[k][1], h.units.data(), h.units.size() * sizeof(int2));
+      if (!h.fat_units.empty())
+        std::memcpy(image.data() + offs[k][2], h.fat_units.data(), h.fat_units.size() * sizeof(FatUnit));
+    }
+    if (hipMalloc(&g->tables, image.size()) != hipSuccess) {
       (void)hipGetLastError();
       free_group(g);
       return BL_ERR_NOMEM;
     }
-    if (hipMemcpy(g->tables, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+    if (hipMemcpy(g->tables, image.data(), image.size(), hipMemcpyHostToDevice) != hipSuccess) {
       free_group(g);
       return BL_ERR_HIP;
     }
     uint8_t* t = static_cast<uint8_t*>(g->tables);
-    g->d_all = reinterpret_cast<const Prob*>(t + o_all);
-    g->d_gemv = reinterpret_cast<const Prob*>(t + o_gemv);
-    g->d_gemm = reinterpret_cast<const Prob*>(t + o_gemm);
-    g->d_quant_starts = reinterpret_cast<const int*>(t + o_qs);
-    g->d_gemv_starts = reinterpret_cast<const int*>(t + o_vs);
-    g->d_gemm_starts = reinterpret_cast<const int*>(t + o_ms);
+    for (size_t k = 0; k < nst; ++k) {
+      stages[k]->probs = reinterpret_cast<const Prob*>(t + offs[k][0]);
+      stages[k]->units = reinterpret_cast<const int2*>(t + offs[k][1]);
+      stages[k]->fat = hosts[k]->fat ? reinterpret_cast<const FatUnit*>(t + offs[k][2]) : nullptr;
+      stages[k]->total = static_cast<int>(hosts[k]->nunits());
+      stages[k]->max_m = hosts[k]->max_m;
+      stages[k]->max_k = hosts[k]->max_k;
+    }
     *out = g;
     return BL_OK;
   } catch (...) {
@@ -417,9 +449,8 @@ bl_status bl_group_quant(bl_group* g, void* stream) {
   try {
     if (!g) return BL_ERR_INVALID_ARGUMENT;
     bl_status st = group_current_device(g);
-    if (st != BL_OK || g->count == 0) return st;
-    return from_hip(launch_quant(table_set(g->d_all, g->d_quant_starts, g->count, g->quant_total),
-                                 g->max_k, static_cast<hipStream_t>(stream)));
+    if (st != BL_OK || g->quant.total == 0) return st;
+    return from_hip(launch_quant(stage_set(g->quant), g->quant.max_k, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return BL_ERR_INTERNAL;
   }
@@ -431,14 +462,16 @@ bl_status bl_group_matmul(bl_group* g, void* stream) {
     bl_status st = group_current_device(g);
     if (st != BL_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (g->gemv_count > 0) {
-      st = from_hip(launch_gemv(table_set(g->d_gemv, g->d_gemv_starts, g->gemv_count, g->gemv_total),
-                                false, s));
+    for (const auto& kv : g->gemv) {
+      const GroupStage& gs = kv.second;
+      if (gs.total == 0) continue;
+      GemvLaunch L{};
+      L.units = gs.fat;
+      L.total = gs.total;
+      st = from_hip(launch_gemv(L, false, kv.first, gs.max_m, gs.max_k, s));
       if (st != BL_OK) return st;
     }
-    if (g->gemm_count > 0)
-      st = from_hip(launch_gemm(table_set(g->d_gemm, g->d_gemm_starts, g->gemm_count, g->gemm_total),
-                                false, s));
+    if (g->gemm.total > 0) st = from_hip(launch_gemm(stage_set(g->gemm), false, s));
     return st;
   } catch (...) {
     return BL_ERR_INTERNAL;

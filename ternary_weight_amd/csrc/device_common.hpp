@@ -11,6 +11,10 @@ namespace bl {
 constexpr int kWave = 64;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+#define BL_GLOBAL __attribute__((address_space(1)))
+#define BL_CONST __attribute__((address_space(4)))
 
 // One projection as the kernels see it.  Pointers are device pointers.
 // Workspace pointers (xq, factor, rowsum) belong to the library.
@@ -28,35 +32,78 @@ struct Prob {
   int M, K, N;
 };
 
-// A launch covers either one problem passed by value (count == 0) or a table
-// of problems in device memory.  `starts` holds count+1 prefix sums of the
-// work units (rows or tiles) each problem contributes.
+// A launch covers either one problem passed by value (units == nullptr:
+// work unit u is local unit u of that problem) or a table of problems in
+// device memory with one (problem, local unit) pair per work unit, built on
+// the host so that a workgroup finds its problem with one scalar load.
 struct ProbSet {
   Prob single;
   const Prob* probs;
-  const int* starts;
-  int count;
+  const int2* units;
   int total;  // total work units
 };
 
-// Locate the problem owning work unit `u`: returns the problem index and
-// writes the unit's index local to that problem.
+// A work unit that carries its problem record inline: one scalar load finds
+// everything a workgroup needs (used where workgroups are short-lived).
+struct FatUnit {
+  Prob p;
+  int local;
+  int pad;
+};
+
+// Address-space qualified views.  Pointers read from a problem record are
+// generic; casting them to the global space lets the compiler emit global_*
+// memory instructions (counted by vmcnt only) instead of flat_* ones, which
+// also count against lgkmcnt and serialise with LDS traffic.  The problem
+// table itself is read through the constant space, i.e. with scalar loads
+// into SGPRs (the index is wave-uniform).
+template <typename T>
+__device__ __forceinline__ const BL_GLOBAL T* gptr(const void* p) {
+  return (const BL_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ BL_GLOBAL T* gptr_out(void* p) {
+  return (BL_GLOBAL T*)p;
+}
+
+// Locate the problem owning work unit `u` (wave-uniform): returns the
+// problem index (-1 for the by-value problem) and writes the local unit.
 __device__ __forceinline__ int find_prob(const ProbSet& s, int u, int* local) {
-  if (s.count == 0) {
+  if (s.units == nullptr) {
     *local = u;
     return -1;
   }
-  int lo = 0, hi = s.count - 1;
-  while (lo < hi) {  // largest p with starts[p] <= u
-    int mid = (lo + hi + 1) >> 1;
-    if (s.starts[mid] <= u) lo = mid; else hi = mid - 1;
-  }
-  *local = u - s.starts[lo];
-  return lo;
+  const BL_CONST int* e = (const BL_CONST int*)(s.units + u);
+  *local = e[1];
+  return e[0];
 }
 
-__device__ __forceinline__ const Prob& prob_at(const ProbSet& s, int p) {
-  return p < 0 ? s.single : s.probs[p];
+__device__ __forceinline__ Prob prob_at(const ProbSet& s, int p) {
+  if (p < 0) return s.single;
+  static_assert(sizeof(Prob) % 4 == 0, "Prob is copied as dwords");
+  Prob out;
+  const BL_CONST uint32_t* src = (const BL_CONST uint32_t*)(s.probs + p);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(&out);
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(sizeof(Prob) / 4); ++i) dst[i] = src[i];
+  return out;
+}
+
+// Problem record and local unit of work unit u from a FatUnit table.
+__device__ __forceinline__ Prob fat_unit_at(const FatUnit* units, int u, int* local) {
+  static_assert(sizeof(FatUnit) % 4 == 0, "FatUnit is copied as dwords");
+  FatUnit out;
+  const BL_CONST uint32_t* src = (const BL_CONST uint32_t*)(units + u);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(&out);
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(sizeof(FatUnit) / 4); ++i) dst[i] = src[i];
+  *local = out.local;
+  return out.p;
+}
+
+// Wave index as a scalar (uniform across the wave).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 }
 
 // ---- wave64 butterfly reductions (every lane ends with the result) --------

@@ -9,14 +9,24 @@ namespace bl {
 
 // Largest K accepted by the GPU path; rows up to kQuantRegK stay in registers.
 constexpr int kKMax = 65536;
+// Byte offsets into one problem's packed weights and int8 activations are
+// 32-bit (buffer addressing): N*K/4 and M*K must stay below this.
+constexpr int64_t kMaxOffset = (int64_t{1} << 31) - 4096;
 constexpr int kQuantRegK = 4096;
 
 // Rows per skinny-decode pass: M <= kGemvMaxM takes the weight-streaming kernel.
 constexpr int kGemvMaxM = 16;
 
-// Work-unit counts per problem (what ProbSet::starts sums up).
-inline int quant_units(int M) { return M; }
-int gemv_units(int N);
+// Work units (workgroups) per problem.  Quantization: kQuantRows rows per
+// workgroup, kQuantRowsPerWave per wave.
+constexpr int kQuantRowsPerWave = 1;
+constexpr int kQuantRows = 4 * kQuantRowsPerWave;
+inline int quant_units(int M) { return (M + kQuantRows - 1) / kQuantRows; }
+// Decode kernel: a workgroup owns 64 weight rows of one problem.  Problems
+// are launched in buckets of equal superblock count ceil(K/256) (1..16; 0 =
+// the generic variant for longer K).
+int gemv_units(int N, int bucket);
+int gemv_bucket(int K);
 int gemm_units(int M, int N);
 
 // Stage 1: fused RMSNorm + absmax int8 quantization of every row in the set.
@@ -24,8 +34,17 @@ int gemm_units(int M, int N);
 hipError_t launch_quant(const ProbSet& set, int max_k, hipStream_t stream);
 // Row sums of caller-supplied int8 activations (for the raw-integer hook).
 hipError_t launch_rowsum(const Prob& p, hipStream_t stream);
-// Stage 2, M <= kGemvMaxM: weight-streaming MFMA decode kernel.
-hipError_t launch_gemv(const ProbSet& set, bool raw, hipStream_t stream);
+// Stage 2, M <= kGemvMaxM: weight-streaming MFMA decode kernel for one
+// bucket, over one by-value problem (units == nullptr) or a FatUnit table.
+// max_m and max_k bound the launch's M and K (they size the LDS activation
+// staging).
+struct GemvLaunch {
+  Prob single;
+  const FatUnit* units;
+  int total;
+};
+hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,
+                       hipStream_t stream);
 // Stage 2, M > kGemvMaxM: LDS-tiled MFMA kernel.
 hipError_t launch_gemm(const ProbSet& set, bool raw, hipStream_t stream);
 

@@ -39,93 +39,104 @@ __device__ __forceinline__ void finish_row(const Prob& P, int m, double ss, floa
   rs = wave_sum(rs);
   if (lane == 0) {
     double r = 1.0 / sqrt(ss / static_cast<double>(P.K) + static_cast<double>(P.eps));
-    P.factor[m] = static_cast<float>(r * static_cast<double>(amax) / 127.0);
-    if (P.rowsum) P.rowsum[m] = rs;
+    gptr_out<float>(P.factor)[m] = static_cast<float>(r * static_cast<double>(amax) / 127.0);
+    if (P.rowsum) gptr_out<int32_t>(P.rowsum)[m] = rs;
   }
 }
 
-// NC: float4 chunks per lane held in registers (K <= 256*NC).
+// NC: float4 chunks per lane held in registers (K <= 256*NC).  A workgroup
+// owns kQuantRows consecutive rows of one problem, kQuantRowsPerWave per wave.
 template <int NC>
 __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= set.total) return;
-  int m;
-  const Prob& P = prob_at(set, find_prob(set, unit, &m));
+  int local;
+  const Prob P = prob_at(set, find_prob(set, blockIdx.x, &local));
   const int nch = P.K >> 2;
-  const float4* xr = reinterpret_cast<const float4*>(P.x + static_cast<int64_t>(m) * P.K);
-  const float4* wr = reinterpret_cast<const float4*>(P.norm_w);
-
-  float4 u[NC];
-  float ss = 0.f, amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = lane + kWave * i;
-    u[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < nch) {
-      const float4 xv = xr[c];
-      const float4 wv = wr[c];
-      ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
-      u[i] = make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(u[i].x), fabsf(u[i].y)),
-                               fmaxf(fabsf(u[i].z), fabsf(u[i].w))));
-    }
-  }
-  const double ssd = wave_sum(static_cast<double>(ss));
-  amax = wave_max(amax);
-
-  uint32_t* qrow = reinterpret_cast<uint32_t*>(P.xq + static_cast<int64_t>(m) * P.K);
-  int rs = 0;
-  if (amax > 0.f && amax >= 1e-30f) {
-    const float s = 127.0f / amax;
+  const int m_begin = local * kQuantRows + wave_id() * kQuantRowsPerWave;
+  const BL_GLOBAL f4* wr = gptr<f4>(P.norm_w);
+  for (int r = 0; r < kQuantRowsPerWave; ++r) {
+    const int m = m_begin + r;
+    if (m >= P.M) break;
+    const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m) * P.K);
+    f4 u[NC];
+    float ss = 0.f, amax = 0.f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = lane + kWave * i;
+      u[i] = f4{0.f, 0.f, 0.f, 0.f};
       if (c < nch) {
-        const int a = code_f32(u[i].x, s), b = code_f32(u[i].y, s);
-        const int cc = code_f32(u[i].z, s), d = code_f32(u[i].w, s);
-        rs += a + b + cc + d;
-        qrow[c] = pack4(a, b, cc, d);
+        const f4 xv = xr[c];
+        ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+        u[i] = xv * wr[c];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(u[i].x), fabsf(u[i].y)),
+                                 fmaxf(fabsf(u[i].z), fabsf(u[i].w))));
       }
     }
-  } else if (amax > 0.f) {  // tiny row: 127/amax would overflow fp32
-    const double s = 127.0 / static_cast<double>(amax);
+    const double ssd = wave_sum(static_cast<double>(ss));
+    amax = wave_max(amax);
+
+    BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
+    int rs = 0;
+    if (amax >= 1e-30f) {
+      const float s = 127.0f / amax;
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = lane + kWave * i;
-      if (c < nch) {
-        const int a = code_f64(u[i].x, s), b = code_f64(u[i].y, s);
-        const int cc = code_f64(u[i].z, s), d = code_f64(u[i].w, s);
-        rs += a + b + cc + d;
-        qrow[c] = pack4(a, b, cc, d);
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + kWave * i;
+        if (c < nch) {
+          const int a = code_f32(u[i].x, s), b = code_f32(u[i].y, s);
+          const int cc = code_f32(u[i].z, s), d = code_f32(u[i].w, s);
+          rs += a + b + cc + d;
+          qrow[c] = pack4(a, b, cc, d);
+        }
+      }
+    } else if (amax > 0.f) {  // tiny row: 127/amax would overflow fp32
+      const double s = 127.0 / static_cast<double>(amax);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + kWave * i;
+        if (c < nch) {
+          const int a = code_f64(u[i].x, s), b = code_f64(u[i].y, s);
+          const int cc = code_f64(u[i].z, s), d = code_f64(u[i].w, s);
+          rs += a + b + cc + d;
+          qrow[c] = pack4(a, b, cc, d);
+        }
+      }
+    } else {  // all-zero row: zero codes, factor 0
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + kWave * i;
+        if (c < nch) qrow[c] = 0u;
       }
     }
-  } else {  // all-zero row: zero codes, factor 0
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = lane + kWave * i;
-      if (c < nch) qrow[c] = 0u;
-    }
+    finish_row(P, m, ssd, amax, rs, lane);
   }
-  finish_row(P, m, ssd, amax, rs, lane);
 }
 
 // Rows longer than the register budget: two streaming passes over the row.
+__device__ void quant_stream_row(const Prob& P, int m, int lane);
 __global__ __launch_bounds__(256) void quant_stream_kernel(ProbSet set) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= set.total) return;
-  int m;
-  const Prob& P = prob_at(set, find_prob(set, unit, &m));
+  int local;
+  const Prob P = prob_at(set, find_prob(set, blockIdx.x, &local));
+  const int m_begin = local * kQuantRows + wave_id() * kQuantRowsPerWave;
+  for (int r = 0; r < kQuantRowsPerWave; ++r) {
+    const int m = m_begin + r;
+    if (m >= P.M) break;
+    quant_stream_row(P, m, lane);
+  }
+}
+
+// One row, two streaming passes (used for K above the register budget).
+__device__ void quant_stream_row(const Prob& P, int m, int lane) {
   const int nch = P.K >> 2;
-  const float4* xr = reinterpret_cast<const float4*>(P.x + static_cast<int64_t>(m) * P.K);
-  const float4* wr = reinterpret_cast<const float4*>(P.norm_w);
+  const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m) * P.K);
+  const BL_GLOBAL f4* wr = gptr<f4>(P.norm_w);
 
   double ss = 0.0;
   float amax = 0.f;
   for (int c = lane; c < nch; c += kWave) {
-    const float4 xv = xr[c];
-    const float4 wv = wr[c];
+    const f4 xv = xr[c];
+    const f4 wv = wr[c];
     ss += static_cast<double>(xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w);
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xv.x * wv.x), fabsf(xv.y * wv.y)),
                              fmaxf(fabsf(xv.z * wv.z), fabsf(xv.w * wv.w))));
@@ -133,15 +144,15 @@ __global__ __launch_bounds__(256) void quant_stream_kernel(ProbSet set) {
   ss = wave_sum(ss);
   amax = wave_max(amax);
 
-  uint32_t* qrow = reinterpret_cast<uint32_t*>(P.xq + static_cast<int64_t>(m) * P.K);
+  BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
   int rs = 0;
   const bool tiny = amax < 1e-30f;
   const float s = amax > 0.f && !tiny ? 127.0f / amax : 0.f;
   const double sd = amax > 0.f ? 127.0 / static_cast<double>(amax) : 0.0;
   for (int c = lane; c < nch; c += kWave) {
-    const float4 xv = xr[c];
-    const float4 wv = wr[c];
-    const float4 u = make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
+    const f4 xv = xr[c];
+    const f4 wv = wr[c];
+    const f4 u = xv * wv;
     int a = 0, b = 0, cc = 0, d = 0;
     if (amax > 0.f) {
       if (!tiny) {
@@ -159,9 +170,9 @@ __global__ __launch_bounds__(256) void quant_stream_kernel(ProbSet set) {
 // Row sums of int8 codes supplied by the caller (raw-integer hook only).
 __global__ __launch_bounds__(256) void rowsum_kernel(Prob P) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int m = blockIdx.x * 4 + wave_id();
   if (m >= P.M) return;
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(P.xq + static_cast<int64_t>(m) * P.K);
+  const BL_GLOBAL uint32_t* row = gptr<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
   int rs = 0;
   for (int c = lane; c < (P.K >> 2); c += kWave) {
     const uint32_t d = row[c];
@@ -169,12 +180,12 @@ __global__ __launch_bounds__(256) void rowsum_kernel(Prob P) {
           static_cast<int8_t>((d >> 16) & 0xff) + static_cast<int8_t>(d >> 24);
   }
   rs = wave_sum(rs);
-  if (lane == 0) P.rowsum[m] = rs;
+  if (lane == 0) gptr_out<int32_t>(P.rowsum)[m] = rs;
 }
 
 hipError_t launch_quant(const ProbSet& set, int max_k, hipStream_t stream) {
   if (set.total <= 0) return hipSuccess;
-  const dim3 grid((set.total + 3) / 4), block(256);
+  const dim3 grid(set.total), block(256);
   const int nc = (max_k + 255) / 256;
   if (max_k > kQuantRegK)
     hipLaunchKernelGGL(quant_stream_kernel, grid, block, 0, stream, set);

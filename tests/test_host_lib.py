@@ -19,13 +19,15 @@ from conftest import ROOT
 from ternary_weight_amd import bitlinear as bl
 from ternary_weight_amd import inputs
 
-HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("bitlinear.h", "bitlinear_probe.h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text))
+    return sorted(names - {"defined"})
 
 
 def test_header_symbols_exported():
@@ -33,7 +35,7 @@ def test_header_symbols_exported():
     assert "bitlinear_forward" in names and "i2s_pack" in names
     lib = ctypes.CDLL(bl.LIB_PATH)
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in bitlinear.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(names) == set(bl.EXPORTED)
 
 
@@ -146,6 +148,16 @@ def test_quant_and_matmul_validation():
     assert mm(A, MIS, 4, 128, 8, A, None) == bl.BL_ERR_MISALIGNED
     assert mm(A, A, 4, 128, 8, MIS, None) == bl.BL_ERR_MISALIGNED
     assert mm(A, A, 0, 128, 8, A, None) == bl.BL_OK
+
+
+def test_probe_validation():
+    lib = bl.lib
+    assert lib.bl_probe_read(None, 64, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_probe_read(A, 63, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_probe_read(MIS, 64, A, 1, None) == bl.BL_ERR_MISALIGNED
+    assert lib.bl_probe_copy(A, MIS, 64, 1, None) == bl.BL_ERR_MISALIGNED
+    assert lib.bl_probe_copy(A, A, 64, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_probe_mfma_i8(0, 1, A, None) == bl.BL_ERR_INVALID_ARGUMENT
 
 
 def test_group_validation():
