@@ -234,11 +234,15 @@ def measure_peaks(torch, bl):
     copy = max(2 * half / timed(lambda: bl.probe_copy(src, dst, b)) / 1e9 for b in (4096, 16384))
     del buf, src, dst
     iters, blocks = 4000, 256 * 8
-    t = timed(lambda: bl.probe_mfma_i8(iters, blocks, sink), reps=3)
-    mfma = blocks * 4 * 4 * iters * 32768 / t / 1e12
+    mfma = {}
+    for shape in (16, 32):
+        t = timed(lambda: bl.probe_mfma_i8(iters, blocks, sink, shape=shape), reps=3)
+        mfma[shape] = blocks * 4 * iters * 131072 / t / 1e12
     return {"hbm_read_GBps": round(max(read.values()), 1),
             "hbm_read_by_blocks": {str(k): round(v, 1) for k, v in read.items()},
-            "copy_GBps_read_plus_write": round(copy, 1), "mfma_i8_TOPS": round(mfma, 1)}
+            "copy_GBps_read_plus_write": round(copy, 1),
+            "mfma_i8_TOPS": round(max(mfma.values()), 1),
+            "mfma_i8_TOPS_by_shape": {f"{k}x{k}": round(v, 1) for k, v in mfma.items()}}
 
 
 def cpu_baseline_decode(projs, seconds: float):

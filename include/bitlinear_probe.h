@@ -29,10 +29,13 @@ bl_status bl_probe_read(const void* buf, size_t bytes, uint32_t* sink, int32_t b
  * `blocks` workgroups of 256 threads: exactly `bytes` read and written. */
 bl_status bl_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* stream);
 
-/* int8 matrix-core throughput: each of `blocks` workgroups of 4 waves runs
- * 4*iters dependent-chain v_mfma_i32_16x16x64_i8 (32768 int8 operations
- * each) per wave on register operands.  sink: device int32 (see above). */
-bl_status bl_probe_mfma_i8(int32_t iters, int32_t blocks, int32_t* sink, void* stream);
+/* int8 matrix-core throughput: each of `blocks` workgroups of 4 waves runs,
+ * per wave on register operands, either (shape 16) 4*iters
+ * v_mfma_i32_16x16x64_i8 in four independent chains or (shape 32) 2*iters
+ * v_mfma_i32_32x32x32_i8 in two chains: 131072*iters int8 operations per
+ * wave either way.  sink: device int32 (see above). */
+bl_status bl_probe_mfma_i8(int32_t iters, int32_t blocks, int32_t shape, int32_t* sink,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -56,7 +56,7 @@ _SIGS = {
     # measurement probes (include/bitlinear_probe.h)
     "bl_probe_read": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
     "bl_probe_copy": ([_p, _p, ctypes.c_size_t, _i32, _p], _i32),
-    "bl_probe_mfma_i8": ([_i32, _i32, _p, _p], _i32),
+    "bl_probe_mfma_i8": ([_i32, _i32, _i32, _p, _p], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -248,7 +248,7 @@ def probe_copy(src, dst, blocks: int, stream=None) -> None:
                               src.numel(), blocks, _stream_handle(stream)), "bl_probe_copy")
 
 
-def probe_mfma_i8(iters: int, blocks: int, sink, stream=None) -> None:
+def probe_mfma_i8(iters: int, blocks: int, sink, shape: int = 16, stream=None) -> None:
     torch = _torch()
-    _check(_lib.bl_probe_mfma_i8(iters, blocks, _dev(sink, torch.int32, "sink"),
+    _check(_lib.bl_probe_mfma_i8(iters, blocks, shape, _dev(sink, torch.int32, "sink"),
                                  _stream_handle(stream)), "bl_probe_mfma_i8")

@@ -89,33 +89,32 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   const int n0 = (local % tiles_n) * kTileN;
   const int nblk = K / kBlockK;
 
-  // This lane's direct-load sources: for activation instruction i the lane
-  // fills LDS row 32*wave + 8*i + lane/8, physical slot lane%8; for weight
-  // instruction i, row 64*wave + 32*i + lane/2, physical slot lane%2.
-  const int8_t* xsrc[kXLoads];
+  // This lane's direct-load sources (32-bit offsets from the problem's
+  // bases): for activation instruction i the lane fills LDS row
+  // 32*wave + 8*i + lane/8, physical slot lane%8; for weight instruction i,
+  // row 64*wave + 32*i + lane/2, physical slot lane%2.
+  int xoff[kXLoads];
 #pragma unroll
   for (int i = 0; i < kXLoads; ++i) {
     const int row = 32 * wave + 8 * i + (lane >> 3);
     const int slot = xs_slot(row, lane & 7);
-    const int m = min(m0 + row, M - 1);
-    xsrc[i] = P.xq + static_cast<int64_t>(m) * K + slot * 16;
+    xoff[i] = min(m0 + row, M - 1) * K + slot * 16;
   }
-  const uint8_t* wsrc[kWLoads];
+  int woff[kWLoads];
 #pragma unroll
   for (int i = 0; i < kWLoads; ++i) {
     const int row = 64 * wave + 32 * i + (lane >> 1);
     const int slot = ws_slot(row, lane & 1);
-    const int n = min(n0 + row, N - 1);
-    wsrc[i] = P.w + static_cast<int64_t>(n) * rowbytes + slot * 16;
+    woff[i] = min(n0 + row, N - 1) * rowbytes + slot * 16;
   }
   auto issue = [&](int kb) {
     uint8_t* st = smem + (kb % kStages) * kStageBytes;
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i)
-      dma16(xsrc[i] + kb * kBlockK, st + (kXLoads * wave + i) * 1024);
+      dma16(P.xq + xoff[i] + kb * kBlockK, st + (kXLoads * wave + i) * 1024);
 #pragma unroll
     for (int i = 0; i < kWLoads; ++i)
-      dma16(wsrc[i] + kb * (kBlockK / 4), st + kXStage + (kWLoads * wave + i) * 1024);
+      dma16(P.w + woff[i] + kb * (kBlockK / 4), st + kXStage + (kWLoads * wave + i) * 1024);
   };
 
   v16i acc[4][2];
@@ -126,6 +125,22 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
 
   issue(0);
   if (nblk > 1) issue(1);
+
+  // LDS byte offsets of this lane's fragments inside a stage.
+  int xrd[4][2];  // [k-step j][fm]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+      const int row = wm * 64 + fm * 32 + r32;
+      xrd[j][fm] = row * kBlockK + xs_slot(row, 2 * j + g) * 16;
+    }
+  int wrd[4];
+#pragma unroll
+  for (int fn = 0; fn < 4; ++fn) {
+    const int row = wn * 128 + fn * 32 + r32;
+    wrd[fn] = kXStage + row * 32 + ws_slot(row, g) * 16;
+  }
 
   for (int kb = 0; kb < nblk; ++kb) {
     // Stage kb's loads are done once at most stage kb+1's are outstanding.
@@ -138,21 +153,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
     // Every wave is past stage kb-1, whose ring slot stage kb+2 reuses.
     if (kb + 2 < nblk) issue(kb + 2);
 
-    const uint8_t* xs = smem + (kb % kStages) * kStageBytes;
-    const uint8_t* ws = xs + kXStage;
+    const uint8_t* st = smem + (kb % kStages) * kStageBytes;
     v4i wp[4];  // 16-byte half g of 4 weight rows per lane (one per fragment)
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn) {
-      const int row = wn * 128 + fn * 32 + r32;
-      wp[fn] = *reinterpret_cast<const v4i*>(ws + row * 32 + ws_slot(row, g) * 16);
-    }
+    for (int fn = 0; fn < 4; ++fn) wp[fn] = *reinterpret_cast<const v4i*>(st + wrd[fn]);
+    // Activation fragments run one k-step ahead of the MFMAs.
+    v4i b[2][2];
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) b[0][fm] = *reinterpret_cast<const v4i*>(st + xrd[0][fm]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v4i b[2];
+      if (j + 1 < 4) {
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm) {
-        const int row = wm * 64 + fm * 32 + r32;
-        b[fm] = *reinterpret_cast<const v4i*>(xs + row * kBlockK + xs_slot(row, 2 * j + g) * 16);
+        for (int fm = 0; fm < 2; ++fm)
+          b[(j + 1) & 1][fm] = *reinterpret_cast<const v4i*>(st + xrd[j + 1][fm]);
       }
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn) {
@@ -161,43 +175,81 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
         for (int i = 0; i < 4; ++i) a[i] = field_codes(static_cast<uint32_t>(wp[fn][i]), j);
 #pragma unroll
         for (int fm = 0; fm < 2; ++fm)
-          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[fm], acc[fn][fm], 0, 0, 0);
+          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[j & 1][fm], acc[fn][fm], 0, 0, 0);
       }
     }
+    // Issue order for the stage: the packed weights and the first activation
+    // fragments, then per k-step the next step's fragments ahead of the
+    // decode/MFMA pairs, so LDS latency hides behind the previous step.
+    // (0x100: LDS reads, 0x002: VALU, 0x008: MFMA.)
+#define BL_STEP(ds, valu)                                                 \
+  if (ds) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);              \
+  for (int fn = 0; fn < 4; ++fn) {                                        \
+    __builtin_amdgcn_sched_group_barrier(0x002, valu, 0);                 \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                    \
+  }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    BL_STEP(true, 8)
+    BL_STEP(true, 8)
+    BL_STEP(true, 8)
+    BL_STEP(false, 4)
+#undef BL_STEP
   }
 
-  // Epilogue: fragment (fn, fm) lane holds weight rows 8q + 4g + r (q, r in
-  // 0..3) of activation row r32.
+  // Epilogue.  Fragment (fn, fm) lane holds weight rows 8q + 4g + r (q, r in
+  // 0..3) of activation row r32: a store straight from there would write
+  // 32 B into each of 32 rows per instruction.  Instead each 32-row half of
+  // the wave tile (fm) is scaled, transposed through the now idle stage ring
+  // (16 KB per wave, 16-byte slots XOR-swizzled by row) and written back so
+  // that each store instruction covers two full 512-byte row segments.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // every wave is done with the last stage
+  asm volatile("" ::: "memory");
+  uint8_t* tbuf = smem + wave * (32 * 512);
+  const int nw0 = n0 + wn * 128;  // first output column of this wave
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm) {
-    const int m = m0 + wm * 64 + fm * 32 + r32;
-    if (m >= M) continue;
-    const int rs = gptr<int32_t>(P.rowsum)[m];
-    float scale = 0.f;
-    if (!RAW) scale = gptr<float>(P.factor)[m] / P.w_scale;
+    const int mbase = m0 + wm * 64 + fm * 32;
+    {
+      const int m = mbase + r32;
+      const bool mok = m < M;
+      const int rs = mok ? gptr<int32_t>(P.rowsum)[m] : 0;
+      float scale = 0.f;
+      if (!RAW && mok) scale = gptr<float>(P.factor)[m] / P.w_scale;
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn) {
+      for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 128 + fn * 32 + 8 * q + 4 * g;
-        if (n >= N) continue;
-        const v4i v = v4i{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
-                          acc[fn][fm][4 * q + 3]};
-        const int64_t o = static_cast<int64_t>(m) * N + n;
-        if (RAW) {
-          if ((N & 3) == 0) {
-            *gptr_out<v4i>(P.acc + o) = v - rs;
-          } else {
-            for (int i = 0; i < 4 && n + i < N; ++i) gptr_out<int32_t>(P.acc)[o + i] = v[i] - rs;
+        for (int q = 0; q < 4; ++q) {
+          const int slot = fn * 8 + 2 * q + g;  // 16-byte column slot (4 outputs)
+          v4i v = v4i{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                      acc[fn][fm][4 * q + 3]} - rs;
+          if (!RAW) {
+            const f4 out = f4{static_cast<float>(v[0]) * scale, static_cast<float>(v[1]) * scale,
+                              static_cast<float>(v[2]) * scale, static_cast<float>(v[3]) * scale};
+            v = __builtin_bit_cast(v4i, out);
           }
-        } else {
-          const f4 out = f4{static_cast<float>(v[0] - rs) * scale, static_cast<float>(v[1] - rs) * scale,
-                            static_cast<float>(v[2] - rs) * scale, static_cast<float>(v[3] - rs) * scale};
-          if ((N & 3) == 0) {
-            *gptr_out<f4>(P.y + o) = out;
-          } else {
-            for (int i = 0; i < 4 && n + i < N; ++i) gptr_out<float>(P.y)[o + i] = out[i];
-          }
+          *reinterpret_cast<v4i*>(tbuf + r32 * 512 + ((slot ^ r32) & 31) * 16) = v;
+        }
+    }
+    // Read back row-contiguous: lane covers slot (lane % 32) of row 2i + lane/32.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 2 * i + g;
+      const int slot = lane & 31;
+      const v4i v = *reinterpret_cast<const v4i*>(tbuf + row * 512 + ((slot ^ row) & 31) * 16);
+      const int m = mbase + row;
+      const int n = nw0 + 4 * slot;
+      if (m >= M || n >= N) continue;
+      const int64_t o = static_cast<int64_t>(m) * N + n;
+      if ((N & 3) == 0) {
+        // Non-temporal: the output is written once and not read back here.
+        if (RAW) __builtin_nontemporal_store(v, gptr_out<v4i>(P.acc + o));
+        else __builtin_nontemporal_store(__builtin_bit_cast(f4, v), gptr_out<f4>(P.y + o));
+      } else {
+        const f4 fv = __builtin_bit_cast(f4, v);
+        for (int e = 0; e < 4 && n + e < N; ++e) {
+          if (RAW) gptr_out<int32_t>(P.acc)[o + e] = v[e];
+          else gptr_out<float>(P.y)[o + e] = fv[e];
         }
       }
     }

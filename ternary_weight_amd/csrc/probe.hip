@@ -40,6 +40,8 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const v4i* __restrict__
     dst[i] = src[i];
 }
 
+typedef int v16i __attribute__((ext_vector_type(16)));
+
 __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int32_t* sink) {
   const int lane = threadIdx.x & 63;
   v4i a = v4i{lane, lane + 1, lane + 2, lane + 3};
@@ -52,6 +54,21 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int32_t* sin
     c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, b, c3, 0, 0, 0);
   }
   const v4i s = c0 + c1 + c2 + c3;
+  if (s[0] == 0x7f123456) sink[0] = s[1];  // keeps the chain alive
+}
+
+// Same rate probe for the 32x32x32 shape (65536 operations per MFMA); iters
+// counts pairs so both probes issue the same number of int8 operations.
+__global__ __launch_bounds__(256) void probe_mfma32_kernel(int iters, int32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  v4i a = v4i{lane, lane + 1, lane + 2, lane + 3};
+  v4i b = v4i{3 * lane, lane ^ 5, lane + 7, 1};
+  v16i c0 = v16i{}, c1 = v16i{};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c1, 0, 0, 0);
+  }
+  const v16i s = c0 + c1;
   if (s[0] == 0x7f123456) sink[0] = s[1];  // keeps the chain alive
 }
 
@@ -82,10 +99,16 @@ bl_status bl_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks
   return bl::hip_status(hipGetLastError());
 }
 
-bl_status bl_probe_mfma_i8(int32_t iters, int32_t blocks, int32_t* sink, void* stream) {
-  if (!sink || iters <= 0 || blocks <= 0) return BL_ERR_INVALID_ARGUMENT;
-  hipLaunchKernelGGL(bl::probe_mfma_kernel, dim3(blocks), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), iters, sink);
+bl_status bl_probe_mfma_i8(int32_t iters, int32_t blocks, int32_t shape, int32_t* sink,
+                           void* stream) {
+  if (!sink || iters <= 0 || blocks <= 0 || (shape != 16 && shape != 32))
+    return BL_ERR_INVALID_ARGUMENT;
+  if (shape == 16)
+    hipLaunchKernelGGL(bl::probe_mfma_kernel, dim3(blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), iters, sink);
+  else
+    hipLaunchKernelGGL(bl::probe_mfma32_kernel, dim3(blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), iters, sink);
   return bl::hip_status(hipGetLastError());
 }
 
