@@ -106,24 +106,34 @@ class Arena:
 # -------------------------------------------------------------- timing ---
 
 def run_timed(torch, group, steps: int, warmup: int):
-    """Warm up, then time exactly `steps` steps; events bracket each stage."""
+    """Warm up, then time exactly `steps` steps.
+
+    A step is the quantization launch followed by every matmul launch, all on
+    the current stream; HIP events bracket each launch (events are recorded
+    on the stream the kernels run on).  Returns the wall-clock ms per step
+    and the mean ms of the quant launch, of the whole matmul stage and of
+    each matmul launch.
+    """
     stream = torch.cuda.current_stream()
+    nl = len(group.launches())
     for _ in range(warmup):
         group.forward()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for e in ev:
         e[0].record(stream)
         group.quant()
         e[1].record(stream)
-        group.matmul()
-        e[2].record(stream)
+        for i in range(nl):
+            group.matmul_launch(i)
+            e[i + 2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    quant_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    mm_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    return wall * 1e3 / steps, float(np.mean(quant_ms)), float(np.mean(mm_ms)), float(np.median(mm_ms))
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    mm_ms = float(np.mean([e[1].elapsed_time(e[nl + 1]) for e in ev]))
+    launch_ms = [float(np.mean([e[i + 1].elapsed_time(e[i + 2]) for e in ev])) for i in range(nl)]
+    return wall * 1e3 / steps, quant_ms, mm_ms, launch_ms
 
 
 def traffic_from_profiles(kernel_tag: str, source: str):
@@ -171,15 +181,24 @@ def bench_decode(torch, bl, args):
         y = arena.take(4 * N, torch.float32, (1, N))
         items.append(dict(x=x, norm_w=nw, packed_w=pw, w_scale=p["scale"], eps=inputs.EPS, N=N, y=y))
     group = bl.Group(items)
-    ms, quant_ms, mm_ms, mm_med = run_timed(torch, group, args.steps, args.warmup)
+    launches = group.launches()
+    ms, quant_ms, mm_ms, launch_ms = run_timed(torch, group, args.steps, args.warmup)
     group.close()
-    weight_bytes = sum(N * K // 4 for p in projs for K, N in [(p["K"], p["N"])])
-    # Algorithmic bytes of one decode-kernel launch: packed weights, int8
-    # activations, factor + row sum, fp32 outputs.
-    mm_bytes = sum(p["N"] * p["K"] // 4 + p["K"] + 8 + 4 * p["N"] for p in projs)
-    achieved = mm_bytes / (mm_ms * 1e-3) / 1e9
-    return dict(R=R, projs=projs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, mm_med=mm_med,
-                weight_bytes=weight_bytes, mm_bytes=mm_bytes, achieved=achieved,
+    weight_bytes = sum(p["N"] * p["K"] // 4 for p in projs)
+    # Algorithmic bytes of a decode launch, per BitLinear: packed weights
+    # N*K/4, int8 activations M*K, factor + row sum 8*M, fp32 outputs 4*M*N
+    # (M = 1).  The decode launches are one per superblock count ceil(K/256).
+    per_launch = []
+    for info, t in zip(launches, launch_ms):
+        members = [p for p in projs if (p["K"] + 255) // 256 == info["bucket"]]
+        nbytes = sum(p["N"] * p["K"] // 4 + p["K"] + 8 + 4 * p["N"] for p in members)
+        per_launch.append(dict(bucket=info["bucket"], bitlinears=len(members), K=members[0]["K"],
+                               bytes=nbytes, us=t * 1e3, GBps=nbytes / (t * 1e-3) / 1e9))
+    dom = max(per_launch, key=lambda d: d["bytes"])
+    mm_bytes = sum(d["bytes"] for d in per_launch)
+    return dict(R=R, projs=projs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, per_launch=per_launch,
+                dominant=dom, weight_bytes=weight_bytes, mm_bytes=mm_bytes,
+                stage_GBps=mm_bytes / (mm_ms * 1e-3) / 1e9,
                 value=weight_bytes / (ms * 1e-3) / 1e9)
 
 
@@ -200,7 +219,7 @@ def bench_prefill(torch, bl, args):
                           eps=inputs.EPS, N=p["N"],
                           y=torch.empty((w.M, p["N"]), dtype=torch.float32, device=dev)))
     group = bl.Group(items)
-    ms, quant_ms, mm_ms, mm_med = run_timed(torch, group, max(3, args.steps // 2), max(1, args.warmup // 2))
+    ms, quant_ms, mm_ms, _ = run_timed(torch, group, max(3, args.steps // 2), max(1, args.warmup // 2))
     group.close()
     ops = sum(2 * w.M * p["N"] * p["K"] for p in projs)
     return dict(projs=projs, xs=xs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, ops=ops, M=w.M,
@@ -303,10 +322,12 @@ def main():
     peaks = measure_peaks(torch, bl)
     log(f"measured peaks: {peaks}")
     dec = bench_decode(torch, bl, args)
+    dom = dec["dominant"]
     log(f"decode: {dec['ms']:.3f} ms/step, {dec['value']:.0f} GB/s weights; "
-        f"quant {dec['quant_ms'] * 1e3:.1f} us, decode kernel {dec['mm_ms'] * 1e3:.1f} us "
-        f"({dec['achieved']:.0f} GB/s algorithmic)")
-    traffic = traffic_from_profiles("gemv_decode_qwen3", "gemv.hip")
+        f"quant {dec['quant_ms'] * 1e3:.1f} us, matmul stage {dec['mm_ms'] * 1e3:.1f} us "
+        f"({dec['stage_GBps']:.0f} GB/s algorithmic); launches: "
+        + ", ".join(f"K={d['K']} {d['us']:.1f} us {d['GBps']:.0f} GB/s" for d in dec["per_launch"]))
+    traffic = traffic_from_profiles("gemv_decode_k1024", "gemv.hip")
     out = {
         "metric": METRIC,
         "value": round(dec["value"], 2),
@@ -327,17 +348,21 @@ def main():
             "weight_bytes": dec["weight_bytes"], "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "hbm", "kernel": "gemv_kernel (decode, M<=16)",
-            "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+            "bound": "hbm",
+            "kernel": f"gemv_kernel<false,true,{dom['bucket']}> (decode, K={dom['K']}, "
+                      f"{dom['bitlinears']} BitLinears per launch)",
+            "achieved": round(dom["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": dec["mm_bytes"],
-            "avg_launch_us": round(dec["mm_ms"] * 1e3, 2),
+            "algorithmic_bytes_per_launch": dom["bytes"],
+            "avg_launch_us": round(dom["us"], 2),
         },
-        "stages_us": {"quant": round(dec["quant_ms"] * 1e3, 2), "matmul": round(dec["mm_ms"] * 1e3, 2)},
+        "stages_us": {"quant": round(dec["quant_ms"] * 1e3, 2), "matmul": round(dec["mm_ms"] * 1e3, 2),
+                      "matmul_launches": [{"K": d["K"], "us": round(d["us"], 2),
+                                           "GBps": round(d["GBps"], 1)} for d in dec["per_launch"]]},
         "measured_peaks": peaks,
     }
-    out["roofline"]["frac_of_measured"] = round(dec["achieved"] / peaks["hbm_read_GBps"], 4)
+    out["roofline"]["frac_of_measured"] = round(dom["GBps"] / peaks["hbm_read_GBps"], 4)
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline_decode(dec["projs"], args.cpu_seconds)
     del dec
@@ -354,7 +379,7 @@ def main():
                 "bound": "mfma", "kernel": "gemm_kernel (prefill, M>16)",
                 "achieved": round(pre["mm_tops"], 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": round(pre["mm_tops"] / INT8_PEAK_TOPS, 4),
-                "traffic": traffic_from_profiles("gemm_prefill_qwen3", "gemm.hip"),
+                "traffic": traffic_from_profiles("gemm_prefill_qwen3_stack", "gemm.hip"),
                 "algorithmic_ops_per_launch": pre["ops"],
                 "avg_launch_us": round(pre["mm_ms"] * 1e3, 1),
                 "frac_of_measured": round(pre["mm_tops"] / peaks["mfma_i8_TOPS"], 4),

@@ -136,8 +136,11 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
 
 /*
  * Grouped execution: many independent projections (for example the seven of
- * a layer, or of many layers) run as one launch per stage.  Results are
- * bit-identical to separate bitlinear_forward calls on the same inputs.
+ * a layer, or of many layers) run with few launches: one quantization launch
+ * for all of them, then the matmul stage (one decode launch per distinct
+ * superblock count ceil(K/256) among the M <= 16 problems, one prefill launch
+ * for the rest).  Results are bit-identical to separate bitlinear_forward
+ * calls on the same inputs.
  */
 typedef struct bl_desc {
     const float* x;          /* device [M][K] */
@@ -169,6 +172,20 @@ bl_status bl_group_quant(bl_group* g, void* stream);
 /* Stage 2 only: integer product + epilogue for every descriptor, reading the
  * workspace written by the last bl_group_quant on the same stream. */
 bl_status bl_group_matmul(bl_group* g, void* stream);
+/* The matmul stage as individual launches, for callers that time or
+ * interleave them: the decode problems (M <= 16) run as one launch per
+ * superblock count ceil(K/256), in increasing order, then all prefill
+ * problems (M > 16) as one launch.  bl_group_matmul == every launch in order.
+ *   bl_group_matmul_launches: number of launches (>= 0; -1 for a NULL group).
+ *   bl_group_matmul_launch_info: kind 0 = decode launch (bucket = its
+ *     superblock count, 0 for K > 4096), 1 = prefill launch (bucket = 0);
+ *     count = problems in the launch.  Null outputs are skipped.
+ *   bl_group_matmul_launch: enqueue launch i (0-based) on stream. */
+int32_t bl_group_matmul_launches(const bl_group* g);
+bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kind, int32_t* bucket,
+                                      int32_t* count);
+bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream);
+
 /* Frees the group (synchronises the device first). NULL is a no-op. */
 bl_status bl_group_destroy(bl_group* g);
 

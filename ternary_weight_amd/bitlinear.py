@@ -52,6 +52,9 @@ _SIGS = {
     "bl_group_quant": ([_p, _p], _i32),
     "bl_group_matmul": ([_p, _p], _i32),
     "bl_group_destroy": ([_p], _i32),
+    "bl_group_matmul_launches": ([_p], _i32),
+    "bl_group_matmul_launch_info": ([_p, _i32, _p, _p, _p], _i32),
+    "bl_group_matmul_launch": ([_p, _i32, _p], _i32),
     "bl_release_workspace": ([], _i32),
     # measurement probes (include/bitlinear_probe.h)
     "bl_probe_read": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
@@ -207,6 +210,22 @@ class Group:
 
     def matmul(self, stream=None) -> None:
         _check(_lib.bl_group_matmul(self._h, _stream_handle(stream)), "bl_group_matmul")
+
+    def launches(self) -> list[dict]:
+        """The matmul stage's launches: kind ("decode"/"prefill"), bucket, count."""
+        out = []
+        for i in range(_lib.bl_group_matmul_launches(self._h)):
+            kind, bucket, count = _i32(), _i32(), _i32()
+            _check(_lib.bl_group_matmul_launch_info(self._h, i, ctypes.byref(kind),
+                                                    ctypes.byref(bucket), ctypes.byref(count)),
+                   "bl_group_matmul_launch_info")
+            out.append(dict(kind="decode" if kind.value == 0 else "prefill",
+                            bucket=bucket.value, count=count.value))
+        return out
+
+    def matmul_launch(self, i: int, stream=None) -> None:
+        _check(_lib.bl_group_matmul_launch(self._h, i, _stream_handle(stream)),
+               "bl_group_matmul_launch")
 
     def close(self) -> None:
         if self._h:

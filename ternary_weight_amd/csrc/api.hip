@@ -264,6 +264,7 @@ struct GroupStage {
   const int2* units = nullptr;
   const FatUnit* fat = nullptr;  // decode stages: problem records inline
   int total = 0;
+  int count = 0;  // problems
   int max_m = 0, max_k = 0;
 };
 
@@ -306,6 +307,7 @@ struct StageHost {
   std::vector<FatUnit> fat_units;
   int max_m = 0, max_k = 0;
   void add(const Prob& p, int nunits) {
+    ++nprobs;
     const int idx = static_cast<int>(probs.size());
     if (fat) {
       for (int u = 0; u < nunits; ++u) fat_units.push_back(FatUnit{p, u, 0});
@@ -317,6 +319,7 @@ struct StageHost {
     max_k = std::max(max_k, p.K);
   }
   size_t nunits() const { return fat ? fat_units.size() : units.size(); }
+  int nprobs = 0;
 };
 
 }  // namespace
@@ -435,6 +438,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       stages[k]->units = reinterpret_cast<const int2*>(t + offs[k][1]);
       stages[k]->fat = hosts[k]->fat ? reinterpret_cast<const FatUnit*>(t + offs[k][2]) : nullptr;
       stages[k]->total = static_cast<int>(hosts[k]->nunits());
+      stages[k]->count = hosts[k]->nprobs;
       stages[k]->max_m = hosts[k]->max_m;
       stages[k]->max_k = hosts[k]->max_k;
     }
@@ -456,26 +460,48 @@ bl_status bl_group_quant(bl_group* g, void* stream) {
   }
 }
 
-bl_status bl_group_matmul(bl_group* g, void* stream) {
+int32_t bl_group_matmul_launches(const bl_group* g) {
+  if (!g) return -1;
+  return static_cast<int32_t>(g->gemv.size()) + (g->gemm.total > 0 ? 1 : 0);
+}
+
+bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kind, int32_t* bucket,
+                                      int32_t* count) {
+  if (!g || i < 0 || i >= bl_group_matmul_launches(g)) return BL_ERR_INVALID_ARGUMENT;
+  const bool decode = i < static_cast<int32_t>(g->gemv.size());
+  if (kind) *kind = decode ? 0 : 1;
+  if (bucket) *bucket = decode ? g->gemv[i].first : 0;
+  if (count) *count = decode ? g->gemv[i].second.count : g->gemm.count;
+  return BL_OK;
+}
+
+bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream) {
   try {
-    if (!g) return BL_ERR_INVALID_ARGUMENT;
+    if (!g || i < 0 || i >= bl_group_matmul_launches(g)) return BL_ERR_INVALID_ARGUMENT;
     bl_status st = group_current_device(g);
     if (st != BL_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    for (const auto& kv : g->gemv) {
-      const GroupStage& gs = kv.second;
-      if (gs.total == 0) continue;
+    if (i < static_cast<int32_t>(g->gemv.size())) {
+      const GroupStage& gs = g->gemv[i].second;
       GemvLaunch L{};
       L.units = gs.fat;
       L.total = gs.total;
-      st = from_hip(launch_gemv(L, false, kv.first, gs.max_m, gs.max_k, s));
-      if (st != BL_OK) return st;
+      return from_hip(launch_gemv(L, false, g->gemv[i].first, gs.max_m, gs.max_k, s));
     }
-    if (g->gemm.total > 0) st = from_hip(launch_gemm(stage_set(g->gemm), false, s));
-    return st;
+    return from_hip(launch_gemm(stage_set(g->gemm), false, s));
   } catch (...) {
     return BL_ERR_INTERNAL;
   }
+}
+
+bl_status bl_group_matmul(bl_group* g, void* stream) {
+  if (!g) return BL_ERR_INVALID_ARGUMENT;
+  const int32_t n = bl_group_matmul_launches(g);
+  for (int32_t i = 0; i < n; ++i) {
+    const bl_status st = bl_group_matmul_launch(g, i, stream);
+    if (st != BL_OK) return st;
+  }
+  return group_current_device(g);
 }
 
 bl_status bl_group_forward(bl_group* g, void* stream) {

@@ -239,6 +239,20 @@ def test_group_matches_separate_calls():
         torch.cuda.synchronize()
         for it, ys in zip(items, singles):
             assert torch.equal(it["y"], ys)
+        # The matmul stage launch by launch: decode buckets (K 640, 1024,
+        # 2048, 3072 -> 3, 4, 8, 12 superblocks) in order, then prefill.
+        info = g.launches()
+        assert [d["kind"] for d in info] == ["decode"] * 3 + ["prefill"]
+        assert [d["bucket"] for d in info[:3]] == [4, 8, 12]
+        assert sum(d["count"] for d in info) == len(items)
+        for it in items:
+            it["y"].fill_(float("nan"))
+        g.quant()
+        for i in range(len(info)):
+            g.matmul_launch(i)
+        torch.cuda.synchronize()
+        for it, ys in zip(items, singles):
+            assert torch.equal(it["y"], ys)
 
 
 # ------------------------------------------ full-size workloads, sampled ---

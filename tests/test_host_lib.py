@@ -175,3 +175,6 @@ def test_group_validation():
     assert lib.bl_group_create(d, 2, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_group_forward(None, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_group_destroy(None) == bl.BL_OK
+    assert lib.bl_group_matmul_launches(None) == -1
+    assert lib.bl_group_matmul_launch(None, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_group_matmul_launch_info(None, 0, None, None, None) == bl.BL_ERR_INVALID_ARGUMENT
