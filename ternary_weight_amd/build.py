@@ -26,6 +26,10 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-ffp-contract=fast"]
 CXX_FLAGS = ["-ffp-contract=off", "-pthread"]
+# Per-source extras.  The decode kernel keeps its MFMA accumulators in
+# ordinary VGPRs: its epilogue reads them with plain VALU operations instead
+# of v_accvgpr_read copies.
+EXTRA_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -47,7 +51,8 @@ def build(verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
-        jobs.append([hipcc, "-c", *COMMON, *HIP_FLAGS, os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, "-c", *COMMON, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), os.path.join(CSRC, src),
+                     "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)

@@ -14,24 +14,29 @@
 // chunks.  Lane (r = lane % 16, g = lane / 16) loads chunk g of weight row r
 // with one 16-byte load; field f of that chunk holds 16 consecutive K
 // positions (128*(g/2) + 32f + 16*(g%2) + 0..15 of the superblock), so the
-// four fields feed four MFMAs.  The fields are isolated with a mask only
-// (field 1 = code*16, field 2 = code*4) and accumulated separately; the
-// exact powers of two are divided out at the end.  Codes are 0, 1, 2; the
-// activation row sum is subtracted in the epilogue to turn them into
-// -1, 0, +1.
+// four fields feed four MFMAs.  Fields 1..3 are isolated with a mask only
+// (code*16, code*4, code) and accumulated separately, the exact powers of
+// two divided out at the end; field 0 becomes -64 * weight with one
+// three-input bit operation.  Codes are 0, 1, 2, so the activation sum over
+// the field 1..3 positions (the row sum less the field-0 sum, which the
+// matrix core computes once per wave against an all-ones operand) is
+// subtracted at the end to turn them into -1, 0, +1.
 //
 // Work split: a workgroup owns 4*16*T weight rows of one problem and each of
-// its waves T 16-row tiles (T = 4 for K <= 2048, else 2), walked in order
-// with the next tile's weights loading while the current one is processed.
+// its waves T 16-row tiles, walked in order through a rolling window: the
+// weight loads of D tiles are in flight while one is processed (D = 4, 3, 2
+// for up to 4, 8, 16 superblocks; T = 2D).  Accumulators are combined one
+// tile late, once their MFMAs have drained, and all results are stored
+// after the last tile.
 // The kernel is specialised on the number of superblocks NSB = ceil(K/256):
 // a tile's NSB weight loads are issued together and consumed in order, so
 // the compiler's wait counts are exact and the register footprint small.
 // Weights are read with buffer loads: an offset outside the problem's weight
 // bytes returns 0 without a memory access, which replaces the bounds branches
 // (rows >= N, tiles past the end, the missing half of a half superblock).
-// The <= 16 activation rows (plus one all-zero row for the padding lanes) are
-// staged once per workgroup in LDS, zero-padded along K to NSB superblocks;
-// when they do not fit, fragments come from global memory through the same
+// The <= 16 activation rows are staged once per workgroup in LDS with direct
+// global-to-LDS loads, zero-padded along K to NSB superblocks; when they do
+// not fit, fragments come from global memory through the same
 // out-of-range-reads-zero buffer loads.  K beyond 16 superblocks runs a
 // generic variant (one tile per wave, superblocks streamed two ahead).
 // Bound: HBM, K/4 bytes per output column.
@@ -44,41 +49,63 @@ constexpr int kOob = 0x7FFFFFF0;           // buffer offset that always reads 0
 constexpr int kBufferDword3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 constexpr int kMaxNsb = 16;                // specialised superblock counts 1..16
 
+// The four MFMA operands of one 16-byte chunk, one dword at a time.  Fields
+// 1..3 are isolated with a mask only and stay scaled by their bit position
+// (code*16, code*4, code).  Field 0 (bits 7:6) cannot be masked in place,
+// since code 2 * 64 = 128 overflows int8; flipping its low bit first maps
+// codes 0, 1, 2 to bit patterns 1, 0, 3, which read as signed bytes
+// 64, 0, -64: -64 * (code - 1), the ternary weight itself, negated and
+// scaled.  One three-input bit operation per field.
 __device__ __forceinline__ void decode_fields(const v4i& w, v4i& a0, v4i& a1, v4i& a2, v4i& a3) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t d = static_cast<uint32_t>(w[i]);
-    a0[i] = static_cast<int>((d >> 6) & 0x03030303u);  // field 0: code
-    a1[i] = static_cast<int>(d & 0x30303030u);         // field 1: code*16
-    a2[i] = static_cast<int>(d & 0x0C0C0C0Cu);         // field 2: code*4
-    a3[i] = static_cast<int>(d & 0x03030303u);         // field 3: code
+    a0[i] = static_cast<int>((d ^ 0x40404040u) & 0xC0C0C0C0u);  // -64 * weight
+    a1[i] = static_cast<int>(d & 0x30303030u);                  // code * 16
+    a2[i] = static_cast<int>(d & 0x0C0C0C0Cu);                  // code * 4
+    a3[i] = static_cast<int>(d & 0x03030303u);                  // code
   }
 }
 
-constexpr int gemv_tiles(int nsb) { return nsb == 0 ? 1 : (nsb <= 8 ? 4 : 2); }
+// Tiles in flight per wave (the weight loads of D tiles are outstanding while
+// one is processed) and tiles per wave.  Deeper windows for short rows: the
+// in-flight bytes per wave must cover the memory latency.
+constexpr int gemv_depth(int nsb) { return nsb == 0 ? 1 : (nsb <= 4 ? 4 : (nsb <= 8 ? 3 : 2)); }
+constexpr int gemv_tiles(int nsb) { return nsb == 0 ? 1 : 2 * gemv_depth(nsb); }
 
+// Tile result for the lane's activation row r16 and 4 weight rows: the
+// field accumulators combined (field 0 carries -64 * weight, fields 1..3
+// code * 16, code * 4, code), minus rs123, the activation sum over the
+// field 1..3 positions (codes -> weights there), and for the forward the
+// scale applied; returned as raw bits.  All shifts are exact.
 template <bool RAW>
-__device__ __forceinline__ void gemv_epilogue(const Prob& P, const v4i* acc, int nrow, int r16,
-                                              int rs, float scale) {
+__device__ __forceinline__ v4i gemv_result(const v4i* acc, int rs123, float scale) {
+  const v4i v = (acc[1] >> 4) + (acc[2] >> 2) + acc[3] - (acc[0] >> 6) - rs123;
+  if (RAW) return v;
+  return __builtin_bit_cast(v4i, f4{static_cast<float>(v[0]) * scale, static_cast<float>(v[1]) * scale,
+                                    static_cast<float>(v[2]) * scale, static_cast<float>(v[3]) * scale});
+}
+
+// Stores a tile result at output row r16, columns nrow..nrow+3 (clipped to N).
+template <bool RAW>
+__device__ __forceinline__ void gemv_store(const Prob& P, const v4i& v, int nrow, int r16) {
   const int N = P.N;
   if (r16 >= P.M || nrow >= N) return;
-  const v4i v = acc[0] + (acc[1] >> 4) + (acc[2] >> 2) + acc[3];
   const int64_t o = static_cast<int64_t>(r16) * N + nrow;
-  if (RAW) {
-    if ((N & 3) == 0) {
-      *gptr_out<v4i>(P.acc + o) = v - rs;
-    } else {
-      for (int i = 0; i < 4 && nrow + i < N; ++i) gptr_out<int32_t>(P.acc)[o + i] = v[i] - rs;
-    }
+  int32_t* out = RAW ? P.acc : reinterpret_cast<int32_t*>(P.y);
+  if ((N & 3) == 0) {
+    *gptr_out<v4i>(out + o) = v;
   } else {
-    const f4 out = f4{static_cast<float>(v[0] - rs) * scale, static_cast<float>(v[1] - rs) * scale,
-                      static_cast<float>(v[2] - rs) * scale, static_cast<float>(v[3] - rs) * scale};
-    if ((N & 3) == 0) {
-      *gptr_out<f4>(P.y + o) = out;
-    } else {
-      for (int i = 0; i < 4 && nrow + i < N; ++i) gptr_out<float>(P.y)[o + i] = out[i];
-    }
+    for (int i = 0; i < 4 && nrow + i < N; ++i) gptr_out<int32_t>(out)[o + i] = v[i];
   }
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in [3:0] and
+// [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // NSB > 0: exactly NSB superblocks per tile.  NSB == 0: any K, streamed.
@@ -87,7 +114,12 @@ __device__ __forceinline__ void gemv_epilogue(const Prob& P, const v4i* acc, int
 template <bool RAW, bool FROM_LDS, int NSB>
 __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* units) {
   constexpr int T = gemv_tiles(NSB);
-  extern __shared__ __attribute__((aligned(16))) int8_t xlds[];
+  constexpr int D = gemv_depth(NSB);
+  constexpr int kHeld = NSB > 0 ? NSB : 2;
+  // Weight loads issued after the activation staging and before its wait.
+  constexpr int kInFlight = D * kHeld;
+  static_assert(kInFlight < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(1024))) int8_t xlds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
@@ -97,6 +129,39 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
   const int rowbytes = K >> 2;
   const int nsb = NSB > 0 ? NSB : (K + 255) >> 8;
   const int kpad = (NSB > 0 ? nsb : (nsb + 1) & ~1) * 256;
+  // Lanes past the M activation rows read row M-1: the MFMA columns they
+  // feed are output rows that are never stored.
+  const int xrow = min(r16, M - 1);
+
+  // Startup order matters: every load whose result the wave waits for before
+  // its first tile (activation staging, row sum, factor) is issued ahead of
+  // the weight loads, so those waits leave the weights in flight.
+  //
+  // Activations go straight to LDS (buffer_load ... lds): each wave
+  // instruction fills 1 KB linearly.  Row m occupies kpad bytes at m*kpad,
+  // its 16-byte slots XOR-swizzled by m % 8 so that the 8 lanes reading one
+  // slot of 8 different rows hit distinct banks; each lane fetches the
+  // global chunk that belongs at its swizzled position.  Positions past K or
+  // past row M-1 read 0 without a memory access (their products meet weight
+  // codes 0 anyway).
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(P.xq), 0, M * K, kBufferDword3);
+  if (FROM_LDS) {
+    const int row_slots = kpad >> 4;
+    const int lds_units = (M * kpad + 1023) >> 10;
+    for (int i = wave; i < lds_units; i += 4) {
+      const int ps = 64 * i + lane;  // physical 16-byte slot
+      const int m = ps / row_slots;
+      const int slot = (ps - m * row_slots) ^ (m & 7);
+      const bool ok = (m < M) & (16 * slot < K);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, (__attribute__((address_space(3))) void*)(xlds + 1024 * i), 16,
+          ok ? m * K + 16 * slot : kOob, 0, 0, 0);
+    }
+  }
+  const int rs = gptr<int32_t>(P.rowsum)[xrow];
+  const float scale = RAW ? 0.f : gptr<float>(P.factor)[xrow] / P.w_scale;
+  asm volatile("" ::: "memory");  // keep the loads above ahead of the weight loads
 
   // Weight loads: lane reads 16 bytes of row tile0 + 16t + r16 at superblock sb.
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -108,45 +173,35 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
     return __builtin_amdgcn_raw_buffer_load_b128(
         wrs, ok ? wbase + 16 * t * rowbytes + 64 * sb : kOob, 0, 0);
   };
+  v4i buf[D][kHeld];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+#pragma unroll
+    for (int sb = 0; sb < kHeld; ++sb) buf[d][sb] = wload(d, sb);
 
-  // Activation fragment (B operand): 16 bytes of row r16 at K offset
-  // 256*sb + 32*f + koff; zero for padding rows and past K.
-  const int xstride = kpad + 16;  // LDS row stride (padding against bank conflicts)
+  if (FROM_LDS) {
+    // The staging loads are complete once at most the weight loads are
+    // outstanding; the barrier then publishes every wave's part.
+    wait_vmcnt<kInFlight>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
+  // Activation fragment (B operand): 16 bytes of row xrow at K offset
+  // 256*sb + 32*f + koff, i.e. logical slot 16*sb + 8*(g/2) + 2*f + g%2.
   const int koff = 128 * (g >> 1) + 16 * (g & 1);
-  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(P.xq), 0, M * K, kBufferDword3);
-  const int8_t* xl = xlds + min(r16, M) * xstride + koff;
+  const int8_t* xl = xlds + xrow * kpad + 128 * (g >> 1);
+  const int xsw = xrow & 7;
   auto xfrag = [&](int sb, int f) -> v4i {
+    if (FROM_LDS)
+      return *reinterpret_cast<const v4i*>(xl + 256 * sb + 16 * ((2 * f + (g & 1)) ^ xsw));
     const int k = 256 * sb + 32 * f;
-    if (FROM_LDS) return *reinterpret_cast<const v4i*>(xl + k);
     const bool ok = (r16 < M) & (k + koff < K);
     return __builtin_amdgcn_raw_buffer_load_b128(xrs, ok ? r16 * K + koff + k : kOob, 0, 0);
   };
 
-  constexpr int kHeld = NSB > 0 ? NSB : 2;
-  v4i wa[kHeld], wb[kHeld];
-  // The first tile's loads go out before the activation staging and its barrier.
-#pragma unroll
-  for (int sb = 0; sb < kHeld; ++sb) wa[sb] = wload(0, sb);
-
-  if (FROM_LDS) {
-    // Rows 0..M-1: activations zero-padded to kpad; row M: zeros.
-    const int row_chunks = kpad >> 4;
-    for (int c = threadIdx.x; c < (M + 1) * row_chunks; c += 256) {
-      const int m = c / row_chunks, o = (c - m * row_chunks) << 4;
-      v4i v = v4i{0, 0, 0, 0};
-      if (m < M && o < K) v = *gptr<v4i>(P.xq + static_cast<int64_t>(m) * K + o);
-      *reinterpret_cast<v4i*>(xlds + m * xstride + o) = v;
-    }
-    __syncthreads();
-  }
-
-  const int rs = r16 < M ? gptr<int32_t>(P.rowsum)[r16] : 0;
-  float scale = 0.f;
-  if (!RAW && r16 < M) scale = gptr<float>(P.factor)[r16] / P.w_scale;
-
-  v4i acc[4];
-  auto process = [&](const v4i& wv, int sb) {
+  auto process = [&](v4i* acc, const v4i& wv, int sb) {
     v4i a0, a1, a2, a3;
     decode_fields(wv, a0, a1, a2, a3);
     acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, xfrag(sb, 0), acc[0], 0, 0, 0);
@@ -154,39 +209,66 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
     acc[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, xfrag(sb, 2), acc[2], 0, 0, 0);
     acc[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, xfrag(sb, 3), acc[3], 0, 0, 0);
   };
-  auto tile = [&](const v4i* w, int t) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) acc[f] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int sb = 0; sb < kHeld; ++sb) process(w[sb], sb);
-    gemv_epilogue<RAW>(P, acc, tile0 + 16 * t + 4 * g, r16, rs, scale);
-  };
+
+  // Activation sum over the field-0 positions of row r16, by the idle matrix
+  // core (an all-ones A operand): rs123 = row sum - that is the sum over the
+  // field 1..3 positions, whose codes the epilogue turns into weights.
+  int rs123;
+  {
+    const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    v4i s0 = v4i{0, 0, 0, 0};
+    for (int sb = 0; sb < nsb; ++sb)
+      s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, xfrag(sb, 0), s0, 0, 0, 0);
+    rs123 = rs - s0[0];
+  }
 
   if (NSB > 0) {
-    // Tiles in pairs through the two buffers; past the wave's last tile the
-    // loads read 0 and the epilogue stores nothing.
+    // A rolling window of D tiles: tile t is processed while t+1..t+D-1
+    // load, then its buffer is refilled with tile t+D.  Past the wave's last
+    // row the loads read 0 and nothing is stored.  Tile t's accumulators are
+    // combined one tile later, when its MFMAs have drained, and results are
+    // held in registers until the end: a store counts against vmcnt like a
+    // load, so waits on later weight loads would also wait for it.
+    v4i acc[2][4];
+    v4i res[T];
+    auto finish = [&](int t) {
+      v4i r = gemv_result<RAW>(acc[t & 1], rs123, scale);
+      asm volatile("" : "+v"(r));  // combine here: frees the accumulators for tile t + 2
+      res[t] = r;
+    };
 #pragma unroll
-    for (int t = 0; t < T; t += 2) {
+    for (int t = 0; t < T; ++t) {
+      // The activation fragments are re-read from LDS for every tile rather
+      // than held in registers: registers are worth more as load buffers.
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int sb = 0; sb < kHeld; ++sb) wb[sb] = wload(t + 1, sb);
-      tile(wa, t);
+      for (int f = 0; f < 4; ++f) acc[t & 1][f] = v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int sb = 0; sb < kHeld; ++sb) wa[sb] = wload(t + 2, sb);
-      tile(wb, t + 1);
+      for (int sb = 0; sb < kHeld; ++sb) process(acc[t & 1], buf[t % D][sb], sb);
+      if (t + D < T) {
+#pragma unroll
+        for (int sb = 0; sb < kHeld; ++sb) buf[t % D][sb] = wload(t + D, sb);
+      }
+      if (t > 0) finish(t - 1);
     }
+    finish(T - 1);
+#pragma unroll
+    for (int t = 0; t < T; ++t) gemv_store<RAW>(P, res[t], tile0 + 16 * t + 4 * g, r16);
   } else {
     // Generic K, one tile: two superblocks in flight, pairs processed
     // unconditionally (past nsb both operands are zero: loads read 0,
     // staging is padded).
+    v4i acc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[f] = v4i{0, 0, 0, 0};
+    v4i* w = buf[0];
     for (int sb = 0; sb < nsb; sb += 2) {
-      process(wa[0], sb);
-      wa[0] = wload(0, sb + 2);
-      process(wa[1], sb + 1);
-      wa[1] = wload(0, sb + 3);
+      process(acc, w[0], sb);
+      w[0] = wload(0, sb + 2);
+      process(acc, w[1], sb + 1);
+      w[1] = wload(0, sb + 3);
     }
-    gemv_epilogue<RAW>(P, acc, tile0 + 4 * g, r16, rs, scale);
+    gemv_store<RAW>(P, gemv_result<RAW>(acc, rs123, scale), tile0 + 4 * g, r16);
   }
 }
 
@@ -202,12 +284,14 @@ int gemv_units(int N, int bucket) {
 
 namespace {
 
-// Staged K of a launch: the bucket's superblocks, or for the generic variant
-// the largest K rounded up to a pair of superblocks (processed in pairs).
+// Staged activation bytes of a launch: max_m rows of the bucket's
+// superblocks (for the generic variant the largest K rounded up to a pair of
+// superblocks), rounded up to the 1 KB granule of the direct LDS loads.
 size_t gemv_lds_bytes(int bucket, int max_m, int max_k) {
   int nsb = bucket > 0 ? bucket : (max_k + 255) >> 8;
   if (bucket == 0) nsb = (nsb + 1) & ~1;
-  return static_cast<size_t>(max_m + 1) * (static_cast<size_t>(nsb) * 256 + 16);
+  const size_t bytes = static_cast<size_t>(max_m) * static_cast<size_t>(nsb) * 256;
+  return (bytes + 1023) / 1024 * 1024;
 }
 
 template <bool RAW, bool LDS>
