@@ -108,32 +108,37 @@ class Arena:
 def run_timed(torch, group, steps: int, warmup: int):
     """Warm up, then time exactly `steps` steps.
 
-    A step is the quantization launch followed by every matmul launch, all on
-    the current stream; HIP events bracket each launch (events are recorded
-    on the stream the kernels run on).  Returns the wall-clock ms per step
-    and the mean ms of the quant launch, of the whole matmul stage and of
-    each matmul launch.
+    A step is the group's forward: every forward launch in order on the
+    current stream; HIP events bracket each launch (recorded on the stream the
+    kernels run on).  Returns the wall-clock ms per step, the launch list and
+    the mean ms of each launch.
     """
     stream = torch.cuda.current_stream()
-    nl = len(group.launches())
+    info = group.forward_launches()
+    nl = len(info)
     for _ in range(warmup):
         group.forward()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 2)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
     for e in ev:
         e[0].record(stream)
-        group.quant()
-        e[1].record(stream)
         for i in range(nl):
-            group.matmul_launch(i)
-            e[i + 2].record(stream)
+            group.forward_launch(i)
+            e[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    mm_ms = float(np.mean([e[1].elapsed_time(e[nl + 1]) for e in ev]))
-    launch_ms = [float(np.mean([e[i + 1].elapsed_time(e[i + 2]) for e in ev])) for i in range(nl)]
-    return wall * 1e3 / steps, quant_ms, mm_ms, launch_ms
+    launch_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(nl)]
+    return wall * 1e3 / steps, info, launch_ms
+
+
+def launch_bytes(kind: str, M: int, K: int, N: int) -> int:
+    """Algorithmic HBM bytes of one BitLinear in a launch of the given kind."""
+    if kind in ("decode", "prefill"):  # packed weights, int8 codes, factor + row sum, fp32 y
+        return N * K // 4 + M * K + 8 * M + 4 * M * N
+    if kind == "quant":          # fp32 x and norm weight in, int8 codes, factor + row sum out
+        return 4 * M * K + 4 * K + M * K + 8 * M
+    raise ValueError(kind)
 
 
 def traffic_from_profiles(kernel_tag: str, source: str):
@@ -181,25 +186,21 @@ def bench_decode(torch, bl, args):
         y = arena.take(4 * N, torch.float32, (1, N))
         items.append(dict(x=x, norm_w=nw, packed_w=pw, w_scale=p["scale"], eps=inputs.EPS, N=N, y=y))
     group = bl.Group(items)
-    launches = group.launches()
-    ms, quant_ms, mm_ms, launch_ms = run_timed(torch, group, args.steps, args.warmup)
+    ms, info, launch_ms = run_timed(torch, group, args.steps, args.warmup)
     group.close()
     weight_bytes = sum(p["N"] * p["K"] // 4 for p in projs)
-    # Algorithmic bytes of a decode launch, per BitLinear: packed weights
-    # N*K/4, int8 activations M*K, factor + row sum 8*M, fp32 outputs 4*M*N
-    # (M = 1).  The decode launches are one per superblock count ceil(K/256).
+    # Algorithmic bytes per launch (launch_bytes, M = 1): the quantization
+    # launch, then one decode launch per superblock count ceil(K/256).
     per_launch = []
-    for info, t in zip(launches, launch_ms):
-        members = [p for p in projs if (p["K"] + 255) // 256 == info["bucket"]]
-        nbytes = sum(p["N"] * p["K"] // 4 + p["K"] + 8 + 4 * p["N"] for p in members)
-        per_launch.append(dict(bucket=info["bucket"], bitlinears=len(members), K=members[0]["K"],
-                               bytes=nbytes, us=t * 1e3, GBps=nbytes / (t * 1e-3) / 1e9))
+    for d, t in zip(info, launch_ms):
+        members = [p for p in projs if (p["K"] + 255) // 256 == d["bucket"]] if d["bucket"] else projs
+        nbytes = sum(launch_bytes(d["kind"], 1, p["K"], p["N"]) for p in members)
+        per_launch.append(dict(kind=d["kind"], bucket=d["bucket"], bitlinears=len(members),
+                               K=members[0]["K"], bytes=nbytes, us=t * 1e3,
+                               GBps=nbytes / (t * 1e-3) / 1e9))
     dom = max(per_launch, key=lambda d: d["bytes"])
-    mm_bytes = sum(d["bytes"] for d in per_launch)
-    return dict(R=R, projs=projs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, per_launch=per_launch,
-                dominant=dom, weight_bytes=weight_bytes, mm_bytes=mm_bytes,
-                stage_GBps=mm_bytes / (mm_ms * 1e-3) / 1e9,
-                value=weight_bytes / (ms * 1e-3) / 1e9)
+    return dict(R=R, projs=projs, ms=ms, per_launch=per_launch, dominant=dom,
+                weight_bytes=weight_bytes, value=weight_bytes / (ms * 1e-3) / 1e9)
 
 
 def bench_prefill(torch, bl, args):
@@ -219,8 +220,10 @@ def bench_prefill(torch, bl, args):
                           eps=inputs.EPS, N=p["N"],
                           y=torch.empty((w.M, p["N"]), dtype=torch.float32, device=dev)))
     group = bl.Group(items)
-    ms, quant_ms, mm_ms, _ = run_timed(torch, group, max(3, args.steps // 2), max(1, args.warmup // 2))
+    ms, info, launch_ms = run_timed(torch, group, max(3, args.steps // 2), max(1, args.warmup // 2))
     group.close()
+    assert [d["kind"] for d in info] == ["quant", "prefill"], info
+    quant_ms, mm_ms = launch_ms
     ops = sum(2 * w.M * p["N"] * p["K"] for p in projs)
     return dict(projs=projs, xs=xs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, ops=ops, M=w.M,
                 tops=ops / (ms * 1e-3) / 1e12, mm_tops=ops / (mm_ms * 1e-3) / 1e12)
@@ -323,10 +326,9 @@ def main():
     log(f"measured peaks: {peaks}")
     dec = bench_decode(torch, bl, args)
     dom = dec["dominant"]
-    log(f"decode: {dec['ms']:.3f} ms/step, {dec['value']:.0f} GB/s weights; "
-        f"quant {dec['quant_ms'] * 1e3:.1f} us, matmul stage {dec['mm_ms'] * 1e3:.1f} us "
-        f"({dec['stage_GBps']:.0f} GB/s algorithmic); launches: "
-        + ", ".join(f"K={d['K']} {d['us']:.1f} us {d['GBps']:.0f} GB/s" for d in dec["per_launch"]))
+    log(f"decode: {dec['ms']:.3f} ms/step, {dec['value']:.0f} GB/s weights; launches: "
+        + ", ".join(f"{d['kind']} K={d['K']} {d['us']:.1f} us {d['GBps']:.0f} GB/s"
+                    for d in dec["per_launch"]))
     traffic = traffic_from_profiles("gemv_decode_k1024", "gemv.hip")
     out = {
         "metric": METRIC,
@@ -357,9 +359,8 @@ def main():
             "algorithmic_bytes_per_launch": dom["bytes"],
             "avg_launch_us": round(dom["us"], 2),
         },
-        "stages_us": {"quant": round(dec["quant_ms"] * 1e3, 2), "matmul": round(dec["mm_ms"] * 1e3, 2),
-                      "matmul_launches": [{"K": d["K"], "us": round(d["us"], 2),
-                                           "GBps": round(d["GBps"], 1)} for d in dec["per_launch"]]},
+        "launches_us": [{"kind": d["kind"], "K": d["K"], "bitlinears": d["bitlinears"],
+                         "us": round(d["us"], 2), "GBps": round(d["GBps"], 1)} for d in dec["per_launch"]],
         "measured_peaks": peaks,
     }
     out["roofline"]["frac_of_measured"] = round(dom["GBps"] / peaks["hbm_read_GBps"], 4)

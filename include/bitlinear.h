@@ -142,6 +142,11 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
  * for the rest).  Results are bit-identical to separate bitlinear_forward
  * calls on the same inputs.
  */
+
+/* Kinds of launch reported by the per-launch calls below. */
+#define BL_LAUNCH_DECODE 0  /* decode product (M <= 16) */
+#define BL_LAUNCH_PREFILL 1 /* tiled product (M > 16) */
+#define BL_LAUNCH_QUANT 2   /* RMSNorm + int8 quantization of every descriptor */
 typedef struct bl_desc {
     const float* x;          /* device [M][K] */
     const float* norm_w;     /* device [K] */
@@ -177,14 +182,22 @@ bl_status bl_group_matmul(bl_group* g, void* stream);
  * superblock count ceil(K/256), in increasing order, then all prefill
  * problems (M > 16) as one launch.  bl_group_matmul == every launch in order.
  *   bl_group_matmul_launches: number of launches (>= 0; -1 for a NULL group).
- *   bl_group_matmul_launch_info: kind 0 = decode launch (bucket = its
- *     superblock count, 0 for K > 4096), 1 = prefill launch (bucket = 0);
+ *   bl_group_matmul_launch_info: kind BL_LAUNCH_DECODE (bucket = its
+ *     superblock count, 0 for K > 4096) or BL_LAUNCH_PREFILL (bucket = 0);
  *     count = problems in the launch.  Null outputs are skipped.
  *   bl_group_matmul_launch: enqueue launch i (0-based) on stream. */
 int32_t bl_group_matmul_launches(const bl_group* g);
 bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kind, int32_t* bucket,
                                       int32_t* count);
 bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream);
+/* The whole forward as individual launches: launch 0 is the quantization
+ * (kind BL_LAUNCH_QUANT, bucket 0, count = problems), launch i >= 1 is matmul
+ * launch i-1.  bl_group_forward == every forward launch in order.
+ *   bl_group_forward_launches: number of launches (-1 for a NULL group). */
+int32_t bl_group_forward_launches(const bl_group* g);
+bl_status bl_group_forward_launch_info(const bl_group* g, int32_t i, int32_t* kind,
+                                       int32_t* bucket, int32_t* count);
+bl_status bl_group_forward_launch(bl_group* g, int32_t i, void* stream);
 
 /* Frees the group (synchronises the device first). NULL is a no-op. */
 bl_status bl_group_destroy(bl_group* g);

@@ -32,6 +32,9 @@ BL_ERR_INTERNAL = -7
 
 _p, _i64, _f32, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32
 
+# BL_LAUNCH_* of include/bitlinear.h
+LAUNCH_KINDS = {0: "decode", 1: "prefill", 2: "quant"}
+
 
 class BlDesc(ctypes.Structure):
     """Mirror of ``bl_desc``."""
@@ -55,6 +58,9 @@ _SIGS = {
     "bl_group_matmul_launches": ([_p], _i32),
     "bl_group_matmul_launch_info": ([_p, _i32, _p, _p, _p], _i32),
     "bl_group_matmul_launch": ([_p, _i32, _p], _i32),
+    "bl_group_forward_launches": ([_p], _i32),
+    "bl_group_forward_launch_info": ([_p, _i32, _p, _p, _p], _i32),
+    "bl_group_forward_launch": ([_p, _i32, _p], _i32),
     "bl_release_workspace": ([], _i32),
     # measurement probes (include/bitlinear_probe.h)
     "bl_probe_read": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
@@ -211,21 +217,32 @@ class Group:
     def matmul(self, stream=None) -> None:
         _check(_lib.bl_group_matmul(self._h, _stream_handle(stream)), "bl_group_matmul")
 
+    def _launch_list(self, n_fn, info_fn, what) -> list[dict]:
+        out = []
+        for i in range(n_fn(self._h)):
+            kind, bucket, count = _i32(), _i32(), _i32()
+            _check(info_fn(self._h, i, ctypes.byref(kind), ctypes.byref(bucket), ctypes.byref(count)),
+                   what)
+            out.append(dict(kind=LAUNCH_KINDS[kind.value], bucket=bucket.value, count=count.value))
+        return out
+
     def launches(self) -> list[dict]:
         """The matmul stage's launches: kind ("decode"/"prefill"), bucket, count."""
-        out = []
-        for i in range(_lib.bl_group_matmul_launches(self._h)):
-            kind, bucket, count = _i32(), _i32(), _i32()
-            _check(_lib.bl_group_matmul_launch_info(self._h, i, ctypes.byref(kind),
-                                                    ctypes.byref(bucket), ctypes.byref(count)),
-                   "bl_group_matmul_launch_info")
-            out.append(dict(kind="decode" if kind.value == 0 else "prefill",
-                            bucket=bucket.value, count=count.value))
-        return out
+        return self._launch_list(_lib.bl_group_matmul_launches, _lib.bl_group_matmul_launch_info,
+                                 "bl_group_matmul_launch_info")
 
     def matmul_launch(self, i: int, stream=None) -> None:
         _check(_lib.bl_group_matmul_launch(self._h, i, _stream_handle(stream)),
                "bl_group_matmul_launch")
+
+    def forward_launches(self) -> list[dict]:
+        """The forward's launches: kind ("quant"/"decode"/"prefill"), bucket, count."""
+        return self._launch_list(_lib.bl_group_forward_launches, _lib.bl_group_forward_launch_info,
+                                 "bl_group_forward_launch_info")
+
+    def forward_launch(self, i: int, stream=None) -> None:
+        _check(_lib.bl_group_forward_launch(self._h, i, _stream_handle(stream)),
+               "bl_group_forward_launch")
 
     def close(self) -> None:
         if self._h:

@@ -469,7 +469,7 @@ bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kin
                                       int32_t* count) {
   if (!g || i < 0 || i >= bl_group_matmul_launches(g)) return BL_ERR_INVALID_ARGUMENT;
   const bool decode = i < static_cast<int32_t>(g->gemv.size());
-  if (kind) *kind = decode ? 0 : 1;
+  if (kind) *kind = decode ? BL_LAUNCH_DECODE : BL_LAUNCH_PREFILL;
   if (bucket) *bucket = decode ? g->gemv[i].first : 0;
   if (count) *count = decode ? g->gemv[i].second.count : g->gemm.count;
   return BL_OK;
@@ -508,6 +508,27 @@ bl_status bl_group_forward(bl_group* g, void* stream) {
   bl_status st = bl_group_quant(g, stream);
   if (st != BL_OK) return st;
   return bl_group_matmul(g, stream);
+}
+
+// Forward launches: the quantization launch, then the matmul launches.
+int32_t bl_group_forward_launches(const bl_group* g) {
+  if (!g) return -1;
+  return 1 + bl_group_matmul_launches(g);
+}
+
+bl_status bl_group_forward_launch_info(const bl_group* g, int32_t i, int32_t* kind,
+                                       int32_t* bucket, int32_t* count) {
+  if (!g || i < 0 || i >= bl_group_forward_launches(g)) return BL_ERR_INVALID_ARGUMENT;
+  if (i > 0) return bl_group_matmul_launch_info(g, i - 1, kind, bucket, count);
+  if (kind) *kind = BL_LAUNCH_QUANT;
+  if (bucket) *bucket = 0;
+  if (count) *count = g->quant.count;
+  return BL_OK;
+}
+
+bl_status bl_group_forward_launch(bl_group* g, int32_t i, void* stream) {
+  if (!g || i < 0 || i >= bl_group_forward_launches(g)) return BL_ERR_INVALID_ARGUMENT;
+  return i == 0 ? bl_group_quant(g, stream) : bl_group_matmul_launch(g, i - 1, stream);
 }
 
 bl_status bl_group_destroy(bl_group* g) {

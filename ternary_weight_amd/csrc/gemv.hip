@@ -96,7 +96,11 @@ __device__ __forceinline__ void gemv_store(const Prob& P, const v4i& v, int nrow
   if ((N & 3) == 0) {
     *gptr_out<v4i>(out + o) = v;
   } else {
-    for (int i = 0; i < 4 && nrow + i < N; ++i) gptr_out<int32_t>(out)[o + i] = v[i];
+    // Ragged N: at most four guarded stores (a bounded count keeps the
+    // compiler's wait-count bookkeeping for the weight loads exact).
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (nrow + i < N) gptr_out<int32_t>(out)[o + i] = v[i];
   }
 }
 

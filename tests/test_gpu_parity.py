@@ -199,6 +199,84 @@ def test_hooks_compose_to_forward_bitwise():
         assert torch.equal(y, y2)
 
 
+COMPOSE_CASES = [(M, K) for K in (640, 1152, 3072, 4096) for M in (1, 2, 3, 4, 5, 8, 9, 13, 16)]
+
+
+@pytest.mark.parametrize("M,K", COMPOSE_CASES)
+def test_forward_matches_hooks_bitwise(M, K):
+    # forward == fp32 epilogue of matmul_i32 o quant over decode shapes with
+    # half superblocks; rows: heavy tailed, one all-zero, one tiny (the
+    # double-precision code path), one one-hot.
+    N = 96
+    x, nw, packed, scale = proj_inputs(17, M, K, M, K, N, heavy=True)
+    x[M // 2] = 0.0
+    if M > 2:
+        x[1] *= 1e-36
+    if M > 3:
+        x[3] = 0.0
+        x[3, K // 3] = -2.5
+    dx, dn, dp = dev(x), dev(nw), dev(packed)
+    y = bl.bitlinear_forward(dx, dn, dp, scale, N, EPS)
+    xq, f = bl.bitlinear_quant(dx, dn, EPS)
+    acc = bl.bitlinear_matmul_i32(xq, dp, N)
+    y2 = acc.to(torch.float32) * (f / torch.tensor(scale, dtype=torch.float32, device=DEV))[:, None]
+    assert torch.equal(y, y2)
+    assert rel_l2(host(y), oracle.bitlinear(x, nw, packed, N, EPS)) <= 1e-3
+
+
+def test_group_forward_launch_kinds_and_order():
+    # The forward as launches: quantization, decode launches by increasing
+    # superblock count (3, 4, 16), then the prefill launch.
+    specs = [(1, 1024, 64), (8, 640, 40), (16, 4096, 32), (3, 1024, 48), (40, 1024, 72),
+             (2, 4096, 24)]
+    items, singles = [], []
+    for i, (M, K, N) in enumerate(specs):
+        x, nw, packed, scale = proj_inputs(18, i, 0, M, K, N)
+        it = dict(x=dev(x), norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                  y=torch.full((M, N), float("nan"), device=DEV))
+        items.append(it)
+        singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, N, EPS))
+    with bl.Group(items) as g:
+        info = g.forward_launches()
+        assert [d["kind"] for d in info] == ["quant", "decode", "decode", "decode", "prefill"]
+        assert [d["bucket"] for d in info] == [0, 3, 4, 16, 0]
+        assert [d["count"] for d in info] == [6, 1, 2, 2, 1]
+        for i in range(len(info)):
+            g.forward_launch(i)
+        torch.cuda.synchronize()
+        for it, ys in zip(items, singles):
+            assert torch.equal(it["y"], ys)
+
+
+def test_large_mixed_group():
+    # About 2000 64-row blocks over 40 decode problems of mixed K (1 to 16
+    # superblocks, half superblocks), M and ragged N, in one group: the same
+    # results as separate calls and, on sampled problems, the oracle's.
+    Ks = (640, 1024, 1152, 2048, 3072, 4096, 128, 384)
+    Ms = (1, 2, 5, 16, 1, 3, 7, 1)
+    items, refs = [], []
+    for i in range(40):
+        K, M = Ks[i % len(Ks)], Ms[(i // 3) % len(Ms)]
+        N = 3072 if i % 5 else 1000
+        x, nw, packed, scale = proj_inputs(19, i, 0, M, K, N, heavy=(i % 4 == 1))
+        if M > 2:
+            x[M - 1] = 0.0
+        it = dict(x=dev(x), norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                  y=torch.full((M, N), float("nan"), device=DEV))
+        items.append(it)
+        refs.append((x, nw, packed, N))
+    singles = [bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], it["w_scale"], it["N"], EPS)
+               for it in items]
+    with bl.Group(items) as g:
+        g.forward()
+        torch.cuda.synchronize()
+        for it, ys in zip(items, singles):
+            assert torch.equal(it["y"], ys)
+    for i in (0, 7, 13, 22, 39):
+        x, nw, packed, N = refs[i]
+        assert rel_l2(host(singles[i]), oracle.bitlinear(x, nw, packed, N, EPS)) <= 1e-3
+
+
 def test_determinism_nan_poison_and_guards():
     for M in (8, 600):
         K, N = 2048, 1000

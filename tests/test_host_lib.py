@@ -178,3 +178,6 @@ def test_group_validation():
     assert lib.bl_group_matmul_launches(None) == -1
     assert lib.bl_group_matmul_launch(None, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_group_matmul_launch_info(None, 0, None, None, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_group_forward_launches(None) == -1
+    assert lib.bl_group_forward_launch(None, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_group_forward_launch_info(None, 0, None, None, None) == bl.BL_ERR_INVALID_ARGUMENT
