@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="decode layer copies (0 = enough for 1 GiB)")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     return ap.parse_args()
 
 
@@ -254,6 +254,9 @@ def measure_peaks(torch, bl):
     half = nbytes // 2
     src, dst = buf[:half], buf[half:]
     copy = max(2 * half / timed(lambda: bl.probe_copy(src, dst, b)) / 1e9 for b in (4096, 16384))
+    write = {}
+    for nt in (False, True):
+        write[nt] = max(nbytes / timed(lambda: bl.probe_write(buf, b, nt)) / 1e9 for b in (4096, 16384))
     del buf, src, dst
     iters, blocks = 4000, 256 * 8
     mfma = {}
@@ -263,16 +266,33 @@ def measure_peaks(torch, bl):
     return {"hbm_read_GBps": round(max(read.values()), 1),
             "hbm_read_by_blocks": {str(k): round(v, 1) for k, v in read.items()},
             "copy_GBps_read_plus_write": round(copy, 1),
+            "hbm_write_GBps": round(max(write.values()), 1),
+            "hbm_write_by_kind": {"plain": round(write[False], 1), "nontemporal": round(write[True], 1)},
             "mfma_i8_TOPS": round(max(mfma.values()), 1),
             "mfma_i8_TOPS_by_shape": {f"{k}x{k}": round(v, 1) for k, v in mfma.items()}}
 
 
-def cpu_baseline_decode(projs, seconds: float):
-    """The oracle, single-threaded, over the first BitLinears of the decode step."""
+def _oracle_parallel(jobs, threads: int):
+    """Run oracle.bitlinear on every (x, norm_w, packed, N) job with `threads`
+    host threads (the C oracle runs outside the GIL); returns the wall time."""
     import oracle
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda j: oracle.bitlinear(j[0], j[1], j[2], j[3], inputs.EPS), jobs))
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_decode(projs, seconds: float):
+    """The oracle, unchanged, on the BitLinears of the decode step: one host
+    core on the first BitLinears (about `seconds`), then every host core the
+    run may use, each thread running the single-threaded oracle on its own
+    BitLinears (about `seconds` of wall time)."""
+    import oracle
+    jobs = []
     done_bytes, t_used, n = 0, 0.0, 0
     for p in projs:
         x = inputs.activations(2, p["layer"], p["proj"], 1, p["K"])
+        jobs.append((x, p["norm_w"], p["packed"], p["N"]))
         t0 = time.perf_counter()
         oracle.bitlinear(x, p["norm_w"], p["packed"], p["N"], inputs.EPS)
         t_used += time.perf_counter() - t0
@@ -280,13 +300,24 @@ def cpu_baseline_decode(projs, seconds: float):
         n += 1
         if t_used >= seconds:
             break
-    return dict(value=done_bytes / t_used / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"first {n} of {len(projs)} M=1 BitLinears of the decode step "
-                       f"({done_bytes / 1e6:.0f} MB of packed weights, {t_used:.1f} s)")
+    single = dict(value=done_bytes / t_used / 1e9, unit="GB/s", cores=1,
+                  sample=f"first {n} of {len(projs)} BitLinears ({t_used:.1f} s)")
+    P = _threads()
+    m = min(len(projs), max(n, int(n * P * 0.9)))
+    for p in projs[len(jobs):m]:
+        jobs.append((inputs.activations(2, p["layer"], p["proj"], 1, p["K"]), p["norm_w"], p["packed"], p["N"]))
+    wall = _oracle_parallel(jobs[:m], P)
+    nbytes = sum(p["N"] * p["K"] // 4 for p in projs[:m])
+    return dict(value=nbytes / wall / 1e9, unit="GB/s", cores=P, kind="oracle",
+                sample=f"first {m} of {len(projs)} M=1 BitLinears of the decode step "
+                       f"({nbytes / 1e6:.0f} MB of packed weights), {P} threads each running the "
+                       f"single-threaded oracle on its own BitLinears, {wall:.1f} s wall",
+                single_core=single)
 
 
 def cpu_baseline_prefill(pre, seconds: float):
-    """The oracle on sampled token rows of the prefill stack (rows are independent)."""
+    """The oracle on sampled token rows of the prefill stack (rows are
+    independent): one core, then every host core the run may use."""
     import oracle
     rows = inputs.sample_rows(pre["M"], 2, seed=4)
     xs_host = {K: x[torch_rows(x, rows)].cpu().numpy() for K, x in pre["xs"].items()}
@@ -299,9 +330,18 @@ def cpu_baseline_prefill(pre, seconds: float):
         n += 1
         if t_used >= seconds:
             break
-    return dict(value=ops / t_used / 1e12, unit="TOPS", cores=1, kind="oracle",
-                sample=f"{len(rows)} sampled token rows through the first {n} of "
-                       f"{len(pre['projs'])} BitLinears ({t_used:.1f} s)")
+    single = dict(value=ops / t_used / 1e12, unit="TOPS", cores=1,
+                  sample=f"{len(rows)} rows through the first {n} BitLinears ({t_used:.1f} s)")
+    P = _threads()
+    m = min(len(pre["projs"]), max(n, int(n * P * 0.9)))
+    sel = pre["projs"][:m]
+    wall = _oracle_parallel([(xs_host[p["K"]], p["norm_w"], p["packed"], p["N"]) for p in sel], P)
+    ops = sum(2 * len(rows) * p["N"] * p["K"] for p in sel)
+    return dict(value=ops / wall / 1e12, unit="TOPS", cores=P, kind="oracle",
+                sample=f"{len(rows)} sampled token rows through the first {m} of "
+                       f"{len(pre['projs'])} BitLinears, {P} threads each running the "
+                       f"single-threaded oracle on its own BitLinears, {wall:.1f} s wall",
+                single_core=single)
 
 
 def torch_rows(x, rows):

@@ -29,6 +29,11 @@ bl_status bl_probe_read(const void* buf, size_t bytes, uint32_t* sink, int32_t b
  * `blocks` workgroups of 256 threads: exactly `bytes` read and written. */
 bl_status bl_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* stream);
 
+/* Streaming write of `bytes` (16-byte aligned, bytes % 16 == 0) by `blocks`
+ * workgroups of 256 threads, one 16-byte store per thread per step;
+ * nontemporal != 0 uses non-temporal stores. */
+bl_status bl_probe_write(void* dst, size_t bytes, int32_t blocks, int32_t nontemporal, void* stream);
+
 /* int8 matrix-core throughput: each of `blocks` workgroups of 4 waves runs,
  * per wave on register operands, either (shape 16) 4*iters
  * v_mfma_i32_16x16x64_i8 in four independent chains or (shape 32) 2*iters

@@ -65,6 +65,7 @@ _SIGS = {
     # measurement probes (include/bitlinear_probe.h)
     "bl_probe_read": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
     "bl_probe_copy": ([_p, _p, ctypes.c_size_t, _i32, _p], _i32),
+    "bl_probe_write": ([_p, ctypes.c_size_t, _i32, _i32, _p], _i32),
     "bl_probe_mfma_i8": ([_i32, _i32, _i32, _p, _p], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -282,6 +283,13 @@ def probe_copy(src, dst, blocks: int, stream=None) -> None:
         raise ValueError("src and dst sizes differ")
     _check(_lib.bl_probe_copy(_dev(src, torch.uint8, "src"), _dev(dst, torch.uint8, "dst"),
                               src.numel(), blocks, _stream_handle(stream)), "bl_probe_copy")
+
+
+def probe_write(dst, blocks: int, nontemporal: bool = False, stream=None) -> None:
+    """Streaming-write probe over a uint8 device tensor (see bitlinear_probe.h)."""
+    torch = _torch()
+    _check(_lib.bl_probe_write(_dev(dst, torch.uint8, "dst"), dst.numel(), blocks, int(nontemporal),
+                               _stream_handle(stream)), "bl_probe_write")
 
 
 def probe_mfma_i8(iters: int, blocks: int, sink, shape: int = 16, stream=None) -> None:

@@ -13,6 +13,11 @@ constexpr int kWave = 64;
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
+// Raw buffer resources: word 3 for the gfx9 family, and an offset past any
+// buffer's records (loads read 0, stores are dropped, no memory access).
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kOob = 0x7FFFFFF0;
+
 #define BL_GLOBAL __attribute__((address_space(1)))
 #define BL_CONST __attribute__((address_space(4)))
 

@@ -45,8 +45,6 @@
 namespace bl {
 
 constexpr int kGemvLdsBytes = 64 * 1024;   // activation staging limit per workgroup
-constexpr int kOob = 0x7FFFFFF0;           // buffer offset that always reads 0
-constexpr int kBufferDword3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 constexpr int kMaxNsb = 16;                // specialised superblock counts 1..16
 
 // The four MFMA operands of one 16-byte chunk, one dword at a time.  Fields

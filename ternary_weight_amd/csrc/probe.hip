@@ -6,6 +6,8 @@
 //     without any compute);
 //   * copy: read + write of a buffer (the reference for scaling HBM byte
 //     counters: its traffic is known exactly);
+//   * streaming write: every byte of a buffer written once (the prefill
+//     kernel's output stream without any compute);
 //   * int8 MFMA: back-to-back v_mfma_i32_16x16x64_i8 on register operands.
 #include "../../include/bitlinear_probe.h"
 #include "kernels.hpp"
@@ -38,6 +40,18 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const v4i* __restrict__
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
        i += stride)
     dst[i] = src[i];
+}
+
+// Streaming write: every 16-byte word of dst written once (NT: non-temporal).
+template <bool NT>
+__global__ __launch_bounds__(256) void probe_write_kernel(v4i* __restrict__ dst, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const v4i v = v4i{static_cast<int>(threadIdx.x), 1, 2, 3};
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+       i += stride) {
+    if (NT) __builtin_nontemporal_store(v, dst + i);
+    else dst[i] = v;
+  }
 }
 
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -96,6 +110,21 @@ bl_status bl_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks
   hipLaunchKernelGGL(bl::probe_copy_kernel, dim3(blocks), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const bl::v4i*>(src),
                      static_cast<bl::v4i*>(dst), static_cast<int64_t>(bytes / 16));
+  return bl::hip_status(hipGetLastError());
+}
+
+bl_status bl_probe_write(void* dst, size_t bytes, int32_t blocks, int32_t nontemporal,
+                         void* stream) {
+  if (!dst || bytes % 16 != 0 || blocks <= 0) return BL_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(dst) & 15u) != 0) return BL_ERR_MISALIGNED;
+  if (nontemporal)
+    hipLaunchKernelGGL(bl::probe_write_kernel<true>, dim3(blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<bl::v4i*>(dst),
+                       static_cast<int64_t>(bytes / 16));
+  else
+    hipLaunchKernelGGL(bl::probe_write_kernel<false>, dim3(blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<bl::v4i*>(dst),
+                       static_cast<int64_t>(bytes / 16));
   return bl::hip_status(hipGetLastError());
 }
 

@@ -157,6 +157,9 @@ def test_probe_validation():
     assert lib.bl_probe_read(MIS, 64, A, 1, None) == bl.BL_ERR_MISALIGNED
     assert lib.bl_probe_copy(A, MIS, 64, 1, None) == bl.BL_ERR_MISALIGNED
     assert lib.bl_probe_copy(A, A, 64, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_probe_write(None, 64, 1, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_probe_write(A, 63, 1, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_probe_write(MIS, 64, 1, 1, None) == bl.BL_ERR_MISALIGNED
     assert lib.bl_probe_mfma_i8(0, 1, 16, A, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_probe_mfma_i8(1, 1, 8, A, None) == bl.BL_ERR_INVALID_ARGUMENT
 
