@@ -12,9 +12,19 @@
 // fragments of 32 x 32).  K advances one I2_S block (128 positions) per stage.
 // A stage holds the activation tile (128 x 128 int8, 16 KB) and the weight
 // tile still in 2-bit form (256 x 32 B, 8 KB) in LDS; three stages form a
-// ring filled by direct global-to-LDS loads (global_load_lds_dwordx4), two
-// stages ahead of the MFMAs, so no VGPRs stage the copies.  Weights are
-// expanded to int8 right before the MFMA (shift + mask per dword).
+// ring filled by direct global-to-LDS loads (global_load_lds_dwordx4), so no
+// VGPRs stage the copies.  Weights are expanded to int8 right before the
+// MFMA (shift + mask per dword).
+//
+// Software pipeline.  The loads of stage s are issued in the middle of stage
+// s - 3 and awaited in the middle of stage s - 1 (two stages of compute cover
+// their latency).  The middle of a stage is the one synchronisation point:
+// after the k-step 2 MFMAs every wave waits for its LDS reads and its loads
+// of the next stage, a barrier makes all loads visible, the slot just read
+// is refilled, and the next stage's packed weights and first activation
+// fragments are read while the k-step 3 MFMAs run.  Activation fragments
+// are read two k-steps ahead, in the middle of a k-step's MFMAs, so every
+// wait for LDS data finds it already returned.
 //
 // K order inside a block: MFMA step j (0..3) covers positions 32j..32j+31;
 // lane half g = lane/32 supplies positions 32j+16g..+15.  In I2_S those are
@@ -28,12 +38,14 @@
 // to the last row (their results are never stored).
 //
 // The direct loads are tracked by vmcnt only, and the compiler does not wait
-// for them before LDS reads, so the loop waits explicitly: before reading
-// stage kb a wave waits until at most the loads of stage kb+1 are
-// outstanding, then a barrier makes every wave's loads visible.
+// for them before LDS reads, so the loop waits explicitly (vmcnt counts the
+// loads of the stages still allowed in flight); scheduling barriers keep the
+// LDS reads, waits and MFMAs in the order above.
 //
 // Bound: int8 MFMA for K >= 2048; for K <= 1024 the fp32 output (4*M*N bytes)
 // weighs as much as the MFMA time.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace bl {
@@ -65,6 +77,12 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// The same with lgkmcnt = 0: this wave's LDS reads have returned as well.
+template <int N>
+__device__ __forceinline__ void wait_lgkm0_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
 __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* ldst) {
@@ -107,8 +125,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
     const int slot = ws_slot(row, lane & 1);
     woff[i] = min(n0 + row, N - 1) * rowbytes + slot * 16;
   }
-  auto issue = [&](int kb) {
-    uint8_t* st = smem + (kb % kStages) * kStageBytes;
+  auto issue = [&](int kb, int slot_off) {
+    uint8_t* st = smem + slot_off;
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i)
       dma16(P.xq + xoff[i] + kb * kBlockK, st + (kXLoads * wave + i) * 1024);
@@ -122,9 +140,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
-
-  issue(0);
-  if (nblk > 1) issue(1);
 
   // LDS byte offsets of this lane's fragments inside a stage.
   int xrd[4][2];  // [k-step j][fm]
@@ -141,60 +156,110 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
     const int row = wn * 128 + fn * 32 + r32;
     wrd[fn] = kXStage + row * 32 + ws_slot(row, g) * 16;
   }
-
-  for (int kb = 0; kb < nblk; ++kb) {
-    // Stage kb's loads are done once at most stage kb+1's are outstanding.
-    if (kb + 1 < nblk) wait_vmcnt<kLoadsPerStage>();
-    else wait_vmcnt<0>();
-    // Compiler-only fences: no LDS access or direct load may cross the barrier.
+  auto read_w = [&](v4i (&w)[4], const uint8_t* st) {
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn) w[fn] = *reinterpret_cast<const v4i*>(st + wrd[fn]);
+  };
+  auto read_x = [&](v4i (&bx)[2], const uint8_t* st, int j) {
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) bx[fm] = *reinterpret_cast<const v4i*>(st + xrd[j][fm]);
+  };
+  // Part of one k-step: field j of the packed weights of fragments
+  // fn0..fn1-1 against activation fragments bx.
+  auto mma_step = [&](const v4i (&w)[4], const v4i (&bx)[2], int j, int fn0, int fn1) {
+#pragma unroll
+    for (int fn = fn0; fn < fn1; ++fn) {
+      v4i a;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = field_codes(static_cast<uint32_t>(w[fn][i]), j);
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+        acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bx[fm], acc[fn][fm], 0, 0, 0);
+    }
+  };
+  // All waves' direct loads visible, and every wave past its reads so far.
+  // Compiler-only fences keep LDS accesses and direct loads on their side.
+  auto block_sync = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // Every wave is past stage kb-1, whose ring slot stage kb+2 reuses.
-    if (kb + 2 < nblk) issue(kb + 2);
+  };
 
-    const uint8_t* st = smem + (kb % kStages) * kStageBytes;
-    v4i wp[4];  // 16-byte half g of 4 weight rows per lane (one per fragment)
+  // Software pipeline.  Stage s lives in ring slot s % 3; its direct loads
+  // are issued in the middle of stage s - 3 (into the slot stage s - 3 has
+  // just finished reading) and awaited in the middle of stage s - 1, so two
+  // stages of compute cover the load latency.  In the middle of stage kb,
+  // after the k-step 2 MFMAs are issued: wait for this wave's LDS reads and
+  // for stage kb + 1's loads, barrier, refill this slot with stage kb + 3,
+  // and read stage kb + 1's packed weights and first activation fragments
+  // into the other register set while the k-step 3 MFMAs run.
+  issue(0, 0);
+  if (nblk > 1) issue(1, kStageBytes);
+  if (nblk > 2) issue(2, 2 * kStageBytes);
+  if (nblk > 2) wait_vmcnt<2 * kLoadsPerStage>();
+  else if (nblk > 1) wait_vmcnt<kLoadsPerStage>();
+  else wait_vmcnt<0>();
+  block_sync();
+
+  v4i wp[4];     // packed weight half-rows of the current stage
+  v4i bx[4][2];  // activation fragments of k-steps 0..3
+  read_w(wp, smem);
+  read_x(bx[0], smem, 0);
+  read_x(bx[1], smem, 1);
+  int slot = 0;  // byte offset of the current stage's ring slot
+
+  // One stage.  Activation fragments are read two k-steps ahead, in the
+  // middle of a k-step's MFMAs (so that any wait for the older reads never
+  // waits for them).  MID: a later stage exists and the middle-of-stage
+  // hand-over runs: the k-step 3 operands are decoded first, which frees the
+  // packed weight registers for the next stage's reads.
+  auto stage = [&](auto mid, int kb) {
+    constexpr bool kMid = decltype(mid)::value;
+    const uint8_t* st = smem + slot;
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn) wp[fn] = *reinterpret_cast<const v4i*>(st + wrd[fn]);
-    // Activation fragments run one k-step ahead of the MFMAs.
-    v4i b[2][2];
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm) b[0][fm] = *reinterpret_cast<const v4i*>(st + xrd[0][fm]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j + 1 < 4) {
-#pragma unroll
-        for (int fm = 0; fm < 2; ++fm)
-          b[(j + 1) & 1][fm] = *reinterpret_cast<const v4i*>(st + xrd[j + 1][fm]);
-      }
+    for (int j = 0; j < 2; ++j) {
+      mma_step(wp, bx[j], j, 0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      read_x(bx[j + 2], st, j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(wp, bx[j], j, 2, 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mma_step(wp, bx[2], 2, 0, 4);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kMid) {
+      // Decode the k-step 3 operands now (pinned here, ahead of the waits).
+      v4i a3[4];
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn) {
-        v4i a;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = field_codes(static_cast<uint32_t>(wp[fn][i]), j);
+        for (int i = 0; i < 4; ++i) a3[fn][i] = field_codes(static_cast<uint32_t>(wp[fn][i]), 3);
+        asm volatile("" : "+v"(a3[fn]));
+      }
+      if (kb + 2 < nblk) wait_lgkm0_vmcnt<kLoadsPerStage>();
+      else wait_lgkm0_vmcnt<0>();
+      block_sync();
+      const int next = slot == 2 * kStageBytes ? 0 : slot + kStageBytes;
+      read_w(wp, smem + next);
+      read_x(bx[0], smem + next, 0);
+      read_x(bx[1], smem + next, 1);
+      if (kb + 3 < nblk) issue(kb + 3, slot);
+      slot = next;
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
         for (int fm = 0; fm < 2; ++fm)
-          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[j & 1][fm], acc[fn][fm], 0, 0, 0);
-      }
+          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a3[fn], bx[3][fm], acc[fn][fm], 0, 0, 0);
+    } else {
+      mma_step(wp, bx[3], 3, 0, 4);
     }
-    // Issue order for the stage: the packed weights and the first activation
-    // fragments, then per k-step the next step's fragments ahead of the
-    // decode/MFMA pairs, so LDS latency hides behind the previous step.
-    // (0x100: LDS reads, 0x002: VALU, 0x008: MFMA.)
-#define BL_STEP(ds, valu)                                                 \
-  if (ds) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);              \
-  for (int fn = 0; fn < 4; ++fn) {                                        \
-    __builtin_amdgcn_sched_group_barrier(0x002, valu, 0);                 \
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                    \
-  }
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    BL_STEP(true, 8)
-    BL_STEP(true, 8)
-    BL_STEP(true, 8)
-    BL_STEP(false, 4)
-#undef BL_STEP
-  }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  int kb = 0;
+  for (; kb + 1 < nblk; ++kb) stage(Yes{}, kb);
+  stage(No{}, kb);
 
   // Epilogue.  Fragment (fn, fm) lane holds weight rows 8q + 4g + r (q, r in
   // 0..3) of activation row r32: a store straight from there would write
