@@ -6,10 +6,11 @@ a Qwen3-0.6B-shaped layer (q 1024->2048, k/v 1024->1024, o 2048->1024,
 gate/up 1024->3072, down 3072->1024), in weight GB/s (packed I2_S bytes
 streamed per second).  One layer is 3.93 MB, far below a kernel launch and
 below the 256 MB MALL, so the step runs R distinct seeded copies of the layer
-(R * 3.93 MB >= 1 GiB) as one grouped launch per stage: the weights come from
-HBM, not from a cache, and launch latency is amortised.  A step is the whole
-path for every copy: fused RMSNorm + int8 quantization, then the ternary
-product with the scale epilogue.
+(R * 3.93 MB >= 1 GiB) as one group: the weights come from HBM, not from a
+cache, and launch latency is amortised.  A step is the whole path for every
+copy: RMSNorm + int8 quantization, the ternary product and the scale
+epilogue, which at M = 1 run as one launch per superblock count ceil(K/256)
+(the decode kernel quantizes its rows itself).
 
 Secondary ("prefill"): the 28-layer Qwen3-0.6B projection stack at
 M = 16384 tokens (196 BitLinears, 14.4 T int8-equivalent operations), in
@@ -136,6 +137,8 @@ def launch_bytes(kind: str, M: int, K: int, N: int) -> int:
     """Algorithmic HBM bytes of one BitLinear in a launch of the given kind."""
     if kind in ("decode", "prefill"):  # packed weights, int8 codes, factor + row sum, fp32 y
         return N * K // 4 + M * K + 8 * M + 4 * M * N
+    if kind == "decode_fused":   # packed weights, fp32 x and norm weight, fp32 y
+        return N * K // 4 + 4 * M * K + 4 * K + 4 * M * N
     if kind == "quant":          # fp32 x and norm weight in, int8 codes, factor + row sum out
         return 4 * M * K + 4 * K + M * K + 8 * M
     raise ValueError(kind)
@@ -190,7 +193,8 @@ def bench_decode(torch, bl, args):
     group.close()
     weight_bytes = sum(p["N"] * p["K"] // 4 for p in projs)
     # Algorithmic bytes per launch (launch_bytes, M = 1): the quantization
-    # launch, then one decode launch per superblock count ceil(K/256).
+    # launch when there is one, then one decode launch per superblock count
+    # ceil(K/256).
     per_launch = []
     for d, t in zip(info, launch_ms):
         members = [p for p in projs if (p["K"] + 255) // 256 == d["bucket"]] if d["bucket"] else projs
@@ -391,8 +395,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"gemv_kernel<false,true,{dom['bucket']}> (decode, K={dom['K']}, "
-                      f"{dom['bitlinears']} BitLinears per launch)",
+            "kernel": f"gemv_kernel<false,true,{dom['bucket']},{str(dom['kind'] == 'decode_fused').lower()}> "
+                      f"({dom['kind'].replace('_', ' ')}, K={dom['K']}, {dom['bitlinears']} BitLinears per launch)",
             "achieved": round(dom["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,

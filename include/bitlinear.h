@@ -104,10 +104,14 @@ bl_status i2s_pack(const float* w, int64_t K, int64_t N, uint8_t* packed, size_t
  * in the codes), factor = max|RMSNorm(x)*norm_w| / 127, an all-zero row gives
  * zero codes and factor 0; y = (sum_k code*ternary) * factor / w_scale.
  * M <= 16 takes the weight-streaming decode kernel, larger M the tiled MFMA
- * kernel; both share the same integer result.  Uses a library-owned
- * workspace (M*K + 8*M bytes) per (device, stream); the workspace is grown
- * with hipMalloc when needed, which is not allowed while the stream is being
- * captured into a graph (BL_ERR_UNSUPPORTED).
+ * kernel; both share the same integer result.  When the decode kernel can
+ * stage the fp32 rows on chip (M*(K + 4*K) + 4*K bytes within its 32 KB
+ * budget after rounding, K <= 4096), the quantization runs inside it: one
+ * launch, no workspace, results bit-identical to the two-stage path.
+ * Otherwise the codes go through a library-owned workspace (M*K + 8*M bytes)
+ * per (device, stream); the workspace is grown with hipMalloc when needed,
+ * which is not allowed while the stream is being captured into a graph
+ * (BL_ERR_UNSUPPORTED).
  */
 bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* packed_w,
                             float w_scale, int64_t M, int64_t K, int64_t N, float eps, float* y,
@@ -137,16 +141,21 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
 /*
  * Grouped execution: many independent projections (for example the seven of
  * a layer, or of many layers) run with few launches: one quantization launch
- * for all of them, then the matmul stage (one decode launch per distinct
- * superblock count ceil(K/256) among the M <= 16 problems, one prefill launch
- * for the rest).  Results are bit-identical to separate bitlinear_forward
- * calls on the same inputs.
+ * for all of them that need one, then the matmul stage (one decode launch per
+ * distinct superblock count ceil(K/256) among the M <= 16 problems, split
+ * into fused and unfused ones, one prefill launch for the rest).  Decode
+ * problems that bitlinear_forward would fuse are fused here too: the
+ * quantization stage skips them and their matmul launch reads x and norm_w.
+ * Results are bit-identical to separate bitlinear_forward calls on the same
+ * inputs.
  */
 
 /* Kinds of launch reported by the per-launch calls below. */
 #define BL_LAUNCH_DECODE 0  /* decode product (M <= 16) */
 #define BL_LAUNCH_PREFILL 1 /* tiled product (M > 16) */
-#define BL_LAUNCH_QUANT 2   /* RMSNorm + int8 quantization of every descriptor */
+#define BL_LAUNCH_QUANT 2   /* RMSNorm + int8 quantization of the unfused descriptors */
+#define BL_LAUNCH_DECODE_FUSED 3 /* RMSNorm + quantization + decode product in one
+                                    launch (M <= 16 with on-chip staging) */
 typedef struct bl_desc {
     const float* x;          /* device [M][K] */
     const float* norm_w;     /* device [K] */
@@ -171,28 +180,33 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out);
 
 /* Both stages for every descriptor, enqueued on stream (quant, then matmul). */
 bl_status bl_group_forward(bl_group* g, void* stream);
-/* Stage 1 only: RMSNorm + int8 quantization of every descriptor's x into the
- * group's workspace. */
+/* Stage 1 only: RMSNorm + int8 quantization of every unfused descriptor's x
+ * into the group's workspace (a no-op when every descriptor is fused). */
 bl_status bl_group_quant(bl_group* g, void* stream);
 /* Stage 2 only: integer product + epilogue for every descriptor, reading the
- * workspace written by the last bl_group_quant on the same stream. */
+ * workspace written by the last bl_group_quant on the same stream (fused
+ * decode launches quantize their own rows). */
 bl_status bl_group_matmul(bl_group* g, void* stream);
 /* The matmul stage as individual launches, for callers that time or
  * interleave them: the decode problems (M <= 16) run as one launch per
- * superblock count ceil(K/256), in increasing order, then all prefill
- * problems (M > 16) as one launch.  bl_group_matmul == every launch in order.
+ * superblock count ceil(K/256) and kind (unfused before fused), in increasing
+ * superblock count, then all prefill problems (M > 16) as one launch.
+ * bl_group_matmul == every launch in order.
  *   bl_group_matmul_launches: number of launches (>= 0; -1 for a NULL group).
- *   bl_group_matmul_launch_info: kind BL_LAUNCH_DECODE (bucket = its
- *     superblock count, 0 for K > 4096) or BL_LAUNCH_PREFILL (bucket = 0);
- *     count = problems in the launch.  Null outputs are skipped.
+ *   bl_group_matmul_launch_info: kind BL_LAUNCH_DECODE or
+ *     BL_LAUNCH_DECODE_FUSED (bucket = its superblock count, 0 for
+ *     K > 4096) or BL_LAUNCH_PREFILL (bucket = 0); count = problems in the
+ *     launch.  Null outputs are skipped.
  *   bl_group_matmul_launch: enqueue launch i (0-based) on stream. */
 int32_t bl_group_matmul_launches(const bl_group* g);
 bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kind, int32_t* bucket,
                                       int32_t* count);
 bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream);
-/* The whole forward as individual launches: launch 0 is the quantization
- * (kind BL_LAUNCH_QUANT, bucket 0, count = problems), launch i >= 1 is matmul
- * launch i-1.  bl_group_forward == every forward launch in order.
+/* The whole forward as individual launches: when any descriptor needs the
+ * separate quantization, launch 0 is that (kind BL_LAUNCH_QUANT, bucket 0,
+ * count = its problems) and launch i >= 1 is matmul launch i-1; otherwise
+ * the forward launches are the matmul launches.  bl_group_forward == every
+ * forward launch in order.
  *   bl_group_forward_launches: number of launches (-1 for a NULL group). */
 int32_t bl_group_forward_launches(const bl_group* g);
 bl_status bl_group_forward_launch_info(const bl_group* g, int32_t i, int32_t* kind,

@@ -113,15 +113,15 @@ ProbSet single_set(const Prob& p, int total) {
   return s;
 }
 
-// Stage 2 for one problem: the decode kernel for M <= kGemvMaxM, else the
-// tiled MFMA kernel.
-hipError_t launch_matmul_single(const Prob& p, bool raw, hipStream_t stream) {
+// Stage 2 for one problem: the decode kernel for M <= kGemvMaxM (fused:
+// with stage 1 inside it), else the tiled MFMA kernel.
+hipError_t launch_matmul_single(const Prob& p, bool raw, bool fused, hipStream_t stream) {
   if (p.M <= kGemvMaxM) {
     GemvLaunch L{};
     L.single = p;
     L.units = nullptr;
     L.total = gemv_units(p.N, gemv_bucket(p.K));
-    return launch_gemv(L, raw, gemv_bucket(p.K), p.M, p.K, stream);
+    return launch_gemv(L, raw, gemv_bucket(p.K), p.M, p.K, fused, stream);
   }
   return launch_gemm(single_set(p, gemm_units(p.M, p.N)), raw, stream);
 }
@@ -153,16 +153,10 @@ bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* 
     bl_status st = check_forward(x, norm_w, packed_w, w_scale, M, K, N, eps, y);
     if (st != BL_OK || M == 0) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const WsLayout l = ws_layout(M, K);
-    uint8_t* ws = nullptr;
-    if ((st = acquire_ws(s, l.bytes, &ws)) != BL_OK) return st;
     Prob p{};
     p.x = x;
     p.norm_w = norm_w;
     p.w = packed_w;
-    p.xq = reinterpret_cast<int8_t*>(ws + l.xq);
-    p.factor = reinterpret_cast<float*>(ws + l.factor);
-    p.rowsum = reinterpret_cast<int32_t*>(ws + l.rowsum);
     p.y = y;
     p.acc = nullptr;
     p.w_scale = w_scale;
@@ -170,8 +164,15 @@ bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* 
     p.M = static_cast<int>(M);
     p.K = static_cast<int>(K);
     p.N = static_cast<int>(N);
+    if (gemv_fusable(p.M, p.K)) return from_hip(launch_matmul_single(p, false, true, s));
+    const WsLayout l = ws_layout(M, K);
+    uint8_t* ws = nullptr;
+    if ((st = acquire_ws(s, l.bytes, &ws)) != BL_OK) return st;
+    p.xq = reinterpret_cast<int8_t*>(ws + l.xq);
+    p.factor = reinterpret_cast<float*>(ws + l.factor);
+    p.rowsum = reinterpret_cast<int32_t*>(ws + l.rowsum);
     if ((st = from_hip(launch_quant(single_set(p, quant_units(p.M)), p.K, s))) != BL_OK) return st;
-    return from_hip(launch_matmul_single(p, false, s));
+    return from_hip(launch_matmul_single(p, false, false, s));
   } catch (...) {
     return BL_ERR_INTERNAL;
   }
@@ -226,7 +227,7 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
     p.K = static_cast<int>(K);
     p.N = static_cast<int>(N);
     if ((st = from_hip(launch_rowsum(p, s))) != BL_OK) return st;
-    return from_hip(launch_matmul_single(p, true, s));
+    return from_hip(launch_matmul_single(p, true, false, s));
   } catch (...) {
     return BL_ERR_INTERNAL;
   }
@@ -266,12 +267,13 @@ struct GroupStage {
   int total = 0;
   int count = 0;  // problems
   int max_m = 0, max_k = 0;
+  bool fused = false;  // decode stages: stage 1 runs inside the launch
 };
 
 struct bl_group {
   int device = 0;
   GroupStage quant, gemm;
-  std::vector<std::pair<int, GroupStage>> gemv;  // one stage per superblock bucket
+  std::vector<std::pair<int, GroupStage>> gemv;  // per (superblock bucket, fused)
   void* tables = nullptr;     // device: problem tables and unit tables
   void* workspace = nullptr;  // device: per-problem xq, factor, rowsum
 };
@@ -322,6 +324,53 @@ struct StageHost {
   int nprobs = 0;
 };
 
+// Prefill work order.  Problems are taken in windows of consecutive problems
+// whose packed weights together fit kGemmWindowBytes (a share of one XCD's
+// L2, so the window's weights stay cached while its tiles run); inside a
+// window the problems' tile lists are merged in proportion to their progress,
+// so output-heavy tiles (small K) run beside compute-heavy ones (large K)
+// instead of after them.  Each problem keeps its own tile order.
+constexpr size_t kGemmWindowBytes = size_t{2} << 20;
+
+void interleave_gemm_units(StageHost& h) {
+  if (h.probs.size() < 2) return;
+  std::vector<int> tiles(h.probs.size(), 0);
+  for (const int2& u : h.units) ++tiles[u.x];
+  std::vector<int2> out;
+  out.reserve(h.units.size());
+  size_t p0 = 0;
+  while (p0 < h.probs.size()) {
+    size_t p1 = p0, bytes = 0;
+    while (p1 < h.probs.size()) {
+      const Prob& q = h.probs[p1];
+      const size_t wb = static_cast<size_t>(q.N) * static_cast<size_t>(q.K / 4);
+      if (p1 > p0 && bytes + wb > kGemmWindowBytes) break;
+      bytes += wb;
+      ++p1;
+    }
+    // Merge: repeatedly take the problem whose next tile is least advanced
+    // relative to its tile count (ties to the lower index).
+    std::vector<int> next(p1 - p0, 0);
+    for (;;) {
+      int best = -1;
+      double key = 0.0;
+      for (size_t i = 0; i < next.size(); ++i) {
+        const int t = tiles[p0 + i];
+        if (next[i] >= t) continue;
+        const double k = (next[i] + 0.5) / t;
+        if (best < 0 || k < key) {
+          best = static_cast<int>(i);
+          key = k;
+        }
+      }
+      if (best < 0) break;
+      out.push_back(int2{static_cast<int>(p0) + best, next[best]++});
+    }
+    p0 = p1;
+  }
+  h.units.swap(out);
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,10 +387,11 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       bl_status st = check_forward(d.x, d.norm_w, d.packed_w, d.w_scale, d.M, d.K, d.N, d.eps, d.y);
       if (st != BL_OK) return st;
       if (d.M == 0) continue;
-      units_q += quant_units(static_cast<int>(d.M));
       if (d.M <= kGemvMaxM)
         units_v += gemv_units(static_cast<int>(d.N), gemv_bucket(static_cast<int>(d.K)));
       else units_m += gemm_units(static_cast<int>(d.M), static_cast<int>(d.N));
+      if (d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K))) continue;
+      units_q += quant_units(static_cast<int>(d.M));
       ws_bytes += ws_layout(d.M, d.K).bytes;
     }
     if (units_q > INT32_MAX / 2 || units_v > INT32_MAX / 2 || units_m > INT32_MAX / 2)
@@ -360,20 +410,24 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
     }
 
     StageHost hq, hm;
-    std::map<int, StageHost> hv;  // decode problems by superblock bucket
+    std::map<std::pair<int, bool>, StageHost> hv;  // decode problems by (bucket, fused)
     uint8_t* ws = static_cast<uint8_t*>(g->workspace);
     size_t off = 0;
     for (int32_t i = 0; i < count; ++i) {
       const bl_desc& d = descs[i];
       if (d.M == 0) continue;
-      const WsLayout l = ws_layout(d.M, d.K);
+      const bool fused = d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K));
       Prob p{};
       p.x = d.x;
       p.norm_w = d.norm_w;
       p.w = d.packed_w;
-      p.xq = reinterpret_cast<int8_t*>(ws + off + l.xq);
-      p.factor = reinterpret_cast<float*>(ws + off + l.factor);
-      p.rowsum = reinterpret_cast<int32_t*>(ws + off + l.rowsum);
+      if (!fused) {
+        const WsLayout l = ws_layout(d.M, d.K);
+        p.xq = reinterpret_cast<int8_t*>(ws + off + l.xq);
+        p.factor = reinterpret_cast<float*>(ws + off + l.factor);
+        p.rowsum = reinterpret_cast<int32_t*>(ws + off + l.rowsum);
+        off += l.bytes;
+      }
       p.y = d.y;
       p.acc = nullptr;
       p.w_scale = d.w_scale;
@@ -381,15 +435,15 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       p.M = static_cast<int>(d.M);
       p.K = static_cast<int>(d.K);
       p.N = static_cast<int>(d.N);
-      off += l.bytes;
-      hq.add(p, quant_units(p.M));
+      if (!fused) hq.add(p, quant_units(p.M));
       if (p.M <= kGemvMaxM) {
-        StageHost& sh = hv[gemv_bucket(p.K)];
+        StageHost& sh = hv[{gemv_bucket(p.K), fused}];
         sh.fat = true;
         sh.add(p, gemv_units(p.N, gemv_bucket(p.K)));
       }
       else hm.add(p, gemm_units(p.M, p.N));
     }
+    interleave_gemm_units(hm);
 
     // One device buffer for every table.
     g->gemv.resize(hv.size());
@@ -397,7 +451,8 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
     std::vector<GroupStage*> stages{&g->quant, &g->gemm};
     size_t bi = 0;
     for (auto& kv : hv) {
-      g->gemv[bi].first = kv.first;
+      g->gemv[bi].first = kv.first.first;
+      g->gemv[bi].second.fused = kv.first.second;
       hosts.push_back(&kv.second);
       stages.push_back(&g->gemv[bi].second);
       ++bi;
@@ -469,7 +524,9 @@ bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kin
                                       int32_t* count) {
   if (!g || i < 0 || i >= bl_group_matmul_launches(g)) return BL_ERR_INVALID_ARGUMENT;
   const bool decode = i < static_cast<int32_t>(g->gemv.size());
-  if (kind) *kind = decode ? BL_LAUNCH_DECODE : BL_LAUNCH_PREFILL;
+  if (kind)
+    *kind = decode ? (g->gemv[i].second.fused ? BL_LAUNCH_DECODE_FUSED : BL_LAUNCH_DECODE)
+                   : BL_LAUNCH_PREFILL;
   if (bucket) *bucket = decode ? g->gemv[i].first : 0;
   if (count) *count = decode ? g->gemv[i].second.count : g->gemm.count;
   return BL_OK;
@@ -486,7 +543,7 @@ bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream) {
       GemvLaunch L{};
       L.units = gs.fat;
       L.total = gs.total;
-      return from_hip(launch_gemv(L, false, g->gemv[i].first, gs.max_m, gs.max_k, s));
+      return from_hip(launch_gemv(L, false, g->gemv[i].first, gs.max_m, gs.max_k, gs.fused, s));
     }
     return from_hip(launch_gemm(stage_set(g->gemm), false, s));
   } catch (...) {
@@ -513,13 +570,14 @@ bl_status bl_group_forward(bl_group* g, void* stream) {
 // Forward launches: the quantization launch, then the matmul launches.
 int32_t bl_group_forward_launches(const bl_group* g) {
   if (!g) return -1;
-  return 1 + bl_group_matmul_launches(g);
+  return (g->quant.total > 0 ? 1 : 0) + bl_group_matmul_launches(g);
 }
 
 bl_status bl_group_forward_launch_info(const bl_group* g, int32_t i, int32_t* kind,
                                        int32_t* bucket, int32_t* count) {
   if (!g || i < 0 || i >= bl_group_forward_launches(g)) return BL_ERR_INVALID_ARGUMENT;
-  if (i > 0) return bl_group_matmul_launch_info(g, i - 1, kind, bucket, count);
+  const int32_t q = g->quant.total > 0 ? 1 : 0;
+  if (i >= q) return bl_group_matmul_launch_info(g, i - q, kind, bucket, count);
   if (kind) *kind = BL_LAUNCH_QUANT;
   if (bucket) *bucket = 0;
   if (count) *count = g->quant.count;
@@ -528,7 +586,8 @@ bl_status bl_group_forward_launch_info(const bl_group* g, int32_t i, int32_t* ki
 
 bl_status bl_group_forward_launch(bl_group* g, int32_t i, void* stream) {
   if (!g || i < 0 || i >= bl_group_forward_launches(g)) return BL_ERR_INVALID_ARGUMENT;
-  return i == 0 ? bl_group_quant(g, stream) : bl_group_matmul_launch(g, i - 1, stream);
+  const int32_t q = g->quant.total > 0 ? 1 : 0;
+  return i < q ? bl_group_quant(g, stream) : bl_group_matmul_launch(g, i - q, stream);
 }
 
 bl_status bl_group_destroy(bl_group* g) {

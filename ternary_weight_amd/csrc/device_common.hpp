@@ -128,6 +128,56 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
+// ---- activation quantization arithmetic ------------------------------------
+// Every kernel that quantizes a row uses these, in the same order, so that
+// all of them produce the same codes and the same factor bit for bit.
+//
+// Per lane, Sum(x^2) accumulates the lane's 4-element chunks (chunk c =
+// lane + 64 i, increasing i) in fp32; the wave total is taken in double.
+__device__ __forceinline__ float sq4(const f4& v) {
+  return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+}
+__device__ __forceinline__ float absmax4(const f4& u) {
+  return fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w)));
+}
+// Codes: rne(u * 127/max|u|), clamped to [-127, 127].  Rows whose max|u| is
+// below kTinyAmax take the double-precision multiplier (127/max|u| would
+// overflow fp32).
+constexpr float kTinyAmax = 1e-30f;
+__device__ __forceinline__ int code_f32(float u, float s) {
+  float v = rintf(u * s);  // half to even
+  v = fminf(fmaxf(v, -127.0f), 127.0f);
+  return static_cast<int>(v);
+}
+__device__ __forceinline__ int code_f64(float u, double s) {
+  double v = rint(static_cast<double>(u) * s);
+  v = fmin(fmax(v, -127.0), 127.0);
+  return static_cast<int>(v);
+}
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (static_cast<uint32_t>(a) & 0xffu) | ((static_cast<uint32_t>(b) & 0xffu) << 8) |
+         ((static_cast<uint32_t>(c) & 0xffu) << 16) | ((static_cast<uint32_t>(d) & 0xffu) << 24);
+}
+// The four codes of chunk u (zero for an all-zero row) and their sum.
+__device__ __forceinline__ uint32_t codes4(const f4& u, float amax, int* sum) {
+  int a = 0, b = 0, c = 0, d = 0;
+  if (amax >= kTinyAmax) {
+    const float s = 127.0f / amax;
+    a = code_f32(u.x, s); b = code_f32(u.y, s); c = code_f32(u.z, s); d = code_f32(u.w, s);
+  } else if (amax > 0.f) {
+    const double s = 127.0 / static_cast<double>(amax);
+    a = code_f64(u.x, s); b = code_f64(u.y, s); c = code_f64(u.z, s); d = code_f64(u.w, s);
+  }
+  *sum += a + b + c + d;
+  return pack4(a, b, c, d);
+}
+// factor = max|RMSNorm(x) * norm_w| / 127 = r * max|u| / 127 with
+// r = 1/sqrt(mean(x^2) + eps), in double from the row's Sum(x^2).
+__device__ __forceinline__ float quant_factor(double ss, int K, float eps, float amax) {
+  const double r = 1.0 / sqrt(ss / static_cast<double>(K) + static_cast<double>(eps));
+  return static_cast<float>(r * static_cast<double>(amax) / 127.0);
+}
+
 // ---- I2_S field decode ----------------------------------------------------
 // A little-endian dword holds 4 consecutive bytes j..j+3 of a block.  Field f
 // (0 = bits 7:6 ... 3 = bits 1:0) of those bytes carries elements

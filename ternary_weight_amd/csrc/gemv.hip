@@ -22,8 +22,9 @@
 // matrix core computes once per wave against an all-ones operand) is
 // subtracted at the end to turn them into -1, 0, +1.
 //
-// Work split: a workgroup owns 4*16*T weight rows of one problem and each of
-// its waves T 16-row tiles, walked in order through a rolling window: the
+// Work split: a workgroup owns 4*16*T consecutive weight rows of one problem;
+// wave w takes its 16-row tiles w, w+4, w+8, ... (so at any time the four
+// waves stream one contiguous span), walked in order through a rolling window: the
 // weight loads of D tiles are in flight while one is processed (D = 4, 3, 2
 // for up to 4, 8, 16 superblocks; T = 2D).  Accumulators are combined one
 // tile late, once their MFMAs have drained, and all results are stored
@@ -37,7 +38,11 @@
 // The <= 16 activation rows are staged once per workgroup in LDS with direct
 // global-to-LDS loads, zero-padded along K to NSB superblocks; when they do
 // not fit, fragments come from global memory through the same
-// out-of-range-reads-zero buffer loads.  K beyond 16 superblocks runs a
+// out-of-range-reads-zero buffer loads.  Fused variant (the forward when the
+// fp32 rows fit on chip): the workgroup stages the fp32 rows and the norm
+// weight instead and runs the RMSNorm + int8 quantization itself, with the
+// arithmetic of the quantization kernel, while its first weight loads are in
+// flight; no separate launch and no workspace.  K beyond 16 superblocks runs a
 // generic variant (one tile per wave, superblocks streamed two ahead).
 // Bound: HBM, K/4 bytes per output column.
 #include "kernels.hpp"
@@ -46,6 +51,23 @@ namespace bl {
 
 constexpr int kGemvLdsBytes = 64 * 1024;   // activation staging limit per workgroup
 constexpr int kMaxNsb = 16;                // specialised superblock counts 1..16
+constexpr int kGemvFusedLdsBytes = 32 * 1024;  // fused-variant staging limit per workgroup
+
+// LDS layout of the fused variant (byte offsets): the staged codes (M rows of
+// nsb superblocks), a row table (epilogue scale and row sum of up to 16
+// rows), the fp32 rows and the norm weight, each 1 KB aligned.  Monotonic in
+// M and K, so a launch sized for its largest problem fits every problem.
+struct FusedLds {
+  int rows, x, nw, bytes;
+};
+__host__ __device__ inline FusedLds fused_lds(int M, int K, int nsb) {
+  FusedLds l;
+  l.rows = (M * nsb * 256 + 1023) & ~1023;
+  l.x = l.rows + 1024;
+  l.nw = l.x + ((M * K * 4 + 1023) & ~1023);
+  l.bytes = l.nw + ((K * 4 + 1023) & ~1023);
+  return l;
+}
 
 // The four MFMA operands of one 16-byte chunk, one dword at a time.  Fields
 // 1..3 are isolated with a mask only and stay scaled by their bit position
@@ -113,8 +135,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // NSB > 0: exactly NSB superblocks per tile.  NSB == 0: any K, streamed.
 // The launch covers the by-value problem in `single` (units == nullptr) or
 // the FatUnit table `units`.
-template <bool RAW, bool FROM_LDS, int NSB>
+template <bool RAW, bool FROM_LDS, int NSB, bool FUSED>
 __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* units) {
+  static_assert(!FUSED || (FROM_LDS && !RAW && NSB > 0), "fused: forward, staged, specialised K");
   constexpr int T = gemv_tiles(NSB);
   constexpr int D = gemv_depth(NSB);
   constexpr int kHeld = NSB > 0 ? NSB : 2;
@@ -147,8 +170,25 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
   // past row M-1 read 0 without a memory access (their products meet weight
   // codes 0 anyway).
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(P.xq), 0, M * K, kBufferDword3);
-  if (FROM_LDS) {
+      const_cast<int8_t*>(P.xq), 0, FUSED ? 0 : M * K, kBufferDword3);
+  const FusedLds fl = fused_lds(M, K, NSB);
+  if (FUSED) {
+    // fp32 rows and the norm weight, copied linearly (1 KB per wave
+    // instruction; bytes past either buffer read 0).
+    const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(P.x), 0, M * K * 4, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(P.norm_w), 0, K * 4, kBufferDword3);
+    const int ux = (M * K * 4 + 1023) >> 10, un = (K * 4 + 1023) >> 10;
+    for (int i = wave; i < ux + un; i += 4) {
+      const bool isx = i < ux;
+      const int u = isx ? i : i - ux;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          isx ? frs : nrs,
+          (__attribute__((address_space(3))) void*)(xlds + (isx ? fl.x : fl.nw) + 1024 * u), 16,
+          1024 * u + 16 * lane, 0, 0, 0);
+    }
+  } else if (FROM_LDS) {
     const int row_slots = kpad >> 4;
     const int lds_units = (M * kpad + 1023) >> 10;
     for (int i = wave; i < lds_units; i += 4) {
@@ -161,19 +201,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
           ok ? m * K + 16 * slot : kOob, 0, 0, 0);
     }
   }
-  const int rs = gptr<int32_t>(P.rowsum)[xrow];
-  const float scale = RAW ? 0.f : gptr<float>(P.factor)[xrow] / P.w_scale;
+  int rs = 0;
+  float scale = 0.f;
+  if (!FUSED) {
+    rs = gptr<int32_t>(P.rowsum)[xrow];
+    scale = RAW ? 0.f : gptr<float>(P.factor)[xrow] / P.w_scale;
+  }
   asm volatile("" ::: "memory");  // keep the loads above ahead of the weight loads
 
-  // Weight loads: lane reads 16 bytes of row tile0 + 16t + r16 at superblock sb.
+  // Weight loads: lane reads 16 bytes of row tile0 + 64t + r16 at superblock sb.
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(P.w), 0, N * rowbytes, kBufferDword3);
-  const int tile0 = (unit * 4 + wave) * 16 * T;
+  const int tile0 = (unit * 4 * T + wave) * 16;
   const int wbase = (tile0 + r16) * rowbytes + 16 * g;
   auto wload = [&](int t, int sb) -> v4i {
-    const bool ok = (t < T) & (tile0 + 16 * t + r16 < N) & (sb < nsb) & (64 * sb + 16 * g < rowbytes);
+    const bool ok = (t < T) & (tile0 + 64 * t + r16 < N) & (sb < nsb) & (64 * sb + 16 * g < rowbytes);
     return __builtin_amdgcn_raw_buffer_load_b128(
-        wrs, ok ? wbase + 16 * t * rowbytes + 64 * sb : kOob, 0, 0);
+        wrs, ok ? wbase + 64 * t * rowbytes + 64 * sb : kOob, 0, 0);
   };
   v4i buf[D][kHeld];
 #pragma unroll
@@ -188,6 +232,50 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+  }
+  if (FUSED) {
+    // RMSNorm + absmax int8 quantization of the <= 16 rows, wave w taking
+    // rows w, w+4, ..., while the weight loads are in flight: the codes go
+    // to the staged activation layout (zeros up to the padded length), the
+    // row sum and the epilogue scale to the row table.
+    const int nch = K >> 2;
+    const f4* xf = reinterpret_cast<const f4*>(xlds + fl.x);
+    const f4* nw = reinterpret_cast<const f4*>(xlds + fl.nw);
+    float* row_scale = reinterpret_cast<float*>(xlds + fl.rows);
+    int* row_sum = reinterpret_cast<int*>(xlds + fl.rows + 64);
+    for (int m = wave; m < M; m += 4) {
+      // Two passes over the staged row (no per-lane copy held in registers,
+      // which the weight loads in flight need).
+      float ss = 0.f, amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < NSB; ++j) {
+        const int c = lane + kWave * j;
+        if (c < nch) {
+          const f4 xv = xf[m * nch + c];
+          ss += sq4(xv);
+          amax = fmaxf(amax, absmax4(xv * nw[c]));
+        }
+      }
+      const double ssd = wave_sum(static_cast<double>(ss));
+      amax = wave_max(amax);
+      int sum = 0;
+#pragma unroll
+      for (int j = 0; j < NSB; ++j) {
+        const int c = lane + kWave * j;  // dword c of the padded row
+        const uint32_t q = c < nch ? codes4(xf[m * nch + c] * nw[c], amax, &sum) : 0u;
+        *reinterpret_cast<uint32_t*>(xlds + m * kpad + ((((c >> 2) ^ (m & 7))) << 4) + ((c & 3) << 2)) = q;
+      }
+      sum = wave_sum(sum);
+      if (lane == 0) {
+        row_scale[m] = quant_factor(ssd, K, P.eps, amax) / P.w_scale;
+        row_sum[m] = sum;
+      }
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    rs = row_sum[xrow];
+    scale = row_scale[xrow];
   }
 
   // Activation fragment (B operand): 16 bytes of row xrow at K offset
@@ -255,7 +343,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
     }
     finish(T - 1);
 #pragma unroll
-    for (int t = 0; t < T; ++t) gemv_store<RAW>(P, res[t], tile0 + 16 * t + 4 * g, r16);
+    for (int t = 0; t < T; ++t) gemv_store<RAW>(P, res[t], tile0 + 64 * t + 4 * g, r16);
   } else {
     // Generic K, one tile: two superblocks in flight, pairs processed
     // unconditionally (past nsb both operands are zero: loads read 0,
@@ -296,13 +384,13 @@ size_t gemv_lds_bytes(int bucket, int max_m, int max_k) {
   return (bytes + 1023) / 1024 * 1024;
 }
 
-template <bool RAW, bool LDS>
+template <bool RAW, bool LDS, bool FUSED>
 hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStream_t stream) {
   const dim3 grid(L.total), block(256);
-#define BL_GEMV_CASE(n)                                                                    \
-  case n:                                                                                  \
-    hipLaunchKernelGGL((gemv_kernel<RAW, LDS, n>), grid, block, shmem, stream, L.single,   \
-                       L.units);                                                           \
+#define BL_GEMV_CASE(n)                                                                           \
+  case n:                                                                                         \
+    hipLaunchKernelGGL((gemv_kernel<RAW, LDS, n, FUSED>), grid, block, shmem, stream, L.single,   \
+                       L.units);                                                                  \
     break;
   switch (bucket) {
     BL_GEMV_CASE(1) BL_GEMV_CASE(2) BL_GEMV_CASE(3) BL_GEMV_CASE(4) BL_GEMV_CASE(5)
@@ -310,7 +398,11 @@ hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStrea
     BL_GEMV_CASE(11) BL_GEMV_CASE(12) BL_GEMV_CASE(13) BL_GEMV_CASE(14) BL_GEMV_CASE(15)
     BL_GEMV_CASE(16)
     default:
-      hipLaunchKernelGGL((gemv_kernel<RAW, LDS, 0>), grid, block, shmem, stream, L.single, L.units);
+      if constexpr (!FUSED)
+        hipLaunchKernelGGL((gemv_kernel<RAW, LDS, 0, false>), grid, block, shmem, stream, L.single,
+                           L.units);
+      else
+        return hipErrorInvalidValue;
   }
 #undef BL_GEMV_CASE
   return hipGetLastError();
@@ -318,17 +410,28 @@ hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStrea
 
 }  // namespace
 
+bool gemv_fusable(int M, int K) {
+  const int b = gemv_bucket(K);
+  return M >= 1 && M <= kGemvMaxM && b > 0 &&
+         fused_lds(M, K, b).bytes <= kGemvFusedLdsBytes;
+}
+
 hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,
-                       hipStream_t stream) {
+                       bool fused, hipStream_t stream) {
   if (L.total <= 0) return hipSuccess;
+  if (fused) {
+    if (raw || bucket <= 0) return hipErrorInvalidValue;
+    return launch_bucket<false, true, true>(L, bucket, fused_lds(max_m, max_k, bucket).bytes,
+                                            stream);
+  }
   const size_t shmem = gemv_lds_bytes(bucket, max_m, max_k);
   const bool lds = shmem <= static_cast<size_t>(kGemvLdsBytes);
   if (raw) {
-    return lds ? launch_bucket<true, true>(L, bucket, shmem, stream)
-               : launch_bucket<true, false>(L, bucket, 0, stream);
+    return lds ? launch_bucket<true, true, false>(L, bucket, shmem, stream)
+               : launch_bucket<true, false, false>(L, bucket, 0, stream);
   }
-  return lds ? launch_bucket<false, true>(L, bucket, shmem, stream)
-             : launch_bucket<false, false>(L, bucket, 0, stream);
+  return lds ? launch_bucket<false, true, false>(L, bucket, shmem, stream)
+             : launch_bucket<false, false, false>(L, bucket, 0, stream);
 }
 
 }  // namespace bl

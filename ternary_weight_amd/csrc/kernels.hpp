@@ -37,14 +37,18 @@ hipError_t launch_rowsum(const Prob& p, hipStream_t stream);
 // Stage 2, M <= kGemvMaxM: weight-streaming MFMA decode kernel for one
 // bucket, over one by-value problem (units == nullptr) or a FatUnit table.
 // max_m and max_k bound the launch's M and K (they size the LDS activation
-// staging).
+// staging).  fused: the kernel also runs stage 1 for its rows (RMSNorm +
+// int8 quantization from x and norm_w, same arithmetic as launch_quant), so
+// no quantization launch and no workspace are needed; only for problems
+// with gemv_fusable(M, K) and the forward epilogue.
 struct GemvLaunch {
   Prob single;
   const FatUnit* units;
   int total;
 };
+bool gemv_fusable(int M, int K);
 hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,
-                       hipStream_t stream);
+                       bool fused, hipStream_t stream);
 // Stage 2, M > kGemvMaxM: LDS-tiled MFMA kernel.
 hipError_t launch_gemm(const ProbSet& set, bool raw, hipStream_t stream);
 

@@ -18,28 +18,12 @@
 
 namespace bl {
 
-__device__ __forceinline__ int code_f32(float u, float s) {
-  float v = rintf(u * s);  // half to even
-  v = fminf(fmaxf(v, -127.0f), 127.0f);
-  return static_cast<int>(v);
-}
-__device__ __forceinline__ int code_f64(float u, double s) {
-  double v = rint(static_cast<double>(u) * s);
-  v = fmin(fmax(v, -127.0), 127.0);
-  return static_cast<int>(v);
-}
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-  return (static_cast<uint32_t>(a) & 0xffu) | ((static_cast<uint32_t>(b) & 0xffu) << 8) |
-         ((static_cast<uint32_t>(c) & 0xffu) << 16) | ((static_cast<uint32_t>(d) & 0xffu) << 24);
-}
-
 // Per-row finish shared by both variants: the factor and the row sum.
 __device__ __forceinline__ void finish_row(const Prob& P, int m, double ss, float amax, int rs,
                                            int lane) {
   rs = wave_sum(rs);
   if (lane == 0) {
-    double r = 1.0 / sqrt(ss / static_cast<double>(P.K) + static_cast<double>(P.eps));
-    gptr_out<float>(P.factor)[m] = static_cast<float>(r * static_cast<double>(amax) / 127.0);
+    gptr_out<float>(P.factor)[m] = quant_factor(ss, P.K, P.eps, amax);
     if (P.rowsum) gptr_out<int32_t>(P.rowsum)[m] = rs;
   }
 }
@@ -66,10 +50,9 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
       u[i] = f4{0.f, 0.f, 0.f, 0.f};
       if (c < nch) {
         const f4 xv = xr[c];
-        ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+        ss += sq4(xv);
         u[i] = xv * wr[c];
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(u[i].x), fabsf(u[i].y)),
-                                 fmaxf(fabsf(u[i].z), fabsf(u[i].w))));
+        amax = fmaxf(amax, absmax4(u[i]));
       }
     }
     const double ssd = wave_sum(static_cast<double>(ss));
@@ -77,36 +60,10 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
 
     BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
     int rs = 0;
-    if (amax >= 1e-30f) {
-      const float s = 127.0f / amax;
 #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c = lane + kWave * i;
-        if (c < nch) {
-          const int a = code_f32(u[i].x, s), b = code_f32(u[i].y, s);
-          const int cc = code_f32(u[i].z, s), d = code_f32(u[i].w, s);
-          rs += a + b + cc + d;
-          qrow[c] = pack4(a, b, cc, d);
-        }
-      }
-    } else if (amax > 0.f) {  // tiny row: 127/amax would overflow fp32
-      const double s = 127.0 / static_cast<double>(amax);
-#pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c = lane + kWave * i;
-        if (c < nch) {
-          const int a = code_f64(u[i].x, s), b = code_f64(u[i].y, s);
-          const int cc = code_f64(u[i].z, s), d = code_f64(u[i].w, s);
-          rs += a + b + cc + d;
-          qrow[c] = pack4(a, b, cc, d);
-        }
-      }
-    } else {  // all-zero row: zero codes, factor 0
-#pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c = lane + kWave * i;
-        if (c < nch) qrow[c] = 0u;
-      }
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      if (c < nch) qrow[c] = codes4(u[i], amax, &rs);
     }
     finish_row(P, m, ssd, amax, rs, lane);
   }
@@ -137,33 +94,15 @@ __device__ void quant_stream_row(const Prob& P, int m, int lane) {
   for (int c = lane; c < nch; c += kWave) {
     const f4 xv = xr[c];
     const f4 wv = wr[c];
-    ss += static_cast<double>(xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w);
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xv.x * wv.x), fabsf(xv.y * wv.y)),
-                             fmaxf(fabsf(xv.z * wv.z), fabsf(xv.w * wv.w))));
+    ss += static_cast<double>(sq4(xv));
+    amax = fmaxf(amax, absmax4(xv * wv));
   }
   ss = wave_sum(ss);
   amax = wave_max(amax);
 
   BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
   int rs = 0;
-  const bool tiny = amax < 1e-30f;
-  const float s = amax > 0.f && !tiny ? 127.0f / amax : 0.f;
-  const double sd = amax > 0.f ? 127.0 / static_cast<double>(amax) : 0.0;
-  for (int c = lane; c < nch; c += kWave) {
-    const f4 xv = xr[c];
-    const f4 wv = wr[c];
-    const f4 u = xv * wv;
-    int a = 0, b = 0, cc = 0, d = 0;
-    if (amax > 0.f) {
-      if (!tiny) {
-        a = code_f32(u.x, s); b = code_f32(u.y, s); cc = code_f32(u.z, s); d = code_f32(u.w, s);
-      } else {
-        a = code_f64(u.x, sd); b = code_f64(u.y, sd); cc = code_f64(u.z, sd); d = code_f64(u.w, sd);
-      }
-    }
-    rs += a + b + cc + d;
-    qrow[c] = pack4(a, b, cc, d);
-  }
+  for (int c = lane; c < nch; c += kWave) qrow[c] = codes4(xr[c] * wr[c], amax, &rs);
   finish_row(P, m, ss, amax, rs, lane);
 }
 

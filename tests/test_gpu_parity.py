@@ -225,8 +225,9 @@ def test_forward_matches_hooks_bitwise(M, K):
 
 
 def test_group_forward_launch_kinds_and_order():
-    # The forward as launches: quantization, decode launches by increasing
-    # superblock count (3, 4, 16), then the prefill launch.
+    # The forward as launches: quantization (the problems not fused), decode
+    # launches by increasing superblock count (3 and 4 fused: their fp32 rows
+    # fit the on-chip staging; 16 not), then the prefill launch.
     specs = [(1, 1024, 64), (8, 640, 40), (16, 4096, 32), (3, 1024, 48), (40, 1024, 72),
              (2, 4096, 24)]
     items, singles = [], []
@@ -238,9 +239,9 @@ def test_group_forward_launch_kinds_and_order():
         singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, N, EPS))
     with bl.Group(items) as g:
         info = g.forward_launches()
-        assert [d["kind"] for d in info] == ["quant", "decode", "decode", "decode", "prefill"]
+        assert [d["kind"] for d in info] == ["quant", "decode_fused", "decode_fused", "decode", "prefill"]
         assert [d["bucket"] for d in info] == [0, 3, 4, 16, 0]
-        assert [d["count"] for d in info] == [6, 1, 2, 2, 1]
+        assert [d["count"] for d in info] == [3, 1, 2, 2, 1]
         for i in range(len(info)):
             g.forward_launch(i)
         torch.cuda.synchronize()
@@ -317,11 +318,13 @@ def test_group_matches_separate_calls():
         torch.cuda.synchronize()
         for it, ys in zip(items, singles):
             assert torch.equal(it["y"], ys)
-        # The matmul stage launch by launch: decode buckets (K 640, 1024,
-        # 2048, 3072 -> 3, 4, 8, 12 superblocks) in order, then prefill.
+        # The matmul stage launch by launch: decode buckets (K 1024, 2048,
+        # 3072 -> 4, 8, 12 superblocks) in order, the M = 8 problem unfused
+        # (its fp32 rows exceed the on-chip staging) before the fused M = 1
+        # ones, then prefill.
         info = g.launches()
-        assert [d["kind"] for d in info] == ["decode"] * 3 + ["prefill"]
-        assert [d["bucket"] for d in info[:3]] == [4, 8, 12]
+        assert [d["kind"] for d in info] == ["decode"] + ["decode_fused"] * 3 + ["prefill"]
+        assert [d["bucket"] for d in info[:4]] == [4, 4, 8, 12]
         assert sum(d["count"] for d in info) == len(items)
         for it in items:
             it["y"].fill_(float("nan"))
