@@ -106,31 +106,49 @@ class Arena:
 
 # -------------------------------------------------------------- timing ---
 
-def run_timed(torch, group, steps: int, warmup: int):
-    """Warm up, then time exactly `steps` steps.
+def time_steps(torch, group, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` steps of the group's forward.
 
-    A step is the group's forward: every forward launch in order on the
-    current stream; HIP events bracket each launch (recorded on the stream the
-    kernels run on).  Returns the wall-clock ms per step, the launch list and
-    the mean ms of each launch.
+    A step is one bl_group_forward on the current stream (the fused decode
+    launches run side by side on the group's own streams, forked from and
+    joined back into this one).  The timed region is bracketed by
+    synchronisations; returns the wall-clock ms per step and the mean of HIP
+    events around each step.
     """
     stream = torch.cuda.current_stream()
-    info = group.forward_launches()
-    nl = len(info)
     for _ in range(warmup):
         group.forward()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        group.forward()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def time_launches(torch, group, steps: int):
+    """The forward as individual launches in order on the current stream,
+    HIP events around each (recorded on the stream the kernels run on), over
+    `steps` repetitions: the launch list and the mean ms of each launch."""
+    stream = torch.cuda.current_stream()
+    info = group.forward_launches()
+    nl = len(info)
+    for i in range(nl):
+        group.forward_launch(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(steps)]
     for e in ev:
         e[0].record(stream)
         for i in range(nl):
             group.forward_launch(i)
             e[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     launch_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(nl)]
-    return wall * 1e3 / steps, info, launch_ms
+    return info, launch_ms
 
 
 def launch_bytes(kind: str, M: int, K: int, N: int) -> int:
@@ -189,7 +207,8 @@ def bench_decode(torch, bl, args):
         y = arena.take(4 * N, torch.float32, (1, N))
         items.append(dict(x=x, norm_w=nw, packed_w=pw, w_scale=p["scale"], eps=inputs.EPS, N=N, y=y))
     group = bl.Group(items)
-    ms, info, launch_ms = run_timed(torch, group, args.steps, args.warmup)
+    ms, ms_events = time_steps(torch, group, args.steps, args.warmup)
+    info, launch_ms = time_launches(torch, group, args.steps)
     group.close()
     weight_bytes = sum(p["N"] * p["K"] // 4 for p in projs)
     # Algorithmic bytes per launch (launch_bytes, M = 1): the quantization
@@ -203,7 +222,7 @@ def bench_decode(torch, bl, args):
                                K=members[0]["K"], bytes=nbytes, us=t * 1e3,
                                GBps=nbytes / (t * 1e-3) / 1e9))
     dom = max(per_launch, key=lambda d: d["bytes"])
-    return dict(R=R, projs=projs, ms=ms, per_launch=per_launch, dominant=dom,
+    return dict(R=R, projs=projs, ms=ms, ms_events=ms_events, per_launch=per_launch, dominant=dom,
                 weight_bytes=weight_bytes, value=weight_bytes / (ms * 1e-3) / 1e9)
 
 
@@ -224,7 +243,8 @@ def bench_prefill(torch, bl, args):
                           eps=inputs.EPS, N=p["N"],
                           y=torch.empty((w.M, p["N"]), dtype=torch.float32, device=dev)))
     group = bl.Group(items)
-    ms, info, launch_ms = run_timed(torch, group, max(3, args.steps // 2), max(1, args.warmup // 2))
+    ms, _ = time_steps(torch, group, max(3, args.steps // 2), max(1, args.warmup // 2))
+    info, launch_ms = time_launches(torch, group, max(3, args.steps // 2))
     group.close()
     assert [d["kind"] for d in info] == ["quant", "prefill"], info
     quant_ms, mm_ms = launch_ms
@@ -370,7 +390,8 @@ def main():
     log(f"measured peaks: {peaks}")
     dec = bench_decode(torch, bl, args)
     dom = dec["dominant"]
-    log(f"decode: {dec['ms']:.3f} ms/step, {dec['value']:.0f} GB/s weights; launches: "
+    log(f"decode: {dec['ms']:.3f} ms/step ({dec['ms_events']:.3f} by events), "
+        f"{dec['value']:.0f} GB/s weights; launches: "
         + ", ".join(f"{d['kind']} K={d['K']} {d['us']:.1f} us {d['GBps']:.0f} GB/s"
                     for d in dec["per_launch"]))
     traffic = traffic_from_profiles("gemv_decode_k1024", "gemv.hip")
@@ -392,6 +413,8 @@ def main():
                         f"{dec['R']} distinct seeded layer copies per step (>= 1 GiB of I2_S weights)",
             "M": 1, "bitlinears": len(dec["projs"]), "layer_copies": dec["R"],
             "weight_bytes": dec["weight_bytes"], "parallelism": "single GPU",
+            "step": "one group forward: a fused RMSNorm+quant+decode launch per K bucket, "
+                    "the buckets side by side on the group's streams",
         },
         "roofline": {
             "bound": "hbm",

@@ -178,14 +178,21 @@ typedef struct bl_group bl_group;
  */
 bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out);
 
-/* Both stages for every descriptor, enqueued on stream (quant, then matmul). */
+/* Both stages for every descriptor, enqueued on stream (quant, then matmul).
+ * Fused decode launches (they need no quantization launch) run side by side:
+ * the first on stream, the others on up to three streams the group owns
+ * (default priority), forked from stream and joined back into it with
+ * events, so all of the forward is ordered after earlier work on stream and
+ * before later work on it (graph capture included).  Calls on one group must
+ * not overlap in time. */
 bl_status bl_group_forward(bl_group* g, void* stream);
 /* Stage 1 only: RMSNorm + int8 quantization of every unfused descriptor's x
  * into the group's workspace (a no-op when every descriptor is fused). */
 bl_status bl_group_quant(bl_group* g, void* stream);
 /* Stage 2 only: integer product + epilogue for every descriptor, reading the
  * workspace written by the last bl_group_quant on the same stream (fused
- * decode launches quantize their own rows). */
+ * decode launches quantize their own rows; they run side by side as in
+ * bl_group_forward). */
 bl_status bl_group_matmul(bl_group* g, void* stream);
 /* The matmul stage as individual launches, for callers that time or
  * interleave them: the decode problems (M <= 16) run as one launch per

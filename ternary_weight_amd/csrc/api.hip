@@ -270,12 +270,23 @@ struct GroupStage {
   bool fused = false;  // decode stages: stage 1 runs inside the launch
 };
 
+// Fused decode launches depend on nothing but the caller's earlier work, so
+// a group forward runs them side by side: the first on the caller's stream,
+// the others on up to kAuxStreams streams of the group (default priority),
+// forked from and joined back into the caller's stream with events.  Their
+// tails then overlap instead of idling the GPU between launches.
+constexpr int kAuxStreams = 3;
+
 struct bl_group {
   int device = 0;
   GroupStage quant, gemm;
   std::vector<std::pair<int, GroupStage>> gemv;  // per (superblock bucket, fused)
   void* tables = nullptr;     // device: problem tables and unit tables
   void* workspace = nullptr;  // device: per-problem xq, factor, rowsum
+  int naux = 0;               // auxiliary streams in use
+  hipStream_t aux[kAuxStreams] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kAuxStreams] = {};
 };
 
 namespace {
@@ -296,6 +307,11 @@ ProbSet stage_set(const GroupStage& st) {
 
 void free_group(bl_group* g) {
   if (!g) return;
+  for (int j = 0; j < kAuxStreams; ++j) {
+    if (g->join[j]) (void)hipEventDestroy(g->join[j]);
+    if (g->aux[j]) (void)hipStreamDestroy(g->aux[j]);
+  }
+  if (g->fork) (void)hipEventDestroy(g->fork);
   if (g->tables) (void)hipFree(g->tables);
   if (g->workspace) (void)hipFree(g->workspace);
   delete g;
@@ -497,6 +513,18 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       stages[k]->max_m = hosts[k]->max_m;
       stages[k]->max_k = hosts[k]->max_k;
     }
+    int nfused = 0;
+    for (const auto& st : g->gemv) nfused += st.second.fused ? 1 : 0;
+    g->naux = std::min(std::max(nfused - 1, 0), kAuxStreams);
+    bool ok = g->naux == 0 || hipEventCreateWithFlags(&g->fork, hipEventDisableTiming) == hipSuccess;
+    for (int j = 0; ok && j < g->naux; ++j)
+      ok = hipStreamCreateWithFlags(&g->aux[j], hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&g->join[j], hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+      (void)hipGetLastError();
+      free_group(g);
+      return BL_ERR_HIP;
+    }
     *out = g;
     return BL_OK;
   } catch (...) {
@@ -551,20 +579,60 @@ bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream) {
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Stage 1 (when asked) and stage 2 of a group on `stream`, with the fused
+// decode launches after the first spread over the auxiliary streams.
+bl_status group_run(bl_group* g, hipStream_t s, bool with_quant) {
+  bl_status st = group_current_device(g);
+  if (st != BL_OK) return st;
+  const bool fork = g->naux > 0;
+  if (fork) {
+    if (hipEventRecord(g->fork, s) != hipSuccess) return BL_ERR_HIP;
+    for (int j = 0; j < g->naux; ++j)
+      if (hipStreamWaitEvent(g->aux[j], g->fork, 0) != hipSuccess) return BL_ERR_HIP;
+  }
+  if (with_quant && (st = bl_group_quant(g, s)) != BL_OK) return st;
+  const int32_t n = bl_group_matmul_launches(g);
+  int fused_seen = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    hipStream_t target = s;
+    if (fork && i < static_cast<int32_t>(g->gemv.size()) && g->gemv[i].second.fused &&
+        fused_seen++ > 0)
+      target = g->aux[(fused_seen - 2) % g->naux];
+    if ((st = bl_group_matmul_launch(g, i, target)) != BL_OK) return st;
+  }
+  if (fork) {
+    for (int j = 0; j < g->naux; ++j)
+      if (hipEventRecord(g->join[j], g->aux[j]) != hipSuccess ||
+          hipStreamWaitEvent(s, g->join[j], 0) != hipSuccess)
+        return BL_ERR_HIP;
+  }
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 bl_status bl_group_matmul(bl_group* g, void* stream) {
   if (!g) return BL_ERR_INVALID_ARGUMENT;
-  const int32_t n = bl_group_matmul_launches(g);
-  for (int32_t i = 0; i < n; ++i) {
-    const bl_status st = bl_group_matmul_launch(g, i, stream);
-    if (st != BL_OK) return st;
+  try {
+    return group_run(g, static_cast<hipStream_t>(stream), false);
+  } catch (...) {
+    return BL_ERR_INTERNAL;
   }
-  return group_current_device(g);
 }
 
 bl_status bl_group_forward(bl_group* g, void* stream) {
-  bl_status st = bl_group_quant(g, stream);
-  if (st != BL_OK) return st;
-  return bl_group_matmul(g, stream);
+  if (!g) return BL_ERR_INVALID_ARGUMENT;
+  try {
+    return group_run(g, static_cast<hipStream_t>(stream), true);
+  } catch (...) {
+    return BL_ERR_INTERNAL;
+  }
 }
 
 // Forward launches: the quantization launch, then the matmul launches.

@@ -336,6 +336,38 @@ def test_group_matches_separate_calls():
             assert torch.equal(it["y"], ys)
 
 
+def test_group_forward_in_cuda_graph():
+    # The group forward captured into a graph: the fused decode launches fork
+    # onto the group's own streams and join back inside the capture.  Every
+    # replay (eager work and synchronisation between replays) must reproduce
+    # separate forward calls bit for bit.
+    items, singles = [], []
+    specs = [(1, 1024, 2048), (1, 2048, 1024), (1, 3072, 1024), (2, 640, 256), (8, 1024, 96),
+             (20, 1024, 160)]
+    for i, (M, K, N) in enumerate(specs):
+        x, nw, packed, scale = proj_inputs(19, i, 0, M, K, N)
+        it = dict(x=dev(x), norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                  y=torch.full((M, N), float("nan"), device=DEV))
+        items.append(it)
+        singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, N, EPS))
+    with bl.Group(items) as g:
+        kinds = [d["kind"] for d in g.forward_launches()]
+        assert kinds.count("decode_fused") == 4 and "quant" in kinds and "prefill" in kinds
+        g.forward()  # warm-up outside the capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            g.forward()
+        for rep in range(3):
+            for it in items:
+                it["y"].fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for it, ys in zip(items, singles):
+                assert torch.equal(it["y"], ys), f"replay {rep}"
+
+
 # ------------------------------------------ full-size workloads, sampled ---
 
 def _sampled_check(wid, rows_per, group_items, refs):
