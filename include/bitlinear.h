@@ -146,6 +146,9 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
  * into fused and unfused ones, one prefill launch for the rest).  Decode
  * problems that bitlinear_forward would fuse are fused here too: the
  * quantization stage skips them and their matmul launch reads x and norm_w.
+ * Descriptors with the same x (pointer, M, K and eps), such as the q, k and v
+ * of a layer or gate and up, share one pass over x in the quantization launch:
+ * the input is read once, and each gets its own codes from its own norm_w.
  * Results are bit-identical to separate bitlinear_forward calls on the same
  * inputs.
  */
@@ -156,6 +159,8 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
 #define BL_LAUNCH_QUANT 2   /* RMSNorm + int8 quantization of the unfused descriptors */
 #define BL_LAUNCH_DECODE_FUSED 3 /* RMSNorm + quantization + decode product in one
                                     launch (M <= 16 with on-chip staging) */
+#define BL_LAUNCH_QUANT_SHARED 4 /* RMSNorm + int8 quantization of descriptors that
+                                    share their x, one pass over x per set */
 typedef struct bl_desc {
     const float* x;          /* device [M][K] */
     const float* norm_w;     /* device [K] */
@@ -187,7 +192,10 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out);
  * not overlap in time. */
 bl_status bl_group_forward(bl_group* g, void* stream);
 /* Stage 1 only: RMSNorm + int8 quantization of every unfused descriptor's x
- * into the group's workspace (a no-op when every descriptor is fused). */
+ * into the group's workspace (a no-op when every descriptor is fused): one
+ * launch per register-resident chunk count ceil(K/256) class (1, 2, 3, 4, 6,
+ * 8, 12, 16 chunks of 256; 0 = rows longer than 4096) and kind (single
+ * descriptors, then share sets), in increasing chunk count. */
 bl_status bl_group_quant(bl_group* g, void* stream);
 /* Stage 2 only: integer product + epilogue for every descriptor, reading the
  * workspace written by the last bl_group_quant on the same stream (fused
@@ -209,11 +217,10 @@ int32_t bl_group_matmul_launches(const bl_group* g);
 bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kind, int32_t* bucket,
                                       int32_t* count);
 bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream);
-/* The whole forward as individual launches: when any descriptor needs the
- * separate quantization, launch 0 is that (kind BL_LAUNCH_QUANT, bucket 0,
- * count = its problems) and launch i >= 1 is matmul launch i-1; otherwise
- * the forward launches are the matmul launches.  bl_group_forward == every
- * forward launch in order.
+/* The whole forward as individual launches: first the quantization launches
+ * of bl_group_quant (kind BL_LAUNCH_QUANT or BL_LAUNCH_QUANT_SHARED, bucket =
+ * the chunk count, count = descriptors quantized), then the matmul launches.
+ * bl_group_forward == every forward launch in order.
  *   bl_group_forward_launches: number of launches (-1 for a NULL group). */
 int32_t bl_group_forward_launches(const bl_group* g);
 bl_status bl_group_forward_launch_info(const bl_group* g, int32_t i, int32_t* kind,

@@ -33,7 +33,7 @@ BL_ERR_INTERNAL = -7
 _p, _i64, _f32, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32
 
 # BL_LAUNCH_* of include/bitlinear.h
-LAUNCH_KINDS = {0: "decode", 1: "prefill", 2: "quant", 3: "decode_fused"}
+LAUNCH_KINDS = {0: "decode", 1: "prefill", 2: "quant", 3: "decode_fused", 4: "quant_shared"}
 
 
 class BlDesc(ctypes.Structure):

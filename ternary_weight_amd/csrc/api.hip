@@ -171,7 +171,8 @@ bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* 
     p.xq = reinterpret_cast<int8_t*>(ws + l.xq);
     p.factor = reinterpret_cast<float*>(ws + l.factor);
     p.rowsum = reinterpret_cast<int32_t*>(ws + l.rowsum);
-    if ((st = from_hip(launch_quant(single_set(p, quant_units(p.M)), p.K, s))) != BL_OK) return st;
+    if ((st = from_hip(launch_quant(single_set(p, quant_units(p.M)), p.K, false, s))) != BL_OK)
+      return st;
     return from_hip(launch_matmul_single(p, false, false, s));
   } catch (...) {
     return BL_ERR_INTERNAL;
@@ -199,7 +200,7 @@ bl_status bitlinear_quant(const float* x, const float* norm_w, int64_t M, int64_
     p.K = static_cast<int>(K);
     p.N = 1;
     return from_hip(
-        launch_quant(single_set(p, quant_units(p.M)), p.K, static_cast<hipStream_t>(stream)));
+        launch_quant(single_set(p, quant_units(p.M)), p.K, false, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return BL_ERR_INTERNAL;
   }
@@ -268,6 +269,8 @@ struct GroupStage {
   int count = 0;  // problems
   int max_m = 0, max_k = 0;
   bool fused = false;  // decode stages: stage 1 runs inside the launch
+  bool shared = false; // quantization stages: every unit heads a share set
+  int chunks = 0;      // quantization stages: float4 chunks per lane (0: streaming)
 };
 
 // Fused decode launches depend on nothing but the caller's earlier work, so
@@ -279,7 +282,8 @@ constexpr int kAuxStreams = 3;
 
 struct bl_group {
   int device = 0;
-  GroupStage quant, gemm;
+  std::vector<GroupStage> quant;  // quantization launches, per (chunk count, shared)
+  GroupStage gemm;
   std::vector<std::pair<int, GroupStage>> gemv;  // per (superblock bucket, fused)
   void* tables = nullptr;     // device: problem tables and unit tables
   void* workspace = nullptr;  // device: per-problem xq, factor, rowsum
@@ -339,6 +343,54 @@ struct StageHost {
   size_t nunits() const { return fat ? fat_units.size() : units.size(); }
   int nprobs = 0;
 };
+
+// Quantization stages.  Problems whose rows are the same x (pointer, M, K and
+// eps equal) form a share set: they are placed next to each other, the first
+// carrying the set's size, and only it gets work units, so one pass over x
+// quantizes the rows for every problem of the set.  Sets of two or more go
+// to launches of the shared kernel variant, single problems to the plain
+// one, each by the register-resident chunk count of their K.  Sets keep the
+// order of their first problem.
+struct QuantKey {
+  int chunks;
+  bool shared;
+  bool operator<(const QuantKey& o) const {
+    return chunks != o.chunks ? chunks < o.chunks : shared < o.shared;
+  }
+};
+
+std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs) {
+  std::vector<std::vector<int>> sets;
+  for (size_t i = 0; i < probs.size(); ++i) {
+    const Prob& p = probs[i];
+    int found = -1;
+    for (size_t j = 0; j < sets.size() && found < 0; ++j) {
+      const Prob& q = probs[sets[j][0]];
+      if (q.x == p.x && q.M == p.M && q.K == p.K && q.eps == p.eps) found = static_cast<int>(j);
+    }
+    if (found < 0) {
+      found = static_cast<int>(sets.size());
+      sets.emplace_back();
+    }
+    sets[found].push_back(static_cast<int>(i));
+  }
+  std::map<QuantKey, StageHost> out;
+  for (const auto& set : sets) {
+    const Prob& lead = probs[set[0]];
+    StageHost& h = out[QuantKey{quant_chunks(lead.K), set.size() > 1}];
+    const int first = static_cast<int>(h.probs.size());
+    for (size_t k = 0; k < set.size(); ++k) {
+      Prob p = probs[set[k]];
+      p.share = k == 0 ? static_cast<int>(set.size()) : 0;
+      h.probs.push_back(p);
+      ++h.nprobs;
+    }
+    for (int u = 0; u < quant_units(lead.M); ++u) h.units.push_back(int2{first, u});
+    h.max_m = std::max(h.max_m, lead.M);
+    h.max_k = std::max(h.max_k, lead.K);
+  }
+  return out;
+}
 
 // Prefill work order.  Problems are taken in windows of consecutive problems
 // whose packed weights together fit kGemmWindowBytes (a share of one XCD's
@@ -425,7 +477,8 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       return BL_ERR_NOMEM;
     }
 
-    StageHost hq, hm;
+    std::vector<Prob> qprobs;
+    StageHost hm;
     std::map<std::pair<int, bool>, StageHost> hv;  // decode problems by (bucket, fused)
     uint8_t* ws = static_cast<uint8_t*>(g->workspace);
     size_t off = 0;
@@ -451,7 +504,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       p.M = static_cast<int>(d.M);
       p.K = static_cast<int>(d.K);
       p.N = static_cast<int>(d.N);
-      if (!fused) hq.add(p, quant_units(p.M));
+      if (!fused) qprobs.push_back(p);
       if (p.M <= kGemvMaxM) {
         StageHost& sh = hv[{gemv_bucket(p.K), fused}];
         sh.fat = true;
@@ -459,12 +512,22 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       }
       else hm.add(p, gemm_units(p.M, p.N));
     }
+    std::map<QuantKey, StageHost> hqs = build_quant_stages(qprobs);
     interleave_gemm_units(hm);
 
     // One device buffer for every table.
     g->gemv.resize(hv.size());
-    std::vector<StageHost*> hosts{&hq, &hm};
-    std::vector<GroupStage*> stages{&g->quant, &g->gemm};
+    g->quant.resize(hqs.size());
+    std::vector<StageHost*> hosts{&hm};
+    std::vector<GroupStage*> stages{&g->gemm};
+    size_t qi = 0;
+    for (auto& kv : hqs) {
+      g->quant[qi].shared = kv.first.shared;
+      g->quant[qi].chunks = kv.first.chunks;
+      hosts.push_back(&kv.second);
+      stages.push_back(&g->quant[qi]);
+      ++qi;
+    }
     size_t bi = 0;
     for (auto& kv : hv) {
       g->gemv[bi].first = kv.first.first;
@@ -532,12 +595,26 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+bl_status quant_launch(bl_group* g, size_t i, hipStream_t s) {
+  const GroupStage& q = g->quant[i];
+  return from_hip(launch_quant(stage_set(q), q.max_k, q.shared, s));
+}
+
+}  // namespace
+
+extern "C" {
+
 bl_status bl_group_quant(bl_group* g, void* stream) {
   try {
     if (!g) return BL_ERR_INVALID_ARGUMENT;
     bl_status st = group_current_device(g);
-    if (st != BL_OK || g->quant.total == 0) return st;
-    return from_hip(launch_quant(stage_set(g->quant), g->quant.max_k, static_cast<hipStream_t>(stream)));
+    for (size_t i = 0; st == BL_OK && i < g->quant.size(); ++i)
+      st = quant_launch(g, i, static_cast<hipStream_t>(stream));
+    return st;
   } catch (...) {
     return BL_ERR_INTERNAL;
   }
@@ -635,27 +712,33 @@ bl_status bl_group_forward(bl_group* g, void* stream) {
   }
 }
 
-// Forward launches: the quantization launch, then the matmul launches.
+// Forward launches: the quantization launches, then the matmul launches.
 int32_t bl_group_forward_launches(const bl_group* g) {
   if (!g) return -1;
-  return (g->quant.total > 0 ? 1 : 0) + bl_group_matmul_launches(g);
+  return static_cast<int32_t>(g->quant.size()) + bl_group_matmul_launches(g);
 }
 
 bl_status bl_group_forward_launch_info(const bl_group* g, int32_t i, int32_t* kind,
                                        int32_t* bucket, int32_t* count) {
   if (!g || i < 0 || i >= bl_group_forward_launches(g)) return BL_ERR_INVALID_ARGUMENT;
-  const int32_t q = g->quant.total > 0 ? 1 : 0;
+  const int32_t q = static_cast<int32_t>(g->quant.size());
   if (i >= q) return bl_group_matmul_launch_info(g, i - q, kind, bucket, count);
-  if (kind) *kind = BL_LAUNCH_QUANT;
-  if (bucket) *bucket = 0;
-  if (count) *count = g->quant.count;
+  if (kind) *kind = g->quant[i].shared ? BL_LAUNCH_QUANT_SHARED : BL_LAUNCH_QUANT;
+  if (bucket) *bucket = g->quant[i].chunks;
+  if (count) *count = g->quant[i].count;
   return BL_OK;
 }
 
 bl_status bl_group_forward_launch(bl_group* g, int32_t i, void* stream) {
   if (!g || i < 0 || i >= bl_group_forward_launches(g)) return BL_ERR_INVALID_ARGUMENT;
-  const int32_t q = g->quant.total > 0 ? 1 : 0;
-  return i < q ? bl_group_quant(g, stream) : bl_group_matmul_launch(g, i - q, stream);
+  const int32_t q = static_cast<int32_t>(g->quant.size());
+  if (i >= q) return bl_group_matmul_launch(g, i - q, stream);
+  try {
+    const bl_status st = group_current_device(g);
+    return st != BL_OK ? st : quant_launch(g, static_cast<size_t>(i), static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return BL_ERR_INTERNAL;
+  }
 }
 
 bl_status bl_group_destroy(bl_group* g) {

@@ -35,6 +35,10 @@ struct Prob {
   float w_scale;         // tensor-wide I2_S scale (1/mean|W|)
   float eps;
   int M, K, N;
+  // Quantization launches: the number of consecutive records, this one
+  // first, whose rows are the same x (same pointer, M, K and eps); one pass
+  // over x serves them all.  0 or 1: this record alone.
+  int share;
 };
 
 // A launch covers either one problem passed by value (units == nullptr:

@@ -30,8 +30,12 @@ int gemv_bucket(int K);
 int gemm_units(int M, int N);
 
 // Stage 1: fused RMSNorm + absmax int8 quantization of every row in the set.
-// max_k: the largest K in the set.
-hipError_t launch_quant(const ProbSet& set, int max_k, hipStream_t stream);
+// max_k: the largest K in the set (it selects the register-resident variant:
+// quant_chunks(max_k) float4 chunks per lane, 0 = the streaming variant).
+// shared: every unit's record heads a share set (Prob::share problems read
+// its x).
+int quant_chunks(int max_k);
+hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, hipStream_t stream);
 // Row sums of caller-supplied int8 activations (for the raw-integer hook).
 hipError_t launch_rowsum(const Prob& p, hipStream_t stream);
 // Stage 2, M <= kGemvMaxM: weight-streaming MFMA decode kernel for one

@@ -14,6 +14,12 @@
 // absmax(xhat)/127 = r*max|u|/127, computed in double from the fp32 partial
 // sums.  Bound: HBM, 4K bytes read + K bytes written per row (plus the norm
 // weight, an L2 hit).
+//
+// Projections that read the same input (q, k and v of a layer, or gate and
+// up: each normalises the shared x with its own weight, "BitNet Embeddings
+// GGUF Conversion Implementation" s4.5) form a share set in a grouped launch:
+// one pass reads the row and its Sum(x^2) once and emits every projection's
+// codes, so the input is read once instead of once per projection.
 #include "kernels.hpp"
 
 namespace bl {
@@ -34,7 +40,8 @@ template <int NC>
 __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
   const int lane = threadIdx.x & (kWave - 1);
   int local;
-  const Prob P = prob_at(set, find_prob(set, blockIdx.x, &local));
+  const int pi = find_prob(set, blockIdx.x, &local);
+  const Prob P = prob_at(set, pi);
   const int nch = P.K >> 2;
   const int m_begin = local * kQuantRows + wave_id() * kQuantRowsPerWave;
   const BL_GLOBAL f4* wr = gptr<f4>(P.norm_w);
@@ -42,30 +49,99 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
     const int m = m_begin + r;
     if (m >= P.M) break;
     const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m) * P.K);
-    f4 u[NC];
-    float ss = 0.f, amax = 0.f;
+    {
+      f4 u[NC];
+      float ss = 0.f, amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + kWave * i;
+        u[i] = f4{0.f, 0.f, 0.f, 0.f};
+        if (c < nch) {
+          const f4 xv = xr[c];
+          ss += sq4(xv);
+          u[i] = xv * wr[c];
+          amax = fmaxf(amax, absmax4(u[i]));
+        }
+      }
+      const double ssd = wave_sum(static_cast<double>(ss));
+      amax = wave_max(amax);
+      BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
+      int rs = 0;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + kWave * i;
+        if (c < nch) qrow[c] = codes4(u[i], amax, &rs);
+      }
+      finish_row(P, m, ssd, amax, rs, lane);
+    }
+  }
+}
+
+// Share sets: the workgroup's kQuantRows rows are quantized for every problem
+// of the set, wave w taking problems w, w+4, ...: it keeps that problem's
+// norm weight in registers and has R rows of x in flight at once.  The
+// waves of a workgroup read the same rows at the same time, so x comes from
+// HBM once and from L2 for the siblings; each wave's Sum(x^2) has the order
+// of the plain variant, hence the same factor.
+template <int NC>
+__global__ __launch_bounds__(256) void quant_shared_kernel(ProbSet set) {
+  constexpr int R = NC >= 16 ? 1 : (16 / NC >= kQuantRows ? kQuantRows : 16 / NC);
+  const int lane = threadIdx.x & (kWave - 1);
+  int local;
+  const int pi = find_prob(set, blockIdx.x, &local);
+  const Prob P = prob_at(set, pi);
+  const int nch = P.K >> 2;
+  const int share = P.share > 1 ? P.share : 1;
+  const int m0 = local * kQuantRows;
+  for (int p = wave_id(); p < share; p += 4) {
+    const Prob Q = p == 0 ? P : prob_at(set, pi + p);
+    const BL_GLOBAL f4* wr = gptr<f4>(Q.norm_w);
+    f4 w[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = lane + kWave * i;
-      u[i] = f4{0.f, 0.f, 0.f, 0.f};
-      if (c < nch) {
-        const f4 xv = xr[c];
-        ss += sq4(xv);
-        u[i] = xv * wr[c];
-        amax = fmaxf(amax, absmax4(u[i]));
+      w[i] = c < nch ? wr[c] : f4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int r0 = 0; r0 < kQuantRows; r0 += R) {
+      f4 xv[R][NC];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int m = m0 + r0 + r;
+        const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m < P.M ? m : 0) * P.K);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int c = lane + kWave * i;
+          xv[r][i] = (m < P.M && c < nch) ? xr[c] : f4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int m = m0 + r0 + r;
+        if (m >= P.M) break;
+        float ss = 0.f, amax = 0.f;
+        f4 u[NC];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int c = lane + kWave * i;
+          u[i] = f4{0.f, 0.f, 0.f, 0.f};
+          if (c < nch) {
+            ss += sq4(xv[r][i]);
+            u[i] = xv[r][i] * w[i];
+            amax = fmaxf(amax, absmax4(u[i]));
+          }
+        }
+        const double ssd = wave_sum(static_cast<double>(ss));
+        amax = wave_max(amax);
+        BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(Q.xq + static_cast<int64_t>(m) * Q.K);
+        int rs = 0;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int c = lane + kWave * i;
+          if (c < nch) qrow[c] = codes4(u[i], amax, &rs);
+        }
+        finish_row(Q, m, ssd, amax, rs, lane);
       }
     }
-    const double ssd = wave_sum(static_cast<double>(ss));
-    amax = wave_max(amax);
-
-    BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
-    int rs = 0;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = lane + kWave * i;
-      if (c < nch) qrow[c] = codes4(u[i], amax, &rs);
-    }
-    finish_row(P, m, ssd, amax, rs, lane);
   }
 }
 
@@ -74,12 +150,15 @@ __device__ void quant_stream_row(const Prob& P, int m, int lane);
 __global__ __launch_bounds__(256) void quant_stream_kernel(ProbSet set) {
   const int lane = threadIdx.x & (kWave - 1);
   int local;
-  const Prob P = prob_at(set, find_prob(set, blockIdx.x, &local));
+  const int pi = find_prob(set, blockIdx.x, &local);
+  const Prob P = prob_at(set, pi);
+  const int share = P.share > 1 ? P.share : 1;
   const int m_begin = local * kQuantRows + wave_id() * kQuantRowsPerWave;
   for (int r = 0; r < kQuantRowsPerWave; ++r) {
     const int m = m_begin + r;
     if (m >= P.M) break;
-    quant_stream_row(P, m, lane);
+    // Rows this long are re-read per problem of the share set (same result).
+    for (int p = 0; p < share; ++p) quant_stream_row(p == 0 ? P : prob_at(set, pi + p), m, lane);
   }
 }
 
@@ -122,28 +201,38 @@ __global__ __launch_bounds__(256) void rowsum_kernel(Prob P) {
   if (lane == 0) gptr_out<int32_t>(P.rowsum)[m] = rs;
 }
 
-hipError_t launch_quant(const ProbSet& set, int max_k, hipStream_t stream) {
-  if (set.total <= 0) return hipSuccess;
-  const dim3 grid(set.total), block(256);
+int quant_chunks(int max_k) {
+  if (max_k > kQuantRegK) return 0;
   const int nc = (max_k + 255) / 256;
-  if (max_k > kQuantRegK)
-    hipLaunchKernelGGL(quant_stream_kernel, grid, block, 0, stream, set);
-  else if (nc <= 1)
-    hipLaunchKernelGGL(quant_reg_kernel<1>, grid, block, 0, stream, set);
-  else if (nc <= 2)
-    hipLaunchKernelGGL(quant_reg_kernel<2>, grid, block, 0, stream, set);
-  else if (nc <= 3)
-    hipLaunchKernelGGL(quant_reg_kernel<3>, grid, block, 0, stream, set);
-  else if (nc <= 4)
-    hipLaunchKernelGGL(quant_reg_kernel<4>, grid, block, 0, stream, set);
-  else if (nc <= 6)
-    hipLaunchKernelGGL(quant_reg_kernel<6>, grid, block, 0, stream, set);
-  else if (nc <= 8)
-    hipLaunchKernelGGL(quant_reg_kernel<8>, grid, block, 0, stream, set);
-  else if (nc <= 12)
-    hipLaunchKernelGGL(quant_reg_kernel<12>, grid, block, 0, stream, set);
-  else
-    hipLaunchKernelGGL(quant_reg_kernel<16>, grid, block, 0, stream, set);
+  static const int kNc[] = {1, 2, 3, 4, 6, 8, 12, 16};
+  for (int c : kNc)
+    if (nc <= c) return c;
+  return 0;
+}
+
+#define BL_QUANT_SWITCH(KERNEL)                                                                \
+  switch (nc) {                                                                              \
+    case 1: hipLaunchKernelGGL((KERNEL<1>), grid, block, 0, stream, set); break;             \
+    case 2: hipLaunchKernelGGL((KERNEL<2>), grid, block, 0, stream, set); break;             \
+    case 3: hipLaunchKernelGGL((KERNEL<3>), grid, block, 0, stream, set); break;             \
+    case 4: hipLaunchKernelGGL((KERNEL<4>), grid, block, 0, stream, set); break;             \
+    case 6: hipLaunchKernelGGL((KERNEL<6>), grid, block, 0, stream, set); break;             \
+    case 8: hipLaunchKernelGGL((KERNEL<8>), grid, block, 0, stream, set); break;             \
+    case 12: hipLaunchKernelGGL((KERNEL<12>), grid, block, 0, stream, set); break;           \
+    case 16: hipLaunchKernelGGL((KERNEL<16>), grid, block, 0, stream, set); break;           \
+    default: hipLaunchKernelGGL(quant_stream_kernel, grid, block, 0, stream, set);           \
+  }
+
+hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, hipStream_t stream) {
+  if (set.total <= 0) return hipSuccess;
+  const int nc = quant_chunks(max_k);
+  const dim3 grid(set.total), block(256);
+  if (shared) {
+    BL_QUANT_SWITCH(quant_shared_kernel)
+  } else {
+    BL_QUANT_SWITCH(quant_reg_kernel)
+  }
+#undef BL_QUANT_SWITCH
   return hipGetLastError();
 }
 

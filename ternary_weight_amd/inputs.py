@@ -95,6 +95,26 @@ def activations(workload: int, layer: int, proj: int, M: int, K: int,
     return x
 
 
+# Which projections of a layer read the same input: q, k and v normalise the
+# attention input, gate and up the FFN input (each with its own norm weight);
+# o and down have inputs of their own.  Value: the projection index whose
+# seed stands for the shared input.
+SHARED_INPUT = {"q": 0, "k": 0, "v": 0, "o": 3, "gate": 4, "up": 4, "down": 6}
+
+
+def activations_device(torch, workload: int, layer: int, proj: int, M: int, K: int, device):
+    """Activations [M, K] ~ N(0, 1), float32, drawn on `device` by torch's
+    generator seeded from SeedSequence([workload, layer, proj, ROLE_X]).
+
+    For inputs too large to draw on the host in reasonable time (a stream of
+    numbers different from `activations`; nothing compares the two).
+    """
+    seed = int(np.random.SeedSequence([workload, layer, proj, ROLE_X]).generate_state(1, np.uint64)[0] >> 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn((M, K), generator=g, device=device, dtype=torch.float32)
+
+
 def sample_rows(M: int, count: int, seed: int = 0) -> np.ndarray:
     """Sorted distinct row indices, always including the first and the last."""
     if M <= count:

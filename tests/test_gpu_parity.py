@@ -225,9 +225,10 @@ def test_forward_matches_hooks_bitwise(M, K):
 
 
 def test_group_forward_launch_kinds_and_order():
-    # The forward as launches: quantization (the problems not fused), decode
-    # launches by increasing superblock count (3 and 4 fused: their fp32 rows
-    # fit the on-chip staging; 16 not), then the prefill launch.
+    # The forward as launches: quantization of the problems not fused (by
+    # chunk count: K 1024 -> 4, 4096 -> 16), decode launches by increasing
+    # superblock count (3 and 4 fused: their fp32 rows fit the on-chip
+    # staging; 16 not), then the prefill launch.
     specs = [(1, 1024, 64), (8, 640, 40), (16, 4096, 32), (3, 1024, 48), (40, 1024, 72),
              (2, 4096, 24)]
     items, singles = [], []
@@ -239,9 +240,10 @@ def test_group_forward_launch_kinds_and_order():
         singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, N, EPS))
     with bl.Group(items) as g:
         info = g.forward_launches()
-        assert [d["kind"] for d in info] == ["quant", "decode_fused", "decode_fused", "decode", "prefill"]
-        assert [d["bucket"] for d in info] == [0, 3, 4, 16, 0]
-        assert [d["count"] for d in info] == [3, 1, 2, 2, 1]
+        assert [d["kind"] for d in info] == ["quant", "quant", "decode_fused", "decode_fused", "decode",
+                                             "prefill"]
+        assert [d["bucket"] for d in info] == [4, 16, 3, 4, 16, 0]
+        assert [d["count"] for d in info] == [1, 2, 1, 2, 2, 1]
         for i in range(len(info)):
             g.forward_launch(i)
         torch.cuda.synchronize()
@@ -334,6 +336,41 @@ def test_group_matches_separate_calls():
         torch.cuda.synchronize()
         for it, ys in zip(items, singles):
             assert torch.equal(it["y"], ys)
+
+
+def test_group_shared_input_quantization():
+    # Projections reading one x (q/k/v-like, gate/up-like) share a pass of
+    # the quantization launch; a projection on the same x with another eps,
+    # or on a prefix view of x with another M, must not join the set.
+    M = 300
+    x = dev(inputs.activations(21, 0, 0, M, 1024))
+    x2 = dev(inputs.activations(21, 0, 1, M, 2048))
+    specs = [(x, 1024, 512, EPS), (x, 1024, 256, EPS), (x2, 2048, 384, EPS), (x, 1024, 128, EPS),
+             (x, 1024, 96, 1e-3), (x[:M - 37], 1024, 64, EPS), (x2, 2048, 200, EPS)]
+    items, singles = [], []
+    for i, (xx, K, N, eps) in enumerate(specs):
+        W = inputs.weight(21, 1, i, N, K)
+        packed, scale = oracle.i2s_pack(W)
+        nw = dev(inputs.norm_weight(21, 1, i, K))
+        it = dict(x=xx, norm_w=nw, packed_w=dev(packed), w_scale=scale, eps=eps, N=N,
+                  y=torch.full((xx.shape[0], N), float("nan"), device=DEV))
+        items.append(it)
+        singles.append(bl.bitlinear_forward(xx, nw, it["packed_w"], scale, N, eps))
+    with bl.Group(items) as g:
+        info = g.forward_launches()
+        assert [(d["kind"], d["bucket"], d["count"]) for d in info[:3]] == [
+            ("quant", 4, 2), ("quant_shared", 4, 3), ("quant_shared", 8, 2)]
+        g.forward()
+        torch.cuda.synchronize()
+        for i, (it, ys) in enumerate(zip(items, singles)):
+            assert torch.equal(it["y"], ys), i
+    # and against the oracle for one member of each set
+    for i in (0, 2, 3, 6):
+        xx, K, N, eps = specs[i]
+        W = inputs.weight(21, 1, i, N, K)
+        packed, _ = oracle.i2s_pack(W)
+        ref = oracle.bitlinear(host(xx), inputs.norm_weight(21, 1, i, K), packed, N, eps)
+        assert rel_l2(host(items[i]["y"]), ref) <= 1e-3
 
 
 def test_group_forward_in_cuda_graph():
