@@ -352,7 +352,7 @@ def cpu_baseline_prefill(pre, seconds: float):
     """The oracle on sampled token rows of the prefill stack (rows are
     independent): one core, then every host core the run may use."""
     import oracle
-    rows = inputs.sample_rows(pre["M"], 2, seed=4)
+    rows = inputs.sample_rows(pre["M"], 8, seed=4)
     xs_host = {key: x[torch_rows(x, rows)].cpu().numpy() for key, x in pre["xs"].items()}
     ops, t_used, n = 0, 0.0, 0
     for p in pre["projs"]:
