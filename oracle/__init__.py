@@ -13,6 +13,9 @@ Pages followed (by title and section):
   * "BitNet Inference Framework", "Quantization and Encoding", "Data Layout",
     "Quantization (W1.58A8)", "Architectural Details".
   * "gguf-gemv", "Requirements".
+  * "BitNet Embeddings GGUF Conversion Implementation", s4.5 FFN per-projection
+    norms (act(gate) * up feeding the down projection) and the s1 model table
+    (SiLU for Qwen3, gelu_pytorch_tanh for Gemma3).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` to values fixed by
 the pages' definitions and by mathematics (hand-worked examples, closed forms,
@@ -36,6 +39,9 @@ REF_ERR_CODE3 = -2
 REF_ERR_OVERFLOW = -3
 REF_ERR_NOMEM = -4
 REF_ERR_NONFINITE = -5
+
+ACT_SILU = 0        # Qwen3
+ACT_GELU_TANH = 1   # Gemma3 (gelu_pytorch_tanh)
 
 
 def build() -> str:
@@ -66,8 +72,13 @@ def _load():
         lib.ref_epilogue.argtypes = [p, p, ctypes.c_float, i64, i64, p]
         lib.ref_epilogue.restype = None
         lib.ref_bitlinear.argtypes = [p, p, p, i64, i64, i64, ctypes.c_float, p]
+        lib.ref_act.argtypes = [ctypes.c_int, ctypes.c_double]
+        lib.ref_act.restype = ctypes.c_double
+        lib.ref_glu.argtypes = [p, p, ctypes.c_int, i64, p]
+        lib.ref_glu_quant.argtypes = [p, p, ctypes.c_int, p, i64, i64, ctypes.c_float, p, p]
+        lib.ref_glu_bitlinear.argtypes = [p, p, ctypes.c_int, p, p, i64, i64, i64, ctypes.c_float, p]
         for name in ("ref_i2s_pack", "ref_i2s_unpack", "ref_quant", "ref_matmul_i32",
-                     "ref_bitlinear"):
+                     "ref_bitlinear", "ref_glu", "ref_glu_quant", "ref_glu_bitlinear"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -153,4 +164,47 @@ def bitlinear(x: np.ndarray, norm_w: np.ndarray, packed: np.ndarray, N: int,
     y = np.zeros((M, N), dtype=np.float32)
     _check(_load().ref_bitlinear(_ptr(x), _ptr(norm_w), _ptr(packed), M, K, N, eps, _ptr(y)),
            "ref_bitlinear")
+    return y
+
+
+def act(kind: int, z: float) -> float:
+    """The FFN activation at one point, in double (ACT_SILU or ACT_GELU_TANH)."""
+    return float(_load().ref_act(kind, z))
+
+
+def glu(gate: np.ndarray, up: np.ndarray, kind: int) -> np.ndarray:
+    """act(gate) * up elementwise, float64 (same shape as gate)."""
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    up = np.ascontiguousarray(up, dtype=np.float32)
+    assert gate.shape == up.shape
+    h = np.zeros(gate.shape, dtype=np.float64)
+    _check(_load().ref_glu(_ptr(gate), _ptr(up), kind, gate.size, _ptr(h)), "ref_glu")
+    return h
+
+
+def glu_quant(gate: np.ndarray, up: np.ndarray, kind: int, norm_w: np.ndarray,
+              eps: float) -> tuple[np.ndarray, np.ndarray]:
+    """Down-projection input steps on act(gate) * up: (int8 codes [M, K], float64 factor [M])."""
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    up = np.ascontiguousarray(up, dtype=np.float32)
+    norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
+    M, K = gate.shape
+    q = np.zeros((M, K), dtype=np.int8)
+    factor = np.zeros(M, dtype=np.float64)
+    _check(_load().ref_glu_quant(_ptr(gate), _ptr(up), kind, _ptr(norm_w), M, K, eps, _ptr(q),
+                                 _ptr(factor)), "ref_glu_quant")
+    return q, factor
+
+
+def glu_bitlinear(gate: np.ndarray, up: np.ndarray, kind: int, norm_w: np.ndarray,
+                  packed: np.ndarray, N: int, eps: float) -> np.ndarray:
+    """The down projection fed by act(gate) * up: float32 [M, K] pair -> float32 [M, N]."""
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    up = np.ascontiguousarray(up, dtype=np.float32)
+    norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    M, K = gate.shape
+    y = np.zeros((M, N), dtype=np.float32)
+    _check(_load().ref_glu_bitlinear(_ptr(gate), _ptr(up), kind, _ptr(norm_w), _ptr(packed), M, K,
+                                     N, eps, _ptr(y)), "ref_glu_bitlinear")
     return y

@@ -18,6 +18,10 @@
  *   [GEMV] "gguf-gemv", sections on supported block types and "Requirements"
  *          (128-element I2_S blocks, one f32 tensor-wide scale, K a multiple of
  *          128).
+ *   [EMB s4.5 FFN] the FFN per-projection norms: act(gate) * up, then the
+ *          down projection's RMSNorm and norm weight, then down; the
+ *          activation per model from the [EMB s1] table (SiLU for Qwen3,
+ *          gelu_pytorch_tanh for Gemma3).
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository):
@@ -36,6 +40,10 @@
  *       all-zero row gives zero codes and factor 0.
  *   R6  RMSNorm: x / sqrt(mean(x^2) + eps) * norm_w, norm_w used as given.
  *   R7  Epilogue: y = acc * (absmax/127) / scale, no bias.
+ *   R8  SiLU(z) = z / (1 + exp(-z)); gelu_pytorch_tanh is the tanh
+ *       approximation of GELU, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
+ *       (Hendrycks and Gimpel's published form); the glue product and the
+ *       down projection's input steps run in double.
  */
 #include <math.h>
 #include <stdint.h>
@@ -126,36 +134,80 @@ int ref_i2s_unpack(const uint8_t* packed, int64_t K, int64_t N, int8_t* q_out, f
  *   q     = clamp(round(xhat * 127 / a), -127, 127)
  *   factor= a / 127       (the activation dequantization factor)
  * All arithmetic in double. */
+/* One row of the steps above, on a row given in double. */
+static void quant_row(const double* row, const float* norm_w, int64_t K, float eps, int8_t* q,
+                      double* factor) {
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; ++k) ss += row[k] * row[k];
+    double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+
+    double a = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double xhat = row[k] * r * (double)norm_w[k];
+        if (fabs(xhat) > a) a = fabs(xhat);
+    }
+    if (a == 0.0) {
+        for (int64_t k = 0; k < K; ++k) q[k] = 0;
+        *factor = 0.0;
+        return;
+    }
+    double s = 127.0 / a;
+    for (int64_t k = 0; k < K; ++k) {
+        double xhat = row[k] * r * (double)norm_w[k];
+        double v = nearbyint(xhat * s);
+        if (v > 127.0) v = 127.0;
+        if (v < -127.0) v = -127.0;
+        q[k] = (int8_t)v;
+    }
+    *factor = a / 127.0;
+}
+
 int ref_quant(const float* x, const float* norm_w, int64_t M, int64_t K, float eps,
               int8_t* q_out, double* factor_out) {
     if ((M > 0 && (!x || !q_out || !factor_out)) || !norm_w || M < 0 || K <= 0) return REF_ERR_ARG;
+    double* row = (double*)malloc((size_t)K * sizeof(double));
+    if (!row) return REF_ERR_NOMEM;
     for (int64_t m = 0; m < M; ++m) {
-        const float* row = x + m * K;
-        double ss = 0.0;
-        for (int64_t k = 0; k < K; ++k) ss += (double)row[k] * (double)row[k];
-        double r = 1.0 / sqrt(ss / (double)K + (double)eps);
-
-        double a = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            double xhat = (double)row[k] * r * (double)norm_w[k];
-            if (fabs(xhat) > a) a = fabs(xhat);
-        }
-        if (a == 0.0) {
-            for (int64_t k = 0; k < K; ++k) q_out[m * K + k] = 0;
-            factor_out[m] = 0.0;
-            continue;
-        }
-        double s = 127.0 / a;
-        for (int64_t k = 0; k < K; ++k) {
-            double xhat = (double)row[k] * r * (double)norm_w[k];
-            double v = nearbyint(xhat * s);
-            if (v > 127.0) v = 127.0;
-            if (v < -127.0) v = -127.0;
-            q_out[m * K + k] = (int8_t)v;
-        }
-        factor_out[m] = a / 127.0;
+        for (int64_t k = 0; k < K; ++k) row[k] = (double)x[m * K + k];  /* exact */
+        quant_row(row, norm_w, K, eps, q_out + m * K, factor_out + m);
     }
+    free(row);
     return REF_OK;
+}
+
+/* FFN glue [EMB s4.5 FFN]: the activation of the gate projection's output. */
+#define REF_ACT_SILU 0
+#define REF_ACT_GELU_TANH 1
+double ref_act(int act, double z) {
+    if (act == REF_ACT_SILU) return z / (1.0 + exp(-z));
+    const double c = sqrt(2.0 / acos(-1.0));
+    return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
+}
+
+/* h = act(gate) * up, elementwise, in double. */
+int ref_glu(const float* gate, const float* up, int act, int64_t n, double* h_out) {
+    if (n < 0 || (n > 0 && (!gate || !up || !h_out))) return REF_ERR_ARG;
+    if (act != REF_ACT_SILU && act != REF_ACT_GELU_TANH) return REF_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) h_out[i] = ref_act(act, (double)gate[i]) * (double)up[i];
+    return REF_OK;
+}
+
+/* The down projection's input steps on the glue product: per row,
+ * h = act(gate) * up, then RMSNorm with the down norm weight and the
+ * absmax int8 quantization above, all in double. */
+int ref_glu_quant(const float* gate, const float* up, int act, const float* norm_w, int64_t M,
+                  int64_t K, float eps, int8_t* q_out, double* factor_out) {
+    if ((M > 0 && (!gate || !up || !q_out || !factor_out)) || !norm_w || M < 0 || K <= 0)
+        return REF_ERR_ARG;
+    double* row = (double*)malloc((size_t)K * sizeof(double));
+    if (!row) return REF_ERR_NOMEM;
+    int rc = REF_OK;
+    for (int64_t m = 0; m < M && rc == REF_OK; ++m) {
+        rc = ref_glu(gate + m * K, up + m * K, act, K, row);
+        if (rc == REF_OK) quant_row(row, norm_w, K, eps, q_out + m * K, factor_out + m);
+    }
+    free(row);
+    return rc;
 }
 
 /* Integer product of the int8 activations with the ternary weights decoded
@@ -204,6 +256,31 @@ int ref_bitlinear(const float* x, const float* norm_w, const uint8_t* packed, in
     int rc = REF_ERR_NOMEM;
     if (q && factor && acc) {
         rc = ref_quant(x, norm_w, M, K, eps, q, factor);
+        if (rc == REF_OK) rc = ref_matmul_i32(q, packed, M, K, N, acc);
+        if (rc == REF_OK) {
+            float scale;
+            memcpy(&scale, packed + N * K / 4, 4);
+            ref_epilogue(acc, factor, scale, M, N, y);
+        }
+    }
+    free(q);
+    free(factor);
+    free(acc);
+    return rc;
+}
+
+/* The down projection fed by the glue: glue + quantization, integer
+ * product, epilogue. */
+int ref_glu_bitlinear(const float* gate, const float* up, int act, const float* norm_w,
+                      const uint8_t* packed, int64_t M, int64_t K, int64_t N, float eps, float* y) {
+    if (M < 0 || K <= 0 || N <= 0 || K % BLOCK != 0) return REF_ERR_ARG;
+    if (M == 0) return REF_OK;
+    int8_t* q = (int8_t*)malloc((size_t)(M * K));
+    double* factor = (double*)malloc((size_t)M * sizeof(double));
+    int32_t* acc = (int32_t*)malloc((size_t)(M * N) * sizeof(int32_t));
+    int rc = REF_ERR_NOMEM;
+    if (q && factor && acc) {
+        rc = ref_glu_quant(gate, up, act, norm_w, M, K, eps, q, factor);
         if (rc == REF_OK) rc = ref_matmul_i32(q, packed, M, K, N, acc);
         if (rc == REF_OK) {
             float scale;

@@ -320,3 +320,105 @@ def test_row_separability_and_weight_symmetries():
 def test_path_rejects_ragged_k():
     assert oracle.packed_bytes(100, 4) == 0
     assert oracle.packed_bytes(128, 4) == 4 * 32 + 4
+
+
+# ---------------------------------------------------------------- FFN glue ---
+# "BitNet Embeddings GGUF Conversion Implementation", s4.5 FFN per-projection
+# norms: act(gate) * up feeds the down projection's RMSNorm; the activation
+# per model comes from the s1 table (SiLU for Qwen3, gelu_pytorch_tanh for
+# Gemma3).  The pins below come from the functions' mathematics, not from
+# retyping them.
+
+ACTS = [oracle.ACT_SILU, oracle.ACT_GELU_TANH]
+
+
+@pytest.mark.parametrize("kind", ACTS)
+def test_activation_odd_identity_and_origin(kind):
+    # Both are z * w(z) with w(z) + w(-z) = 1 (sigmoid, resp. (1 + tanh)/2 of
+    # an odd argument), so act(z) - act(-z) = z exactly in real arithmetic.
+    for z in np.linspace(-9.0, 9.0, 181):
+        assert abs(oracle.act(kind, z) - oracle.act(kind, -z) - z) <= 4e-16 * max(1.0, abs(z))
+    assert oracle.act(kind, 0.0) == 0.0
+    # Slope 1/2 at the origin; curvature: SiLU'' (0) = 2 sigma'(0) = 1/2,
+    # GELU'' (0) = 2 phi(0) = sqrt(2/pi) (the tanh form keeps it exactly).
+    h = 1e-4
+    slope = (oracle.act(kind, h) - oracle.act(kind, -h)) / (2 * h)
+    assert abs(slope - 0.5) < 1e-8
+    h = 1e-3
+    curv = (oracle.act(kind, h) - 2 * oracle.act(kind, 0.0) + oracle.act(kind, -h)) / (h * h)
+    want = 0.5 if kind == oracle.ACT_SILU else math.sqrt(2.0 / math.pi)
+    assert abs(curv - want) < 1e-5
+
+
+def test_silu_closed_form_and_limits():
+    # sigma(ln 3) = 3/4.
+    assert abs(oracle.act(oracle.ACT_SILU, math.log(3.0)) - 0.75 * math.log(3.0)) < 1e-15
+    assert abs(oracle.act(oracle.ACT_SILU, -math.log(3.0)) + 0.25 * math.log(3.0)) < 1e-15
+    # exp(-40) ~ 4e-18 is below half an ulp of 1: exactly 40 in double.
+    assert oracle.act(oracle.ACT_SILU, 40.0) == 40.0
+    assert 0.0 > oracle.act(oracle.ACT_SILU, -40.0) > -1e-15
+
+
+def test_gelu_tanh_is_the_tanh_approximation_of_gelu():
+    # Within 5e-4 of the exact GELU z*Phi(z) everywhere, yet not equal to it
+    # (so neither the exact form nor a different approximation slips in).
+    def gelu_exact(z):
+        return 0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0)))
+    worst = max(abs(oracle.act(oracle.ACT_GELU_TANH, z) - gelu_exact(z))
+                for z in np.linspace(-6.0, 6.0, 1201))
+    assert 1e-4 < worst < 5e-4
+    assert abs(oracle.act(oracle.ACT_GELU_TANH, 1.0) - gelu_exact(1.0)) > 1e-4
+    # tanh saturates to exactly 1 in double at these arguments.
+    assert oracle.act(oracle.ACT_GELU_TANH, 10.0) == 10.0
+    assert oracle.act(oracle.ACT_GELU_TANH, -10.0) == 0.0
+
+
+@pytest.mark.parametrize("kind", ACTS)
+def test_glu_elementwise_product(kind):
+    g = inputs.activations(12, 0, kind, 3, 256)
+    u = inputs.activations(12, 1, kind, 3, 256)
+    h = oracle.glu(g, u, kind)
+    # up enters linearly (exact for a power-of-two factor), a zero gate or a
+    # zero up gives zero, and each element is the activation at that gate.
+    assert np.array_equal(oracle.glu(g, u * np.float32(4.0), kind), 4.0 * h)
+    assert not np.any(oracle.glu(np.zeros_like(g), u, kind))
+    assert not np.any(oracle.glu(g, np.zeros_like(u), kind))
+    for m, k in [(0, 0), (1, 17), (2, 255)]:
+        assert h[m, k] == oracle.act(kind, float(g[m, k])) * float(u[m, k])
+
+
+@pytest.mark.parametrize("kind,gate_value", [(oracle.ACT_SILU, 40.0), (oracle.ACT_GELU_TANH, 10.0)])
+def test_glu_quant_reduces_to_quant(kind, gate_value):
+    # Where the activation is exactly the identity (the limits above) the glue
+    # product is gate * up, exactly, and the down projection's input steps
+    # must be the plain quantization of that product, bit for bit.
+    M, K = 4, 384
+    up = (inputs.rng(12, 2, kind, 2).integers(-64, 65, size=(M, K)) / 8.0).astype(np.float32)
+    gate = np.full((M, K), gate_value, np.float32)
+    nw = inputs.norm_weight(12, 2, kind, K)
+    q, f = oracle.glu_quant(gate, up, kind, nw, 1e-6)
+    x = (up.astype(np.float64) * gate_value).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), up.astype(np.float64) * gate_value)
+    q2, f2 = oracle.quant(x, nw, 1e-6)
+    assert np.array_equal(q, q2)
+    assert np.array_equal(f, f2)
+
+
+@pytest.mark.parametrize("kind", ACTS)
+def test_glu_path_equals_float64_dequantized_product(kind):
+    M, K, N = 3, 256, 7
+    gate = inputs.activations(12, 3, kind, M, K)
+    up = inputs.activations(12, 4, kind, M, K)
+    nw = inputs.norm_weight(12, 3, kind, K)
+    W = inputs.weight(12, 3, kind, N, K)
+    packed, scale = oracle.i2s_pack(W)
+    y = oracle.glu_bitlinear(gate, up, kind, nw, packed, N, 1e-6)
+    q, f = oracle.glu_quant(gate, up, kind, nw, 1e-6)
+    qw, _ = oracle.i2s_unpack(packed, K, N)
+    ref = (q.astype(np.float64) * f[:, None]) @ (qw.astype(np.float64) / scale).T
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 1e-7
+    # and the codes are the rounded RMSNorm of the glue product
+    h = oracle.glu(gate, up, kind)
+    r = 1.0 / np.sqrt((h * h).mean(axis=1) + 1e-6)
+    xhat = h * r[:, None] * nw.astype(np.float64)
+    assert np.all(np.abs(xhat - q * f[:, None]) <= 0.5 * f[:, None] * (1 + 1e-12))
