@@ -262,6 +262,51 @@ def bench_prefill(torch, bl, args):
                 tops=ops / (ms * 1e-3) / 1e12, mm_tops=ops / (mm_ms * 1e-3) / 1e12)
 
 
+def bench_ffn_glue(torch, bl, args):
+    """The Qwen3 FFN down projection fed by the glue act(gate) * up at the
+    prefill size (M = 16384, K = 3072 -> N = 1024, SiLU): the fused glue +
+    quantization kernel (act(gate) * up formed in registers, never stored)
+    against its HBM roofline, and the whole glue-fed forward."""
+    M, K, N = 16384, 3072, 1024
+    dev = torch.device("cuda")
+    gate = inputs.activations_device(torch, 4, 0, 100, M, K, dev)
+    up = inputs.activations_device(torch, 4, 0, 101, M, K, dev)
+    nw = torch.from_numpy(inputs.norm_weight(4, 0, 6, K)).to(dev)
+    packed, scale = bl.i2s_pack(inputs.weight(4, 0, 6, N, K))
+    pw = torch.from_numpy(packed).to(dev)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    f = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    def timed(fn, reps):
+        for _ in range(max(1, args.warmup // 2)):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+    reps = max(3, args.steps // 2)
+    q_ms = timed(lambda: bl.bitlinear_glu_quant(gate, up, bl.ACT_SILU, nw, inputs.EPS, xq=xq, x_factor=f), reps)
+    fwd_ms = timed(lambda: bl.bitlinear_glu_forward(gate, up, bl.ACT_SILU, nw, pw, scale, N, inputs.EPS, y=y), reps)
+    q_bytes = 8 * M * K + M * K + 8 * M + 4 * K     # gate + up in, codes + factor + row sum out
+    unfused = q_bytes + 8 * M * K                     # the product written and read back in fp32
+    return {
+        "workload": f"Qwen3 FFN down projection fed by SiLU(gate)*up, M={M}, K={K} -> N={N}",
+        "glue_quant_us": round(q_ms * 1e3, 1),
+        "roofline": {"bound": "hbm", "kernel": "quant_reg_kernel<12, SiLU> (glue + RMSNorm + int8)",
+                     "achieved": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": q_bytes},
+        "bytes_saved_vs_storing_the_product": round(1 - q_bytes / unfused, 3),
+        "forward_ms": round(fwd_ms, 4),
+        "forward_TOPS": round(2 * M * N * K / (fwd_ms * 1e-3) / 1e12, 1),
+    }
+
+
 def measure_peaks(torch, bl):
     """Sustained HBM read / copy bandwidth and int8 MFMA rate of this GPU (probes)."""
     dev = torch.device("cuda")
@@ -466,6 +511,11 @@ def main():
         if not args.skip_cpu:
             pf["cpu_baseline"] = cpu_baseline_prefill(pre, args.cpu_seconds / 2)
         out["prefill"] = pf
+        del pre
+        glue = bench_ffn_glue(torch, bl, args)
+        log(f"ffn glue: glue+quant {glue['glue_quant_us']:.1f} us ({glue['roofline']['achieved']:.0f} GB/s), "
+            f"glue-fed down forward {glue['forward_ms']:.3f} ms ({glue['forward_TOPS']:.0f} TOPS)")
+        out["ffn_glue"] = glue
     print(json.dumps(out), flush=True)
 
 

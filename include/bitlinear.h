@@ -139,6 +139,32 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
                                int64_t N, int32_t* acc, void* stream);
 
 /*
+ * FFN glue ("BitNet Embeddings GGUF Conversion Implementation", s4.5 FFN
+ * per-projection norms; activation per the s1 model table): the down
+ * projection's input is h = act(gate) * up, elementwise, where gate and up are
+ * the outputs of the gate and up projections.  These calls form h row by row
+ * in registers while quantizing it (fp32), so h is never written to memory.
+ *   act  BL_ACT_SILU (Qwen3): z / (1 + exp(-z));
+ *        BL_ACT_GELU_TANH (Gemma3, gelu_pytorch_tanh):
+ *        0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+ *   gate, up  device [M][K] float32 each, 16-byte aligned.
+ * Everything else as in bitlinear_quant and bitlinear_forward (K is the down
+ * projection's input width, the FFN size; norm_w its norm weight); an
+ * unknown act is BL_ERR_INVALID_ARGUMENT.  bitlinear_glu_forward uses the
+ * library workspace (always the two-stage path) and returns
+ * y = BitLinear_down(act(gate) * up).
+ */
+#define BL_ACT_SILU 0
+#define BL_ACT_GELU_TANH 1
+bl_status bitlinear_glu_quant(const float* gate, const float* up, int32_t act, const float* norm_w,
+                              int64_t M, int64_t K, float eps, int8_t* xq, float* x_factor,
+                              void* stream);
+bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
+                                const float* norm_w, const uint8_t* packed_w, float w_scale,
+                                int64_t M, int64_t K, int64_t N, float eps, float* y,
+                                void* stream);
+
+/*
  * Grouped execution: many independent projections (for example the seven of
  * a layer, or of many layers) run with few launches: one quantization launch
  * for all of them that need one, then the matmul stage (one decode launch per

@@ -50,6 +50,8 @@ _SIGS = {
     "bitlinear_forward": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
     "bitlinear_quant": ([_p, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
     "bitlinear_matmul_i32": ([_p, _p, _i64, _i64, _i64, _p, _p], _i32),
+    "bitlinear_glu_quant": ([_p, _p, _i32, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
+    "bitlinear_glu_forward": ([_p, _p, _i32, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
     "bl_group_create": ([ctypes.POINTER(BlDesc), _i32, ctypes.POINTER(_p)], _i32),
     "bl_group_forward": ([_p, _p], _i32),
     "bl_group_quant": ([_p, _p], _i32),
@@ -296,3 +298,41 @@ def probe_mfma_i8(iters: int, blocks: int, sink, shape: int = 16, stream=None) -
     torch = _torch()
     _check(_lib.bl_probe_mfma_i8(iters, blocks, shape, _dev(sink, torch.int32, "sink"),
                                  _stream_handle(stream)), "bl_probe_mfma_i8")
+
+
+# ------------------------------------------------------------- FFN glue ---
+
+ACT_SILU = 0        # BL_ACT_SILU: Qwen3
+ACT_GELU_TANH = 1   # BL_ACT_GELU_TANH: Gemma3 (gelu_pytorch_tanh)
+
+
+def bitlinear_glu_quant(gate, up, act: int, norm_w, eps: float, xq=None, x_factor=None, stream=None):
+    """(int8 codes [M, K], float32 factor [M]) of the down projection's input
+    act(gate) * up (formed in registers, never stored)."""
+    torch = _torch()
+    M, K = gate.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=gate.device)
+    if x_factor is None:
+        x_factor = torch.empty((M,), dtype=torch.float32, device=gate.device)
+    _check(_lib.bitlinear_glu_quant(
+        _dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up", (M, K)), act,
+        _dev(norm_w, torch.float32, "norm_w", (K,)), M, K, eps, _dev(xq, torch.int8, "xq", (M, K)),
+        _dev(x_factor, torch.float32, "x_factor", (M,)), _stream_handle(stream)),
+        "bitlinear_glu_quant")
+    return xq, x_factor
+
+
+def bitlinear_glu_forward(gate, up, act: int, norm_w, packed_w, w_scale: float, N: int, eps: float,
+                          y=None, stream=None):
+    """y[M, N] = BitLinear_down(act(gate) * up) on the GPU; returns y."""
+    torch = _torch()
+    M, K = gate.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=gate.device)
+    _check(_lib.bitlinear_glu_forward(
+        _dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up", (M, K)), act,
+        _dev(norm_w, torch.float32, "norm_w", (K,)), _dev(packed_w, torch.uint8, "packed_w"),
+        w_scale, M, K, N, eps, _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)),
+        "bitlinear_glu_forward")
+    return y

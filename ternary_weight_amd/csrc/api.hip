@@ -171,7 +171,8 @@ bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* 
     p.xq = reinterpret_cast<int8_t*>(ws + l.xq);
     p.factor = reinterpret_cast<float*>(ws + l.factor);
     p.rowsum = reinterpret_cast<int32_t*>(ws + l.rowsum);
-    if ((st = from_hip(launch_quant(single_set(p, quant_units(p.M)), p.K, false, s))) != BL_OK)
+    if ((st = from_hip(launch_quant(single_set(p, quant_units(p.M)), p.K, false, kActNone, s))) !=
+        BL_OK)
       return st;
     return from_hip(launch_matmul_single(p, false, false, s));
   } catch (...) {
@@ -200,7 +201,7 @@ bl_status bitlinear_quant(const float* x, const float* norm_w, int64_t M, int64_
     p.K = static_cast<int>(K);
     p.N = 1;
     return from_hip(
-        launch_quant(single_set(p, quant_units(p.M)), p.K, false, static_cast<hipStream_t>(stream)));
+        launch_quant(single_set(p, quant_units(p.M)), p.K, false, kActNone, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return BL_ERR_INTERNAL;
   }
@@ -229,6 +230,79 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
     p.N = static_cast<int>(N);
     if ((st = from_hip(launch_rowsum(p, s))) != BL_OK) return st;
     return from_hip(launch_matmul_single(p, true, false, s));
+  } catch (...) {
+    return BL_ERR_INTERNAL;
+  }
+}
+
+// ---- FFN glue: the down projection fed by act(gate) * up ------------------
+
+bl_status bitlinear_glu_quant(const float* gate, const float* up, int32_t act, const float* norm_w,
+                              int64_t M, int64_t K, float eps, int8_t* xq, float* x_factor,
+                              void* stream) {
+  try {
+    bl_status st = check_shape(M, K, 1);
+    if (st != BL_OK) return st;
+    if ((st = check_eps(eps)) != BL_OK) return st;
+    if (act != BL_ACT_SILU && act != BL_ACT_GELU_TANH) return BL_ERR_INVALID_ARGUMENT;
+    if (!norm_w || (M > 0 && (!gate || !up || !xq || !x_factor))) return BL_ERR_INVALID_ARGUMENT;
+    if (!aligned16(norm_w) ||
+        (M > 0 && (!aligned16(gate) || !aligned16(up) || !aligned16(xq) || !aligned16(x_factor))))
+      return BL_ERR_MISALIGNED;
+    if (M == 0) return BL_OK;
+    Prob p{};
+    p.x = gate;
+    p.up = up;
+    p.act = act == BL_ACT_SILU ? kActSilu : kActGeluTanh;
+    p.norm_w = norm_w;
+    p.xq = xq;
+    p.factor = x_factor;
+    p.rowsum = nullptr;
+    p.eps = eps;
+    p.M = static_cast<int>(M);
+    p.K = static_cast<int>(K);
+    p.N = 1;
+    return from_hip(launch_quant(single_set(p, quant_units(p.M)), p.K, false, p.act,
+                                 static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BL_ERR_INTERNAL;
+  }
+}
+
+bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
+                                const float* norm_w, const uint8_t* packed_w, float w_scale,
+                                int64_t M, int64_t K, int64_t N, float eps, float* y,
+                                void* stream) {
+  try {
+    bl_status st = check_forward(gate, norm_w, packed_w, w_scale, M, K, N, eps, y);
+    if (st != BL_OK) return st;
+    if (act != BL_ACT_SILU && act != BL_ACT_GELU_TANH) return BL_ERR_INVALID_ARGUMENT;
+    if (M > 0 && !up) return BL_ERR_INVALID_ARGUMENT;
+    if (M > 0 && !aligned16(up)) return BL_ERR_MISALIGNED;
+    if (M == 0) return BL_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const WsLayout l = ws_layout(M, K);
+    uint8_t* ws = nullptr;
+    if ((st = acquire_ws(s, l.bytes, &ws)) != BL_OK) return st;
+    Prob p{};
+    p.x = gate;
+    p.up = up;
+    p.act = act == BL_ACT_SILU ? kActSilu : kActGeluTanh;
+    p.norm_w = norm_w;
+    p.w = packed_w;
+    p.xq = reinterpret_cast<int8_t*>(ws + l.xq);
+    p.factor = reinterpret_cast<float*>(ws + l.factor);
+    p.rowsum = reinterpret_cast<int32_t*>(ws + l.rowsum);
+    p.y = y;
+    p.acc = nullptr;
+    p.w_scale = w_scale;
+    p.eps = eps;
+    p.M = static_cast<int>(M);
+    p.K = static_cast<int>(K);
+    p.N = static_cast<int>(N);
+    if ((st = from_hip(launch_quant(single_set(p, quant_units(p.M)), p.K, false, p.act, s))) != BL_OK)
+      return st;
+    return from_hip(launch_matmul_single(p, false, false, s));
   } catch (...) {
     return BL_ERR_INTERNAL;
   }
@@ -601,7 +675,7 @@ namespace {
 
 bl_status quant_launch(bl_group* g, size_t i, hipStream_t s) {
   const GroupStage& q = g->quant[i];
-  return from_hip(launch_quant(stage_set(q), q.max_k, q.shared, s));
+  return from_hip(launch_quant(stage_set(q), q.max_k, q.shared, kActNone, s));
 }
 
 }  // namespace

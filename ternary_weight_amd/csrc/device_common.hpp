@@ -32,6 +32,7 @@ struct Prob {
   int32_t* rowsum;       // [M] sum_k xq (workspace)
   float* y;              // [M][N] f32 output (forward)
   int32_t* acc;          // [M][N] i32 output (raw-integer hook)
+  const float* up;       // FFN glue: [M][K] up-projection output (x is the gate output)
   float w_scale;         // tensor-wide I2_S scale (1/mean|W|)
   float eps;
   int M, K, N;
@@ -39,7 +40,12 @@ struct Prob {
   // first, whose rows are the same x (same pointer, M, K and eps); one pass
   // over x serves them all.  0 or 1: this record alone.
   int share;
+  // FFN glue: the input row is act(x) * up (kActSilu, kActGeluTanh) instead
+  // of x (kActNone).
+  int act;
 };
+
+constexpr int kActNone = 0, kActSilu = 1, kActGeluTanh = 2;
 
 // A launch covers either one problem passed by value (units == nullptr:
 // work unit u is local unit u of that problem) or a table of problems in
@@ -175,6 +181,21 @@ __device__ __forceinline__ uint32_t codes4(const f4& u, float amax, int* sum) {
   *sum += a + b + c + d;
   return pack4(a, b, c, d);
 }
+// FFN glue ("BitNet Embeddings GGUF Conversion Implementation", s4.5 FFN
+// per-projection norms; activation per the s1 model table): the down
+// projection's input is act(gate) * up.  SiLU(z) = z / (1 + e^-z); the tanh
+// form of GELU, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).  fp32.
+template <int ACT>
+__device__ __forceinline__ float act_f32(float z) {
+  if (ACT == kActSilu) return z / (1.0f + expf(-z));
+  return 0.5f * z * (1.0f + tanhf(0.7978845608f * (z + 0.044715f * z * z * z)));
+}
+template <int ACT>
+__device__ __forceinline__ f4 glu4(f4 g, f4 u) {
+  return f4{act_f32<ACT>(g.x) * u.x, act_f32<ACT>(g.y) * u.y, act_f32<ACT>(g.z) * u.z,
+            act_f32<ACT>(g.w) * u.w};
+}
+
 // factor = max|RMSNorm(x) * norm_w| / 127 = r * max|u| / 127 with
 // r = 1/sqrt(mean(x^2) + eps), in double from the row's Sum(x^2).
 __device__ __forceinline__ float quant_factor(double ss, int K, float eps, float amax) {

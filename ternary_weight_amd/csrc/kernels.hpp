@@ -33,9 +33,10 @@ int gemm_units(int M, int N);
 // max_k: the largest K in the set (it selects the register-resident variant:
 // quant_chunks(max_k) float4 chunks per lane, 0 = the streaming variant).
 // shared: every unit's record heads a share set (Prob::share problems read
-// its x).
+// its x).  act: every record's input is act(x) * up (kActSilu, kActGeluTanh;
+// records carry the same value in Prob::act) or x (kActNone); not with shared.
 int quant_chunks(int max_k);
-hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, hipStream_t stream);
+hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hipStream_t stream);
 // Row sums of caller-supplied int8 activations (for the raw-integer hook).
 hipError_t launch_rowsum(const Prob& p, hipStream_t stream);
 // Stage 2, M <= kGemvMaxM: weight-streaming MFMA decode kernel for one

@@ -36,7 +36,8 @@ __device__ __forceinline__ void finish_row(const Prob& P, int m, double ss, floa
 
 // NC: float4 chunks per lane held in registers (K <= 256*NC).  A workgroup
 // owns kQuantRows consecutive rows of one problem, kQuantRowsPerWave per wave.
-template <int NC>
+// ACT: the row is act(x) * up (FFN glue) instead of x.
+template <int NC, int ACT>
 __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
   const int lane = threadIdx.x & (kWave - 1);
   int local;
@@ -49,6 +50,7 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
     const int m = m_begin + r;
     if (m >= P.M) break;
     const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m) * P.K);
+    const BL_GLOBAL f4* ur = gptr<f4>(P.up + static_cast<int64_t>(m) * P.K);
     {
       f4 u[NC];
       float ss = 0.f, amax = 0.f;
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
         const int c = lane + kWave * i;
         u[i] = f4{0.f, 0.f, 0.f, 0.f};
         if (c < nch) {
-          const f4 xv = xr[c];
+          const f4 xv = ACT == kActNone ? f4(xr[c]) : glu4<ACT>(f4(xr[c]), f4(ur[c]));
           ss += sq4(xv);
           u[i] = xv * wr[c];
           amax = fmaxf(amax, absmax4(u[i]));
@@ -162,6 +164,14 @@ __global__ __launch_bounds__(256) void quant_stream_kernel(ProbSet set) {
   }
 }
 
+// Input chunk c of row m: x, or the FFN glue act(x) * up.
+__device__ __forceinline__ f4 stream_in(const Prob& P, const BL_GLOBAL f4* xr, int64_t m, int c) {
+  if (P.act == kActNone) return xr[c];
+  const f4 u = gptr<f4>(P.up + m * P.K)[c];
+  const f4 g = xr[c];
+  return P.act == kActSilu ? glu4<kActSilu>(g, u) : glu4<kActGeluTanh>(g, u);
+}
+
 // One row, two streaming passes (used for K above the register budget).
 __device__ void quant_stream_row(const Prob& P, int m, int lane) {
   const int nch = P.K >> 2;
@@ -171,7 +181,7 @@ __device__ void quant_stream_row(const Prob& P, int m, int lane) {
   double ss = 0.0;
   float amax = 0.f;
   for (int c = lane; c < nch; c += kWave) {
-    const f4 xv = xr[c];
+    const f4 xv = stream_in(P, xr, m, c);
     const f4 wv = wr[c];
     ss += static_cast<double>(sq4(xv));
     amax = fmaxf(amax, absmax4(xv * wv));
@@ -181,7 +191,7 @@ __device__ void quant_stream_row(const Prob& P, int m, int lane) {
 
   BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
   int rs = 0;
-  for (int c = lane; c < nch; c += kWave) qrow[c] = codes4(xr[c] * wr[c], amax, &rs);
+  for (int c = lane; c < nch; c += kWave) qrow[c] = codes4(stream_in(P, xr, m, c) * wr[c], amax, &rs);
   finish_row(P, m, ss, amax, rs, lane);
 }
 
@@ -210,27 +220,32 @@ int quant_chunks(int max_k) {
   return 0;
 }
 
-#define BL_QUANT_SWITCH(KERNEL)                                                                \
-  switch (nc) {                                                                              \
-    case 1: hipLaunchKernelGGL((KERNEL<1>), grid, block, 0, stream, set); break;             \
-    case 2: hipLaunchKernelGGL((KERNEL<2>), grid, block, 0, stream, set); break;             \
-    case 3: hipLaunchKernelGGL((KERNEL<3>), grid, block, 0, stream, set); break;             \
-    case 4: hipLaunchKernelGGL((KERNEL<4>), grid, block, 0, stream, set); break;             \
-    case 6: hipLaunchKernelGGL((KERNEL<6>), grid, block, 0, stream, set); break;             \
-    case 8: hipLaunchKernelGGL((KERNEL<8>), grid, block, 0, stream, set); break;             \
-    case 12: hipLaunchKernelGGL((KERNEL<12>), grid, block, 0, stream, set); break;           \
-    case 16: hipLaunchKernelGGL((KERNEL<16>), grid, block, 0, stream, set); break;           \
-    default: hipLaunchKernelGGL(quant_stream_kernel, grid, block, 0, stream, set);           \
+#define BL_QUANT_SWITCH(KERNEL, ...)                                                          \
+  switch (nc) {                                                                               \
+    case 1: hipLaunchKernelGGL((KERNEL<1 __VA_ARGS__>), grid, block, 0, stream, set); break;  \
+    case 2: hipLaunchKernelGGL((KERNEL<2 __VA_ARGS__>), grid, block, 0, stream, set); break;  \
+    case 3: hipLaunchKernelGGL((KERNEL<3 __VA_ARGS__>), grid, block, 0, stream, set); break;  \
+    case 4: hipLaunchKernelGGL((KERNEL<4 __VA_ARGS__>), grid, block, 0, stream, set); break;  \
+    case 6: hipLaunchKernelGGL((KERNEL<6 __VA_ARGS__>), grid, block, 0, stream, set); break;  \
+    case 8: hipLaunchKernelGGL((KERNEL<8 __VA_ARGS__>), grid, block, 0, stream, set); break;  \
+    case 12: hipLaunchKernelGGL((KERNEL<12 __VA_ARGS__>), grid, block, 0, stream, set); break; \
+    case 16: hipLaunchKernelGGL((KERNEL<16 __VA_ARGS__>), grid, block, 0, stream, set); break; \
+    default: hipLaunchKernelGGL(quant_stream_kernel, grid, block, 0, stream, set);            \
   }
 
-hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, hipStream_t stream) {
+hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hipStream_t stream) {
   if (set.total <= 0) return hipSuccess;
+  if (shared && act != kActNone) return hipErrorInvalidValue;
   const int nc = quant_chunks(max_k);
   const dim3 grid(set.total), block(256);
   if (shared) {
     BL_QUANT_SWITCH(quant_shared_kernel)
+  } else if (act == kActSilu) {
+    BL_QUANT_SWITCH(quant_reg_kernel, , kActSilu)
+  } else if (act == kActGeluTanh) {
+    BL_QUANT_SWITCH(quant_reg_kernel, , kActGeluTanh)
   } else {
-    BL_QUANT_SWITCH(quant_reg_kernel)
+    BL_QUANT_SWITCH(quant_reg_kernel, , kActNone)
   }
 #undef BL_QUANT_SWITCH
   return hipGetLastError();

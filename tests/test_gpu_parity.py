@@ -405,6 +405,80 @@ def test_group_forward_in_cuda_graph():
                 assert torch.equal(it["y"], ys), f"replay {rep}"
 
 
+# ---------------------------------------------------------------- FFN glue ---
+# The down projection fed by act(gate) * up ("BitNet Embeddings GGUF
+# Conversion Implementation", s4.5 FFN per-projection norms): the GPU forms
+# the product in fp32 registers, the oracle in double; codes and outputs meet
+# the same criteria as the plain path.
+
+def glu_inputs(act, M, K, N=None, seed=0):
+    gate = inputs.activations(22, seed, 2 * act, M, K) * np.float32(2.0)
+    up = inputs.activations(22, seed, 2 * act + 1, M, K)
+    nw = inputs.norm_weight(22, seed, act, K)
+    if M > 3:
+        gate[1] = 0.0               # zero product: zero codes, factor 0
+        gate[2] = -20.0             # activation ~0 but not 0: a tiny row
+        up[3] = 0.0
+    out = [gate, up, nw]
+    if N is not None:
+        W = inputs.weight(22, seed, act, N, K)
+        packed, scale = oracle.i2s_pack(W)
+        out += [packed, scale]
+    return out
+
+
+GLU_QUANT_CASES = [(act, M, K) for act in (bl.ACT_SILU, bl.ACT_GELU_TANH)
+                   for M, K in ((1, 3072), (8, 2048), (300, 3072), (257, 640), (6, 8192))]
+
+
+@pytest.mark.parametrize("act,M,K", GLU_QUANT_CASES)
+def test_glu_quant_parity(act, M, K):
+    gate, up, nw = glu_inputs(act, M, K)
+    xq, f = bl.bitlinear_glu_quant(dev(gate), dev(up), act, dev(nw), EPS)
+    q_ref, f_ref = oracle.glu_quant(gate, up, act, nw, EPS)
+    h = oracle.glu(gate, up, act)
+    flips = check_codes(host(xq), q_ref, h, nw)
+    check_factor(host(f), f_ref)
+    log(f"glu quant act={act} M={M} K={K}: {flips} code flips")
+
+
+GLU_FWD_CASES = [(act, M, K, N) for act in (bl.ACT_SILU, bl.ACT_GELU_TANH)
+                 for M, K, N in ((1, 3072, 1024), (4, 2048, 640), (16, 3072, 96), (17, 2048, 640),
+                                 (512, 2048, 640), (300, 3072, 1024))]
+
+
+@pytest.mark.parametrize("act,M,K,N", GLU_FWD_CASES)
+def test_glu_forward_parity_and_hooks(act, M, K, N):
+    gate, up, nw, packed, scale = glu_inputs(act, M, K, N, seed=1)
+    dg, du, dn, dp = dev(gate), dev(up), dev(nw), dev(packed)
+    y = bl.bitlinear_glu_forward(dg, du, act, dn, dp, scale, N, EPS)
+    ref = oracle.glu_bitlinear(gate, up, act, nw, packed, N, EPS)
+    assert rel_l2(host(y), ref) <= 1e-3
+    if M > 3:
+        assert not np.any(host(y)[1])                  # the zero-product row
+    # forward == fp32 epilogue of matmul_i32 o glu_quant, bit for bit
+    xq, f = bl.bitlinear_glu_quant(dg, du, act, dn, EPS)
+    acc = bl.bitlinear_matmul_i32(xq, dp, N)
+    y2 = acc.to(torch.float32) * (f / torch.tensor(scale, dtype=torch.float32, device=DEV))[:, None]
+    assert torch.equal(y, y2)
+
+
+def test_glu_forward_qwen_down_full_size_sampled_rows():
+    # The Qwen3 FFN down projection at the long-context size (M = 32768,
+    # K = 3072 -> N = 1024, SiLU), checked on sampled rows.
+    act, M, K, N = bl.ACT_SILU, 32768, 3072, 1024
+    dg = inputs.activations_device(torch, 22, 9, 0, M, K, DEV)
+    du = inputs.activations_device(torch, 22, 9, 1, M, K, DEV)
+    nw = inputs.norm_weight(22, 9, 0, K)
+    W = inputs.weight(22, 9, 0, N, K)
+    packed, scale = oracle.i2s_pack(W)
+    y = bl.bitlinear_glu_forward(dg, du, act, dev(nw), dev(packed), scale, N, EPS)
+    rows = inputs.sample_rows(M, 16, seed=9)
+    idx = torch.as_tensor(rows, device=DEV)
+    ref = oracle.glu_bitlinear(host(dg[idx]), host(du[idx]), act, nw, packed, N, EPS)
+    assert rel_l2(host(y[idx]), ref) <= 1e-3
+
+
 # ------------------------------------------ full-size workloads, sampled ---
 
 def _sampled_check(wid, rows_per, group_items, refs):

@@ -150,6 +150,24 @@ def test_quant_and_matmul_validation():
     assert mm(A, A, 0, 128, 8, A, None) == bl.BL_OK
 
 
+def test_glu_validation():
+    gq, gf = bl.lib.bitlinear_glu_quant, bl.lib.bitlinear_glu_forward
+    S, G = bl.ACT_SILU, bl.ACT_GELU_TANH
+    assert gq(0, A, S, A, 4, 128, 1e-6, A, A, None) == bl.BL_ERR_INVALID_ARGUMENT   # null gate
+    assert gq(A, 0, S, A, 4, 128, 1e-6, A, A, None) == bl.BL_ERR_INVALID_ARGUMENT   # null up
+    assert gq(A, A, 2, A, 4, 128, 1e-6, A, A, None) == bl.BL_ERR_INVALID_ARGUMENT   # unknown act
+    assert gq(A, A, -1, A, 4, 128, 1e-6, A, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert gq(A, A, G, A, 4, 100, 1e-6, A, A, None) == bl.BL_ERR_UNSUPPORTED        # K % 128
+    assert gq(A, MIS, G, A, 4, 128, 1e-6, A, A, None) == bl.BL_ERR_MISALIGNED
+    assert gq(A, A, G, A, 0, 128, 1e-6, A, A, None) == bl.BL_OK                     # M = 0
+    assert gf(A, 0, S, A, A, 1.0, 4, 128, 8, 1e-6, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert gf(A, A, 7, A, A, 1.0, 4, 128, 8, 1e-6, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert gf(A, A, S, A, A, 0.0, 4, 128, 8, 1e-6, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert gf(A, A, S, A, A, 1.0, 4, 192, 8, 1e-6, A, None) == bl.BL_ERR_UNSUPPORTED
+    assert gf(A, MIS, S, A, A, 1.0, 4, 128, 8, 1e-6, A, None) == bl.BL_ERR_MISALIGNED
+    assert gf(A, A, S, A, A, 1.0, 0, 128, 8, 1e-6, A, None) == bl.BL_OK
+
+
 def test_probe_validation():
     lib = bl.lib
     assert lib.bl_probe_read(None, 64, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT
