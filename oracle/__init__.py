@@ -123,15 +123,22 @@ def i2s_unpack(packed: np.ndarray, K: int, N: int) -> tuple[np.ndarray, float]:
     return q, float(scale[0])
 
 
-def quant(x: np.ndarray, norm_w: np.ndarray, eps: float) -> tuple[np.ndarray, np.ndarray]:
-    """x float32 [M, K], norm_w float32 [K] -> (int8 codes [M, K], float64 factor [M])."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
+def _norm(norm_w):
+    """norm_w as float32 (None: no per-projection norm) and its pointer."""
+    if norm_w is None:
+        return None, None
     norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
+    return norm_w, _ptr(norm_w)
+
+
+def quant(x: np.ndarray, norm_w, eps: float) -> tuple[np.ndarray, np.ndarray]:
+    """x float32 [M, K], norm_w float32 [K] or None -> (int8 codes [M, K], float64 factor [M])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    norm_w, pn = _norm(norm_w)
     M, K = x.shape
     q = np.zeros((M, K), dtype=np.int8)
     factor = np.zeros(M, dtype=np.float64)
-    _check(_load().ref_quant(_ptr(x), _ptr(norm_w), M, K, eps, _ptr(q), _ptr(factor)),
-           "ref_quant")
+    _check(_load().ref_quant(_ptr(x), pn, M, K, eps, _ptr(q), _ptr(factor)), "ref_quant")
     return q, factor
 
 
@@ -154,15 +161,15 @@ def epilogue(acc: np.ndarray, factor: np.ndarray, scale: float) -> np.ndarray:
     return y
 
 
-def bitlinear(x: np.ndarray, norm_w: np.ndarray, packed: np.ndarray, N: int,
+def bitlinear(x: np.ndarray, norm_w, packed: np.ndarray, N: int,
               eps: float) -> np.ndarray:
-    """The whole forward path: float32 [M, K] -> float32 [M, N]."""
+    """The whole forward path: float32 [M, K] -> float32 [M, N] (norm_w None: no norm)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
+    norm_w, pn = _norm(norm_w)
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     M, K = x.shape
     y = np.zeros((M, N), dtype=np.float32)
-    _check(_load().ref_bitlinear(_ptr(x), _ptr(norm_w), _ptr(packed), M, K, N, eps, _ptr(y)),
+    _check(_load().ref_bitlinear(_ptr(x), pn, _ptr(packed), M, K, N, eps, _ptr(y)),
            "ref_bitlinear")
     return y
 
@@ -187,11 +194,11 @@ def glu_quant(gate: np.ndarray, up: np.ndarray, kind: int, norm_w: np.ndarray,
     """Down-projection input steps on act(gate) * up: (int8 codes [M, K], float64 factor [M])."""
     gate = np.ascontiguousarray(gate, dtype=np.float32)
     up = np.ascontiguousarray(up, dtype=np.float32)
-    norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
+    norm_w, pn = _norm(norm_w)
     M, K = gate.shape
     q = np.zeros((M, K), dtype=np.int8)
     factor = np.zeros(M, dtype=np.float64)
-    _check(_load().ref_glu_quant(_ptr(gate), _ptr(up), kind, _ptr(norm_w), M, K, eps, _ptr(q),
+    _check(_load().ref_glu_quant(_ptr(gate), _ptr(up), kind, pn, M, K, eps, _ptr(q),
                                  _ptr(factor)), "ref_glu_quant")
     return q, factor
 
@@ -201,10 +208,10 @@ def glu_bitlinear(gate: np.ndarray, up: np.ndarray, kind: int, norm_w: np.ndarra
     """The down projection fed by act(gate) * up: float32 [M, K] pair -> float32 [M, N]."""
     gate = np.ascontiguousarray(gate, dtype=np.float32)
     up = np.ascontiguousarray(up, dtype=np.float32)
-    norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
+    norm_w, pn = _norm(norm_w)
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     M, K = gate.shape
     y = np.zeros((M, N), dtype=np.float32)
-    _check(_load().ref_glu_bitlinear(_ptr(gate), _ptr(up), kind, _ptr(norm_w), _ptr(packed), M, K,
+    _check(_load().ref_glu_bitlinear(_ptr(gate), _ptr(up), kind, pn, _ptr(packed), M, K,
                                      N, eps, _ptr(y)), "ref_glu_bitlinear")
     return y

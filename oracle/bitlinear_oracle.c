@@ -44,6 +44,10 @@
  *       approximation of GELU, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
  *       (Hendrycks and Gimpel's published form); the glue product and the
  *       down projection's input steps run in double.
+ *   R9  A projection without a norm weight (norm_w NULL; [EMB s4.5]: the
+ *       projection's input is the shared input itself when its norm tensor
+ *       is absent) is quantized from x unnormalised: codes from max|x|,
+ *       factor = max|x| / 127.
  */
 #include <math.h>
 #include <stdint.h>
@@ -134,16 +138,20 @@ int ref_i2s_unpack(const uint8_t* packed, int64_t K, int64_t N, int8_t* q_out, f
  *   q     = clamp(round(xhat * 127 / a), -127, 127)
  *   factor= a / 127       (the activation dequantization factor)
  * All arithmetic in double. */
-/* One row of the steps above, on a row given in double. */
+/* One row of the steps above, on a row given in double.  norm_w NULL: no
+ * RMSNorm (R9), xhat = x. */
 static void quant_row(const double* row, const float* norm_w, int64_t K, float eps, int8_t* q,
                       double* factor) {
-    double ss = 0.0;
-    for (int64_t k = 0; k < K; ++k) ss += row[k] * row[k];
-    double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+    double r = 1.0;
+    if (norm_w) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) ss += row[k] * row[k];
+        r = 1.0 / sqrt(ss / (double)K + (double)eps);
+    }
 
     double a = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        double xhat = row[k] * r * (double)norm_w[k];
+        double xhat = norm_w ? row[k] * r * (double)norm_w[k] : row[k];
         if (fabs(xhat) > a) a = fabs(xhat);
     }
     if (a == 0.0) {
@@ -153,7 +161,7 @@ static void quant_row(const double* row, const float* norm_w, int64_t K, float e
     }
     double s = 127.0 / a;
     for (int64_t k = 0; k < K; ++k) {
-        double xhat = row[k] * r * (double)norm_w[k];
+        double xhat = norm_w ? row[k] * r * (double)norm_w[k] : row[k];
         double v = nearbyint(xhat * s);
         if (v > 127.0) v = 127.0;
         if (v < -127.0) v = -127.0;
@@ -164,7 +172,7 @@ static void quant_row(const double* row, const float* norm_w, int64_t K, float e
 
 int ref_quant(const float* x, const float* norm_w, int64_t M, int64_t K, float eps,
               int8_t* q_out, double* factor_out) {
-    if ((M > 0 && (!x || !q_out || !factor_out)) || !norm_w || M < 0 || K <= 0) return REF_ERR_ARG;
+    if ((M > 0 && (!x || !q_out || !factor_out)) || M < 0 || K <= 0) return REF_ERR_ARG;
     double* row = (double*)malloc((size_t)K * sizeof(double));
     if (!row) return REF_ERR_NOMEM;
     for (int64_t m = 0; m < M; ++m) {
@@ -197,7 +205,7 @@ int ref_glu(const float* gate, const float* up, int act, int64_t n, double* h_ou
  * absmax int8 quantization above, all in double. */
 int ref_glu_quant(const float* gate, const float* up, int act, const float* norm_w, int64_t M,
                   int64_t K, float eps, int8_t* q_out, double* factor_out) {
-    if ((M > 0 && (!gate || !up || !q_out || !factor_out)) || !norm_w || M < 0 || K <= 0)
+    if ((M > 0 && (!gate || !up || !q_out || !factor_out)) || M < 0 || K <= 0)
         return REF_ERR_ARG;
     double* row = (double*)malloc((size_t)K * sizeof(double));
     if (!row) return REF_ERR_NOMEM;

@@ -422,3 +422,44 @@ def test_glu_path_equals_float64_dequantized_product(kind):
     r = 1.0 / np.sqrt((h * h).mean(axis=1) + 1e-6)
     xhat = h * r[:, None] * nw.astype(np.float64)
     assert np.all(np.abs(xhat - q * f[:, None]) <= 0.5 * f[:, None] * (1 + 1e-12))
+
+
+# ---------------------------------------------------------------- no norm ---
+# A projection without its own norm weight takes the shared input as it is
+# ("BitNet Embeddings GGUF Conversion Implementation", s4.5: the input is used
+# directly when the projection's norm tensor is absent).
+
+def test_no_norm_codes_and_closed_form_factor():
+    M, K = 5, 384
+    x = inputs.activations(13, 0, 0, M, K, heavy_tail=True)
+    x[2] = 0.0
+    q, f = oracle.quant(x, None, 1e-6)
+    # codes: RMSNorm's positive row scalar cancels in x*127/max|x|, so they
+    # equal the codes of the normalised path with a unit norm weight
+    q1, f1 = oracle.quant(x, np.ones(K, np.float32), 1e-6)
+    assert np.array_equal(q, q1)
+    # factor: max|x| / 127 exactly (no normalisation), 0 for a zero row
+    assert np.array_equal(f, np.abs(x.astype(np.float64)).max(axis=1) / 127.0)
+    assert f[2] == 0.0 and not np.any(q[2])
+    # and the normalised factor is the plain one times r = 1/sqrt(mean(x^2) + eps)
+    r = 1.0 / np.sqrt((x.astype(np.float64) ** 2).mean(axis=1) + 1e-6)
+    nz = f > 0
+    assert np.allclose(f1[nz], f[nz] * r[nz], rtol=1e-14)
+
+
+def test_no_norm_path_equals_float64_dequantized_product():
+    M, K, N = 4, 256, 9
+    x = inputs.activations(13, 1, 0, M, K)
+    W = inputs.weight(13, 1, 0, N, K)
+    packed, scale = oracle.i2s_pack(W)
+    y = oracle.bitlinear(x, None, packed, N, 1e-6)
+    q, f = oracle.quant(x, None, 1e-6)
+    qw, _ = oracle.i2s_unpack(packed, K, N)
+    ref = (q.astype(np.float64) * f[:, None]) @ (qw.astype(np.float64) / scale).T
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 1e-7
+    # grid-exact: integer x with max 127 is already on the code grid (factor 1)
+    xi = inputs.rng(13, 2, 0, 2).integers(-127, 128, size=(1, K)).astype(np.float32)
+    xi[0, 7] = 127.0
+    yi = oracle.bitlinear(xi, None, packed, N, 1e-6)
+    exact = (qw.astype(np.float64) @ xi[0].astype(np.float64)) / scale
+    assert np.array_equal(yi[0], exact.astype(np.float32))
