@@ -153,14 +153,16 @@ def time_launches(torch, group, steps: int):
     return info, launch_ms
 
 
-def launch_bytes(kind: str, M: int, K: int, N: int) -> int:
-    """Algorithmic HBM bytes of one BitLinear in a launch of the given kind."""
+def launch_bytes(kind: str, M: int, K: int, N: int, norm: bool = True) -> int:
+    """Algorithmic HBM bytes of one BitLinear in a launch of the given kind
+    (norm False: a projection without a norm weight, which is not read)."""
+    nw = 4 * K if norm else 0
     if kind in ("decode", "prefill"):  # packed weights, int8 codes, factor + row sum, fp32 y
         return N * K // 4 + M * K + 8 * M + 4 * M * N
     if kind == "decode_fused":   # packed weights, fp32 x and norm weight, fp32 y
-        return N * K // 4 + 4 * M * K + 4 * K + 4 * M * N
+        return N * K // 4 + 4 * M * K + nw + 4 * M * N
     if kind == "quant":          # fp32 x and norm weight in, int8 codes, factor + row sum out
-        return 4 * M * K + 4 * K + M * K + 8 * M
+        return 4 * M * K + nw + M * K + 8 * M
     raise ValueError(kind)
 
 
@@ -208,24 +210,32 @@ def bench_decode(torch, bl, args):
         x.copy_(torch.from_numpy(inputs.activations(2, p["layer"], p["proj"], 1, K)))
         y = arena.take(4 * N, torch.float32, (1, N))
         items.append(dict(x=x, norm_w=nw, packed_w=pw, w_scale=p["scale"], eps=inputs.EPS, N=N, y=y))
-    group = bl.Group(items)
-    ms, ms_events = time_steps(torch, group, args.steps, args.warmup)
-    info, launch_ms = time_launches(torch, group, args.steps)
-    group.close()
     weight_bytes = sum(p["N"] * p["K"] // 4 for p in projs)
-    # Algorithmic bytes per launch (launch_bytes, M = 1): the quantization
-    # launch when there is one, then one decode launch per superblock count
-    # ceil(K/256).
-    per_launch = []
-    for d, t in zip(info, launch_ms):
-        members = [p for p in projs if (p["K"] + 255) // 256 == d["bucket"]] if d["bucket"] else projs
-        nbytes = sum(launch_bytes(d["kind"], 1, p["K"], p["N"]) for p in members)
-        per_launch.append(dict(kind=d["kind"], bucket=d["bucket"], bitlinears=len(members),
-                               K=members[0]["K"], bytes=nbytes, us=t * 1e3,
-                               GBps=nbytes / (t * 1e-3) / 1e9))
-    dom = max(per_launch, key=lambda d: d["bytes"])
-    return dict(R=R, projs=projs, ms=ms, ms_events=ms_events, per_launch=per_launch, dominant=dom,
-                weight_bytes=weight_bytes, value=weight_bytes / (ms * 1e-3) / 1e9)
+
+    def run(items, norm):
+        group = bl.Group(items)
+        ms, ms_events = time_steps(torch, group, args.steps, args.warmup)
+        info, launch_ms = time_launches(torch, group, args.steps)
+        group.close()
+        # Algorithmic bytes per launch (launch_bytes, M = 1): the quantization
+        # launch when there is one, then one decode launch per superblock
+        # count ceil(K/256).
+        per_launch = []
+        for d, t in zip(info, launch_ms):
+            members = [p for p in projs if (p["K"] + 255) // 256 == d["bucket"]] if d["bucket"] else projs
+            nbytes = sum(launch_bytes(d["kind"], 1, p["K"], p["N"], norm) for p in members)
+            per_launch.append(dict(kind=d["kind"], bucket=d["bucket"], bitlinears=len(members),
+                                   K=members[0]["K"], bytes=nbytes, us=t * 1e3,
+                                   GBps=nbytes / (t * 1e-3) / 1e9))
+        dom = max(per_launch, key=lambda d: d["bytes"])
+        return dict(ms=ms, ms_events=ms_events, per_launch=per_launch, dominant=dom,
+                    value=weight_bytes / (ms * 1e-3) / 1e9)
+
+    out = run(items, True)
+    # the same step with projections that have no norm weight of their own
+    out["no_norm"] = run([dict(it, norm_w=None) for it in items], False)
+    out.update(R=R, projs=projs, weight_bytes=weight_bytes)
+    return out
 
 
 def bench_prefill(torch, bl, args):
@@ -257,9 +267,15 @@ def bench_prefill(torch, bl, args):
     assert [d["kind"] for d in info][-1] == "prefill" and all(
         d["kind"].startswith("quant") for d in info[:-1]), info
     quant_ms, mm_ms = float(sum(launch_ms[:-1])), launch_ms[-1]
+    # the quantization stage for projections without a norm weight
+    group = bl.Group([dict(it, norm_w=None) for it in items])
+    _, nn_ms = time_launches(torch, group, max(3, args.steps // 2))
+    group.close()
+    nn_quant_ms = float(sum(nn_ms[:-1]))
     ops = sum(2 * w.M * p["N"] * p["K"] for p in projs)
     return dict(projs=projs, xs=xs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, ops=ops, M=w.M,
-                tops=ops / (ms * 1e-3) / 1e12, mm_tops=ops / (mm_ms * 1e-3) / 1e12)
+                tops=ops / (ms * 1e-3) / 1e12, mm_tops=ops / (mm_ms * 1e-3) / 1e12,
+                no_norm_quant_ms=nn_quant_ms)
 
 
 def bench_ffn_glue(torch, bl, args):
@@ -485,6 +501,14 @@ def main():
         "measured_peaks": peaks,
     }
     out["roofline"]["frac_of_measured"] = round(dom["GBps"] / peaks["hbm_read_GBps"], 4)
+    nn = dec["no_norm"]
+    out["no_norm"] = {
+        "workload": "the decode step with norm_w NULL on every projection (no per-projection norm)",
+        "ms_per_step": round(nn["ms"], 5), "value": round(nn["value"], 2), "unit": "GB/s",
+        "launches_us": [{"kind": d["kind"], "K": d["K"], "us": round(d["us"], 2),
+                         "GBps": round(d["GBps"], 1)} for d in nn["per_launch"]],
+    }
+    log(f"decode without norm weights: {nn['ms']:.3f} ms/step, {nn['value']:.0f} GB/s weights")
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline_decode(dec["projs"], args.cpu_seconds)
     del dec
@@ -508,6 +532,8 @@ def main():
             },
             "stages_us": {"quant": round(pre["quant_ms"] * 1e3, 1), "matmul": round(pre["mm_ms"] * 1e3, 1)},
         }
+        out["no_norm"]["prefill_quant_us"] = round(pre["no_norm_quant_ms"] * 1e3, 1)
+        log(f"prefill quant without norm weights: {pre['no_norm_quant_ms']:.3f} ms")
         if not args.skip_cpu:
             pf["cpu_baseline"] = cpu_baseline_prefill(pre, args.cpu_seconds / 2)
         out["prefill"] = pf

@@ -94,7 +94,11 @@ bl_status i2s_pack(const float* w, int64_t K, int64_t N, uint8_t* packed, size_t
  * ("BitNet Embeddings GGUF Conversion Implementation", s1 and s4.5;
  * "BitNet Inference Framework", "Quantization (W1.58A8)").
  *   x        device [M][K] float32.
- *   norm_w   device [K] float32, the projection's norm weight, used as given.
+ *   norm_w   device [K] float32, the projection's norm weight, used as given;
+ *            or NULL for a projection without its own norm ("BitNet
+ *            Embeddings GGUF Conversion Implementation", s4.5: the input then
+ *            feeds the projection directly): no RMSNorm, codes =
+ *            rne(x * 127/max|x|), factor = max|x| / 127.
  *   packed_w device I2_S buffer of i2s_packed_bytes(K, N) bytes.
  *   w_scale  the float32 scale stored at the tail of packed_w (passed by
  *            value so that no device-to-host read is needed).
@@ -149,7 +153,7 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
  *        0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
  *   gate, up  device [M][K] float32 each, 16-byte aligned.
  * Everything else as in bitlinear_quant and bitlinear_forward (K is the down
- * projection's input width, the FFN size; norm_w its norm weight); an
+ * projection's input width, the FFN size; norm_w its norm weight or NULL); an
  * unknown act is BL_ERR_INVALID_ARGUMENT.  bitlinear_glu_forward uses the
  * library workspace (always the two-stage path) and returns
  * y = BitLinear_down(act(gate) * up).
@@ -189,7 +193,7 @@ bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
                                     share their x, one pass over x per set */
 typedef struct bl_desc {
     const float* x;          /* device [M][K] */
-    const float* norm_w;     /* device [K] */
+    const float* norm_w;     /* device [K], or NULL: no norm */
     const uint8_t* packed_w; /* device, I2_S */
     float w_scale;
     float eps;

@@ -145,6 +145,11 @@ def _dev(t, dtype, name: str, shape=None) -> int:
     return t.data_ptr()
 
 
+def _norm(norm_w, K):
+    """The norm weight's pointer, or None (no per-projection norm) for None."""
+    return None if norm_w is None else _dev(norm_w, _torch().float32, "norm_w", (K,))
+
+
 def bitlinear_forward(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y=None,
                       stream=None):
     """y[M, N] (float32) = BitLinear(x[M, K]) on the GPU; returns y."""
@@ -153,7 +158,7 @@ def bitlinear_forward(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _check(_lib.bitlinear_forward(
-        _dev(x, torch.float32, "x"), _dev(norm_w, torch.float32, "norm_w", (K,)),
+        _dev(x, torch.float32, "x"), _norm(norm_w, K),
         _dev(packed_w, torch.uint8, "packed_w"), w_scale, M, K, N, eps,
         _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)), "bitlinear_forward")
     return y
@@ -168,7 +173,7 @@ def bitlinear_quant(x, norm_w, eps: float, xq=None, x_factor=None, stream=None):
     if x_factor is None:
         x_factor = torch.empty((M,), dtype=torch.float32, device=x.device)
     _check(_lib.bitlinear_quant(
-        _dev(x, torch.float32, "x"), _dev(norm_w, torch.float32, "norm_w", (K,)), M, K, eps,
+        _dev(x, torch.float32, "x"), _norm(norm_w, K), M, K, eps,
         _dev(xq, torch.int8, "xq", (M, K)), _dev(x_factor, torch.float32, "x_factor", (M,)),
         _stream_handle(stream)), "bitlinear_quant")
     return xq, x_factor
@@ -190,7 +195,8 @@ class Group:
     """Many independent projections run as one launch per stage.
 
     ``items`` is a sequence of dicts with keys x, norm_w, packed_w, w_scale,
-    eps, N and y (torch tensors on the GPU where applicable).  The tensors are
+    eps, N and y (torch tensors on the GPU where applicable; norm_w None or
+    absent: no per-projection norm).  The tensors are
     kept referenced for the group's lifetime.
     """
 
@@ -202,7 +208,7 @@ class Group:
             x, y = it["x"], it["y"]
             M, K = x.shape
             descs[i] = BlDesc(_dev(x, torch.float32, "x"),
-                              _dev(it["norm_w"], torch.float32, "norm_w", (K,)),
+                              _norm(it.get("norm_w"), K),
                               _dev(it["packed_w"], torch.uint8, "packed_w"),
                               float(it["w_scale"]), float(it["eps"]), M, K, int(it["N"]),
                               _dev(y, torch.float32, "y", (M, int(it["N"]))))
@@ -317,7 +323,7 @@ def bitlinear_glu_quant(gate, up, act: int, norm_w, eps: float, xq=None, x_facto
         x_factor = torch.empty((M,), dtype=torch.float32, device=gate.device)
     _check(_lib.bitlinear_glu_quant(
         _dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up", (M, K)), act,
-        _dev(norm_w, torch.float32, "norm_w", (K,)), M, K, eps, _dev(xq, torch.int8, "xq", (M, K)),
+        _norm(norm_w, K), M, K, eps, _dev(xq, torch.int8, "xq", (M, K)),
         _dev(x_factor, torch.float32, "x_factor", (M,)), _stream_handle(stream)),
         "bitlinear_glu_quant")
     return xq, x_factor
@@ -332,7 +338,7 @@ def bitlinear_glu_forward(gate, up, act: int, norm_w, packed_w, w_scale: float, 
         y = torch.empty((M, N), dtype=torch.float32, device=gate.device)
     _check(_lib.bitlinear_glu_forward(
         _dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up", (M, K)), act,
-        _dev(norm_w, torch.float32, "norm_w", (K,)), _dev(packed_w, torch.uint8, "packed_w"),
+        _norm(norm_w, K), _dev(packed_w, torch.uint8, "packed_w"),
         w_scale, M, K, N, eps, _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)),
         "bitlinear_glu_forward")
     return y

@@ -43,7 +43,7 @@ bl_status check_forward(const float* x, const float* norm_w, const uint8_t* pack
   if (st != BL_OK) return st;
   if ((st = check_eps(eps)) != BL_OK) return st;
   if (!(std::isfinite(w_scale) && w_scale > 0.0f)) return BL_ERR_INVALID_ARGUMENT;
-  if (!norm_w || !packed_w) return BL_ERR_INVALID_ARGUMENT;
+  if (!packed_w) return BL_ERR_INVALID_ARGUMENT;  // norm_w may be null: no norm
   if (M > 0 && (!x || !y)) return BL_ERR_INVALID_ARGUMENT;
   if (!aligned16(norm_w) || !aligned16(packed_w) || (M > 0 && (!aligned16(x) || !aligned16(y))))
     return BL_ERR_MISALIGNED;
@@ -186,7 +186,7 @@ bl_status bitlinear_quant(const float* x, const float* norm_w, int64_t M, int64_
     bl_status st = check_shape(M, K, 1);
     if (st != BL_OK) return st;
     if ((st = check_eps(eps)) != BL_OK) return st;
-    if (!norm_w || (M > 0 && (!x || !xq || !x_factor))) return BL_ERR_INVALID_ARGUMENT;
+    if (M > 0 && (!x || !xq || !x_factor)) return BL_ERR_INVALID_ARGUMENT;
     if (!aligned16(norm_w) || (M > 0 && (!aligned16(x) || !aligned16(xq) || !aligned16(x_factor))))
       return BL_ERR_MISALIGNED;
     if (M == 0) return BL_OK;
@@ -245,7 +245,7 @@ bl_status bitlinear_glu_quant(const float* gate, const float* up, int32_t act, c
     if (st != BL_OK) return st;
     if ((st = check_eps(eps)) != BL_OK) return st;
     if (act != BL_ACT_SILU && act != BL_ACT_GELU_TANH) return BL_ERR_INVALID_ARGUMENT;
-    if (!norm_w || (M > 0 && (!gate || !up || !xq || !x_factor))) return BL_ERR_INVALID_ARGUMENT;
+    if (M > 0 && (!gate || !up || !xq || !x_factor)) return BL_ERR_INVALID_ARGUMENT;
     if (!aligned16(norm_w) ||
         (M > 0 && (!aligned16(gate) || !aligned16(up) || !aligned16(xq) || !aligned16(x_factor))))
       return BL_ERR_MISALIGNED;

@@ -25,7 +25,7 @@ constexpr int kOob = 0x7FFFFFF0;
 // Workspace pointers (xq, factor, rowsum) belong to the library.
 struct Prob {
   const float* x;        // [M][K] f32 activations
-  const float* norm_w;   // [K] f32 norm weight
+  const float* norm_w;   // [K] f32 norm weight; null: no norm (u = x, r = 1)
   const uint8_t* w;      // I2_S codes, row n at byte n*K/4
   int8_t* xq;            // [M][K] int8 codes (workspace or caller's)
   float* factor;         // [M] absmax/127 (workspace or caller's)
@@ -197,9 +197,12 @@ __device__ __forceinline__ f4 glu4(f4 g, f4 u) {
 }
 
 // factor = max|RMSNorm(x) * norm_w| / 127 = r * max|u| / 127 with
-// r = 1/sqrt(mean(x^2) + eps), in double from the row's Sum(x^2).
-__device__ __forceinline__ float quant_factor(double ss, int K, float eps, float amax) {
-  const double r = 1.0 / sqrt(ss / static_cast<double>(K) + static_cast<double>(eps));
+// r = 1/sqrt(mean(x^2) + eps), in double from the row's Sum(x^2).  A
+// projection without a norm weight (norm == false) quantizes x as it is
+// ("BitNet Embeddings GGUF Conversion Implementation", s4.5: the input feeds
+// the projection directly when its norm tensor is absent): u = x, r = 1.
+__device__ __forceinline__ float quant_factor(double ss, int K, float eps, float amax, bool norm) {
+  const double r = norm ? 1.0 / sqrt(ss / static_cast<double>(K) + static_cast<double>(eps)) : 1.0;
   return static_cast<float>(r * static_cast<double>(amax) / 127.0);
 }
 

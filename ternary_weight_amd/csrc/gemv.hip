@@ -178,8 +178,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
     const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(P.x), 0, M * K * 4, kBufferDword3);
     const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(P.norm_w), 0, K * 4, kBufferDword3);
-    const int ux = (M * K * 4 + 1023) >> 10, un = (K * 4 + 1023) >> 10;
+        const_cast<float*>(P.norm_w), 0, P.norm_w ? K * 4 : 0, kBufferDword3);
+    const int ux = (M * K * 4 + 1023) >> 10, un = P.norm_w ? (K * 4 + 1023) >> 10 : 0;
     for (int i = wave; i < ux + un; i += 4) {
       const bool isx = i < ux;
       const int u = isx ? i : i - ux;
@@ -241,6 +241,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
     const int nch = K >> 2;
     const f4* xf = reinterpret_cast<const f4*>(xlds + fl.x);
     const f4* nw = reinterpret_cast<const f4*>(xlds + fl.nw);
+    const bool norm = P.norm_w != nullptr;  // else u = x, r = 1
     float* row_scale = reinterpret_cast<float*>(xlds + fl.rows);
     int* row_sum = reinterpret_cast<int*>(xlds + fl.rows + 64);
     for (int m = wave; m < M; m += 4) {
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
         if (c < nch) {
           const f4 xv = xf[m * nch + c];
           ss += sq4(xv);
-          amax = fmaxf(amax, absmax4(xv * nw[c]));
+          amax = fmaxf(amax, absmax4(norm ? xv * nw[c] : xv));
         }
       }
       const double ssd = wave_sum(static_cast<double>(ss));
@@ -262,12 +263,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
 #pragma unroll
       for (int j = 0; j < NSB; ++j) {
         const int c = lane + kWave * j;  // dword c of the padded row
-        const uint32_t q = c < nch ? codes4(xf[m * nch + c] * nw[c], amax, &sum) : 0u;
+        uint32_t q = 0u;
+        if (c < nch) {
+          const f4 xv = xf[m * nch + c];
+          q = codes4(norm ? xv * nw[c] : xv, amax, &sum);
+        }
         *reinterpret_cast<uint32_t*>(xlds + m * kpad + ((((c >> 2) ^ (m & 7))) << 4) + ((c & 3) << 2)) = q;
       }
       sum = wave_sum(sum);
       if (lane == 0) {
-        row_scale[m] = quant_factor(ssd, K, P.eps, amax) / P.w_scale;
+        row_scale[m] = quant_factor(ssd, K, P.eps, amax, norm) / P.w_scale;
         row_sum[m] = sum;
       }
     }

@@ -15,6 +15,9 @@
 // sums.  Bound: HBM, 4K bytes read + K bytes written per row (plus the norm
 // weight, an L2 hit).
 //
+// A projection without a norm weight (norm_w null) quantizes x unnormalised:
+// u = x and r = 1 (same kernels, the multiply and the rsqrt skipped).
+//
 // Projections that read the same input (q, k and v of a layer, or gate and
 // up: each normalises the shared x with its own weight, "BitNet Embeddings
 // GGUF Conversion Implementation" s4.5) form a share set in a grouped launch:
@@ -29,54 +32,61 @@ __device__ __forceinline__ void finish_row(const Prob& P, int m, double ss, floa
                                            int lane) {
   rs = wave_sum(rs);
   if (lane == 0) {
-    gptr_out<float>(P.factor)[m] = quant_factor(ss, P.K, P.eps, amax);
+    gptr_out<float>(P.factor)[m] = quant_factor(ss, P.K, P.eps, amax, P.norm_w != nullptr);
     if (P.rowsum) gptr_out<int32_t>(P.rowsum)[m] = rs;
   }
 }
 
 // NC: float4 chunks per lane held in registers (K <= 256*NC).  A workgroup
 // owns kQuantRows consecutive rows of one problem, kQuantRowsPerWave per wave.
-// ACT: the row is act(x) * up (FFN glue) instead of x.
-template <int NC, int ACT>
-__global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int local;
-  const int pi = find_prob(set, blockIdx.x, &local);
-  const Prob P = prob_at(set, pi);
+// ACT: the row is act(x) * up (FFN glue) instead of x.  NORM: the problem has
+// a norm weight (the rows of both kinds keep their loads in one block).
+template <int NC, int ACT, bool NORM>
+__device__ __forceinline__ void quant_reg_rows(const Prob& P, int m_begin, int lane) {
   const int nch = P.K >> 2;
-  const int m_begin = local * kQuantRows + wave_id() * kQuantRowsPerWave;
   const BL_GLOBAL f4* wr = gptr<f4>(P.norm_w);
   for (int r = 0; r < kQuantRowsPerWave; ++r) {
     const int m = m_begin + r;
     if (m >= P.M) break;
     const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m) * P.K);
     const BL_GLOBAL f4* ur = gptr<f4>(P.up + static_cast<int64_t>(m) * P.K);
-    {
-      f4 u[NC];
-      float ss = 0.f, amax = 0.f;
+    f4 u[NC];
+    float ss = 0.f, amax = 0.f;
 #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c = lane + kWave * i;
-        u[i] = f4{0.f, 0.f, 0.f, 0.f};
-        if (c < nch) {
-          const f4 xv = ACT == kActNone ? f4(xr[c]) : glu4<ACT>(f4(xr[c]), f4(ur[c]));
-          ss += sq4(xv);
-          u[i] = xv * wr[c];
-          amax = fmaxf(amax, absmax4(u[i]));
-        }
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      u[i] = f4{0.f, 0.f, 0.f, 0.f};
+      if (c < nch) {
+        const f4 xv = ACT == kActNone ? f4(xr[c]) : glu4<ACT>(f4(xr[c]), f4(ur[c]));
+        ss += sq4(xv);
+        u[i] = NORM ? xv * wr[c] : xv;
+        amax = fmaxf(amax, absmax4(u[i]));
       }
-      const double ssd = wave_sum(static_cast<double>(ss));
-      amax = wave_max(amax);
-      BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
-      int rs = 0;
-#pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c = lane + kWave * i;
-        if (c < nch) qrow[c] = codes4(u[i], amax, &rs);
-      }
-      finish_row(P, m, ssd, amax, rs, lane);
     }
+    const double ssd = wave_sum(static_cast<double>(ss));
+    amax = wave_max(amax);
+    BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
+    int rs = 0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      if (c < nch) qrow[c] = codes4(u[i], amax, &rs);
+    }
+    finish_row(P, m, ssd, amax, rs, lane);
   }
+}
+
+template <int NC, int ACT>
+__global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int local;
+  const int pi = find_prob(set, blockIdx.x, &local);
+  const Prob P = prob_at(set, pi);
+  const int m_begin = local * kQuantRows + wave_id() * kQuantRowsPerWave;
+  if (P.norm_w)
+    quant_reg_rows<NC, ACT, true>(P, m_begin, lane);
+  else
+    quant_reg_rows<NC, ACT, false>(P, m_begin, lane);
 }
 
 // Share sets: the workgroup's kQuantRows rows are quantized for every problem
@@ -85,65 +95,75 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
 // waves of a workgroup read the same rows at the same time, so x comes from
 // HBM once and from L2 for the siblings; each wave's Sum(x^2) has the order
 // of the plain variant, hence the same factor.
-template <int NC>
-__global__ __launch_bounds__(256) void quant_shared_kernel(ProbSet set) {
+template <int NC, bool NORM>
+__device__ __forceinline__ void quant_shared_rows(const Prob& P, const Prob& Q, int m0, int lane) {
   constexpr int R = NC >= 16 ? 1 : (16 / NC >= kQuantRows ? kQuantRows : 16 / NC);
-  const int lane = threadIdx.x & (kWave - 1);
-  int local;
-  const int pi = find_prob(set, blockIdx.x, &local);
-  const Prob P = prob_at(set, pi);
   const int nch = P.K >> 2;
-  const int share = P.share > 1 ? P.share : 1;
-  const int m0 = local * kQuantRows;
-  for (int p = wave_id(); p < share; p += 4) {
-    const Prob Q = p == 0 ? P : prob_at(set, pi + p);
+  f4 w[NC];
+  if (NORM) {
     const BL_GLOBAL f4* wr = gptr<f4>(Q.norm_w);
-    f4 w[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = lane + kWave * i;
       w[i] = c < nch ? wr[c] : f4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int r0 = 0; r0 < kQuantRows; r0 += R) {
-      f4 xv[R][NC];
+  }
+  for (int r0 = 0; r0 < kQuantRows; r0 += R) {
+    f4 xv[R][NC];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int m = m0 + r0 + r;
-        const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m < P.M ? m : 0) * P.K);
+    for (int r = 0; r < R; ++r) {
+      const int m = m0 + r0 + r;
+      const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m < P.M ? m : 0) * P.K);
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-          const int c = lane + kWave * i;
-          xv[r][i] = (m < P.M && c < nch) ? xr[c] : f4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int m = m0 + r0 + r;
-        if (m >= P.M) break;
-        float ss = 0.f, amax = 0.f;
-        f4 u[NC];
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-          const int c = lane + kWave * i;
-          u[i] = f4{0.f, 0.f, 0.f, 0.f};
-          if (c < nch) {
-            ss += sq4(xv[r][i]);
-            u[i] = xv[r][i] * w[i];
-            amax = fmaxf(amax, absmax4(u[i]));
-          }
-        }
-        const double ssd = wave_sum(static_cast<double>(ss));
-        amax = wave_max(amax);
-        BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(Q.xq + static_cast<int64_t>(m) * Q.K);
-        int rs = 0;
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-          const int c = lane + kWave * i;
-          if (c < nch) qrow[c] = codes4(u[i], amax, &rs);
-        }
-        finish_row(Q, m, ssd, amax, rs, lane);
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + kWave * i;
+        xv[r][i] = (m < P.M && c < nch) ? xr[c] : f4{0.f, 0.f, 0.f, 0.f};
       }
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int m = m0 + r0 + r;
+      if (m >= P.M) break;
+      float ss = 0.f, amax = 0.f;
+      f4 u[NC];
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + kWave * i;
+        u[i] = f4{0.f, 0.f, 0.f, 0.f};
+        if (c < nch) {
+          ss += sq4(xv[r][i]);
+          u[i] = NORM ? xv[r][i] * w[i] : xv[r][i];
+          amax = fmaxf(amax, absmax4(u[i]));
+        }
+      }
+      const double ssd = wave_sum(static_cast<double>(ss));
+      amax = wave_max(amax);
+      BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(Q.xq + static_cast<int64_t>(m) * Q.K);
+      int rs = 0;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + kWave * i;
+        if (c < nch) qrow[c] = codes4(u[i], amax, &rs);
+      }
+      finish_row(Q, m, ssd, amax, rs, lane);
+    }
+  }
+}
+
+template <int NC>
+__global__ __launch_bounds__(256) void quant_shared_kernel(ProbSet set) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int local;
+  const int pi = find_prob(set, blockIdx.x, &local);
+  const Prob P = prob_at(set, pi);
+  const int share = P.share > 1 ? P.share : 1;
+  const int m0 = local * kQuantRows;
+  for (int p = wave_id(); p < share; p += 4) {
+    const Prob Q = p == 0 ? P : prob_at(set, pi + p);
+    if (Q.norm_w)
+      quant_shared_rows<NC, true>(P, Q, m0, lane);
+    else
+      quant_shared_rows<NC, false>(P, Q, m0, lane);
   }
 }
 
@@ -177,21 +197,24 @@ __device__ void quant_stream_row(const Prob& P, int m, int lane) {
   const int nch = P.K >> 2;
   const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m) * P.K);
   const BL_GLOBAL f4* wr = gptr<f4>(P.norm_w);
+  const bool norm = P.norm_w != nullptr;
 
   double ss = 0.0;
   float amax = 0.f;
   for (int c = lane; c < nch; c += kWave) {
     const f4 xv = stream_in(P, xr, m, c);
-    const f4 wv = wr[c];
     ss += static_cast<double>(sq4(xv));
-    amax = fmaxf(amax, absmax4(xv * wv));
+    amax = fmaxf(amax, absmax4(norm ? xv * wr[c] : xv));
   }
   ss = wave_sum(ss);
   amax = wave_max(amax);
 
   BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
   int rs = 0;
-  for (int c = lane; c < nch; c += kWave) qrow[c] = codes4(stream_in(P, xr, m, c) * wr[c], amax, &rs);
+  for (int c = lane; c < nch; c += kWave) {
+    const f4 xv = stream_in(P, xr, m, c);
+    qrow[c] = codes4(norm ? xv * wr[c] : xv, amax, &rs);
+  }
   finish_row(P, m, ss, amax, rs, lane);
 }
 

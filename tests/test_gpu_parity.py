@@ -405,6 +405,92 @@ def test_group_forward_in_cuda_graph():
                 assert torch.equal(it["y"], ys), f"replay {rep}"
 
 
+# ------------------------------------------------------------ no norm ---
+# A projection without its own norm weight ("BitNet Embeddings GGUF
+# Conversion Implementation", s4.5: the shared input feeds the projection
+# directly): norm_w NULL, codes from max|x|, factor max|x|/127.  Every
+# quantization variant (register, shared, streaming, fused decode) takes it.
+
+NO_NORM_QUANT_CASES = [(1, 128), (8, 1024), (300, 3072), (7, 4096), (257, 640), (3, 8192)]
+
+
+@pytest.mark.parametrize("M,K", NO_NORM_QUANT_CASES)
+def test_no_norm_quant_parity(M, K):
+    x = inputs.activations(23, 0, K, M, K, heavy_tail=True)
+    if M > 3:
+        x[1] = 0.0
+        x[2] *= 1e-36
+    xq, f = bl.bitlinear_quant(dev(x), None, EPS)
+    q_ref, f_ref = oracle.quant(x, None, EPS)
+    flips = check_codes(host(xq), q_ref, x, np.ones(K, np.float32))
+    # max|x| is exact in fp32, so the factor is the correctly rounded max|x|/127
+    assert np.array_equal(host(f), f_ref.astype(np.float32))
+    log(f"no-norm quant M={M} K={K}: {flips} flips")
+
+
+NO_NORM_FWD_CASES = [(1, 1024, 3072), (4, 2048, 640), (16, 3072, 96), (16, 4096, 48),
+                     (17, 2048, 640), (300, 1024, 1024), (5, 8192, 130)]
+
+
+@pytest.mark.parametrize("M,K,N", NO_NORM_FWD_CASES)
+def test_no_norm_forward_parity_and_hooks(M, K, N):
+    # decode fused (small M*K), decode unfused, prefill and the streaming
+    # quantization (K 8192); forward == fp32 epilogue of matmul_i32 o quant.
+    x, _, packed, scale = proj_inputs(23, 1, K, M, K, N, heavy=True)
+    if M > 2:
+        x[M // 2] = 0.0
+    dx, dp = dev(x), dev(packed)
+    y = bl.bitlinear_forward(dx, None, dp, scale, N, EPS)
+    ref = oracle.bitlinear(x, None, packed, N, EPS)
+    assert rel_l2(host(y), ref) <= 1e-3
+    if M > 2:
+        assert not np.any(host(y)[M // 2])
+    xq, f = bl.bitlinear_quant(dx, None, EPS)
+    acc = bl.bitlinear_matmul_i32(xq, dp, N)
+    y2 = acc.to(torch.float32) * (f / torch.tensor(scale, dtype=torch.float32, device=DEV))[:, None]
+    assert torch.equal(y, y2)
+
+
+def test_no_norm_group_mixed_with_normed_share_set():
+    # One x read by projections with and without a norm weight: they share
+    # the quantization pass (and, at M <= 16, the fused decode), each with its
+    # own arithmetic; results equal separate calls bit for bit.
+    items, singles = [], []
+    for M in (1, 8, 300):
+        for K in (1024, 3072):
+            x = dev(inputs.activations(24, M, K, M, K))
+            for i, N in enumerate((256, 128, 96)):
+                W = inputs.weight(24, M, K + i, N, K)
+                packed, scale = oracle.i2s_pack(W)
+                nw = None if i == 1 else dev(inputs.norm_weight(24, M, K + i, K))
+                it = dict(x=x, norm_w=nw, packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                          y=torch.full((M, N), float("nan"), device=DEV))
+                items.append(it)
+                singles.append(bl.bitlinear_forward(x, nw, it["packed_w"], scale, N, EPS))
+    with bl.Group(items) as g:
+        kinds = [d["kind"] for d in g.forward_launches()]
+        assert "quant_shared" in kinds and "decode_fused" in kinds
+        g.forward()
+        torch.cuda.synchronize()
+        for i, (it, ys) in enumerate(zip(items, singles)):
+            assert torch.equal(it["y"], ys), i
+    it = items[-2]  # M 300, K 3072, no norm
+    W = inputs.weight(24, 300, 3072 + 1, 128, 3072)
+    packed, _ = oracle.i2s_pack(W)
+    assert rel_l2(host(it["y"]), oracle.bitlinear(host(it["x"]), None, packed, 128, EPS)) <= 1e-3
+
+
+@pytest.mark.parametrize("act,M,K,N", [(bl.ACT_SILU, 1, 3072, 1024), (bl.ACT_GELU_TANH, 300, 2048, 640)])
+def test_no_norm_glu_forward(act, M, K, N):
+    gate, up, _, packed, scale = glu_inputs(act, M, K, N, seed=2)
+    y = bl.bitlinear_glu_forward(dev(gate), dev(up), act, None, dev(packed), scale, N, EPS)
+    assert rel_l2(host(y), oracle.glu_bitlinear(gate, up, act, None, packed, N, EPS)) <= 1e-3
+    xq, f = bl.bitlinear_glu_quant(dev(gate), dev(up), act, None, EPS)
+    q_ref, f_ref = oracle.glu_quant(gate, up, act, None, EPS)
+    check_codes(host(xq), q_ref, oracle.glu(gate, up, act), np.ones(K, np.float32))
+    check_factor(host(f), f_ref)
+
+
 # ---------------------------------------------------------------- FFN glue ---
 # The down projection fed by act(gate) * up ("BitNet Embeddings GGUF
 # Conversion Implementation", s4.5 FFN per-projection norms): the GPU forms

@@ -112,7 +112,8 @@ A, MIS = 0x10000, 0x10004
 
 @pytest.mark.parametrize("args,code", [
     ((0, A, A, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # null x
-    ((A, 0, A, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # null norm_w
+    ((0, 0, A, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # null x, no norm
+    ((A, 0, 0, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # no norm, null weights
     ((A, A, 0, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # null weights
     ((A, A, A, 1.0, 4, 128, 8, 1e-6, 0), bl.BL_ERR_INVALID_ARGUMENT),        # null y
     ((A, A, A, 1.0, -1, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),       # M < 0
