@@ -16,6 +16,8 @@ Pages followed (by title and section):
   * "BitNet Embeddings GGUF Conversion Implementation", s4.5 FFN per-projection
     norms (act(gate) * up feeding the down projection) and the s1 model table
     (SiLU for Qwen3, gelu_pytorch_tanh for Gemma3).
+  * "BitNet Embeddings GGUF Conversion Implementation", s3 tensor type table
+    and s6.1 "F16 Norm Weight Support" (norm weights stored as float16).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` to values fixed by
 the pages' definitions and by mathematics (hand-worked examples, closed forms,
@@ -77,6 +79,8 @@ def _load():
         lib.ref_glu.argtypes = [p, p, ctypes.c_int, i64, p]
         lib.ref_glu_quant.argtypes = [p, p, ctypes.c_int, p, i64, i64, ctypes.c_float, p, p]
         lib.ref_glu_bitlinear.argtypes = [p, p, ctypes.c_int, p, p, i64, i64, i64, ctypes.c_float, p]
+        lib.ref_half_to_float.argtypes = [p, i64, p]
+        lib.ref_half_to_float.restype = None
         for name in ("ref_i2s_pack", "ref_i2s_unpack", "ref_quant", "ref_matmul_i32",
                      "ref_bitlinear", "ref_glu", "ref_glu_quant", "ref_glu_bitlinear"):
             getattr(lib, name).restype = ctypes.c_int
@@ -123,10 +127,24 @@ def i2s_unpack(packed: np.ndarray, K: int, N: int) -> tuple[np.ndarray, float]:
     return q, float(scale[0])
 
 
+def half_to_float(h: np.ndarray) -> np.ndarray:
+    """IEEE binary16 values (a float16 array, or their uint16 bit patterns)
+    widened to float32 by the oracle's own decoder."""
+    bits = np.ascontiguousarray(np.asarray(h).view(np.uint16) if np.asarray(h).dtype == np.float16
+                                else np.asarray(h, dtype=np.uint16))
+    out = np.empty(bits.shape, dtype=np.float32)
+    _load().ref_half_to_float(_ptr(bits), bits.size, _ptr(out))
+    return out
+
+
 def _norm(norm_w):
-    """norm_w as float32 (None: no per-projection norm) and its pointer."""
+    """norm_w as float32 (None: no per-projection norm) and its pointer.  A
+    float16 norm weight is widened exactly first (its stored dtype in the
+    pages' GGUF files)."""
     if norm_w is None:
         return None, None
+    if np.asarray(norm_w).dtype == np.float16:
+        norm_w = half_to_float(norm_w)
     norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
     return norm_w, _ptr(norm_w)
 

@@ -18,6 +18,9 @@
  *   [GEMV] "gguf-gemv", sections on supported block types and "Requirements"
  *          (128-element I2_S blocks, one f32 tensor-wide scale, K a multiple of
  *          128).
+ *   [EMB s3 types, s6.1] norm weights are stored as float16 (the tensor type
+ *          table of section 3) and multiplied into the f32 activations
+ *          elementwise (section 6.1, F16 norm weight support).
  *   [EMB s4.5 FFN] the FFN per-projection norms: act(gate) * up, then the
  *          down projection's RMSNorm and norm weight, then down; the
  *          activation per model from the [EMB s1] table (SiLU for Qwen3,
@@ -48,6 +51,9 @@
  *       projection's input is the shared input itself when its norm tensor
  *       is absent) is quantized from x unnormalised: codes from max|x|,
  *       factor = max|x| / 127.
+ *   R10 A float16 norm weight is widened to its exact value (every binary16
+ *       number is exactly representable in float32 and double) and then used
+ *       as a float32 norm weight.  NaN and infinite halves decode as such.
  */
 #include <math.h>
 #include <stdint.h>
@@ -83,6 +89,22 @@ static void ref_locate(int64_t K, int64_t n, int64_t k, int64_t* byte, int* shif
 /* Absmean ternary quantization and I2_S packing [EMB s3], [INF "Quantization
  * and Encoding"]: scale = 1/mean|w|, q = round(w*scale) clamped to [-1,1],
  * code = q + 1 (-1 -> 0, 0 -> 1, +1 -> 2), then four codes per byte. */
+/* IEEE 754 binary16 -> float, from the format's definition: 1 sign bit, 5
+ * exponent bits with bias 15, 10 fraction bits; exponent 0 holds zero and the
+ * subnormals f * 2^-24, exponent 31 infinity (f = 0) or NaN. */
+void ref_half_to_float(const uint16_t* h, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) {
+        const int sign = (h[i] >> 15) & 1;
+        const int e = (h[i] >> 10) & 31;
+        const int f = h[i] & 1023;
+        double v;
+        if (e == 0) v = ldexp((double)f, -24);
+        else if (e == 31) v = f == 0 ? INFINITY : NAN;
+        else v = ldexp((double)(1024 + f), e - 25);
+        out[i] = (float)(sign ? -v : v);
+    }
+}
+
 int ref_i2s_pack(const float* w, int64_t K, int64_t N, uint8_t* out, float* scale_out) {
     if (!w || !out || K <= 0 || N <= 0 || K % BLOCK != 0) return REF_ERR_ARG;
     int64_t total = N * K;

@@ -463,3 +463,44 @@ def test_no_norm_path_equals_float64_dequantized_product():
     yi = oracle.bitlinear(xi, None, packed, N, 1e-6)
     exact = (qw.astype(np.float64) @ xi[0].astype(np.float64)) / scale
     assert np.array_equal(yi[0], exact.astype(np.float32))
+
+
+# ------------------------------------------------------- f16 norm weights ---
+# Norm weights are stored as float16 and multiplied into the f32 activations
+# ("BitNet Embeddings GGUF Conversion Implementation", s3 tensor type table,
+# s6.1 F16 norm weight support).
+
+def test_half_decoder_exhaustive_against_numpy():
+    # every one of the 65536 bit patterns against numpy's own float16 widening
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.half_to_float(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))  # -0 kept
+
+
+def test_half_decoder_landmarks():
+    cases = {0x3C00: 1.0, 0xC000: -2.0, 0x3555: 0.333251953125, 0x7BFF: 65504.0,
+             0x0400: 2.0 ** -14, 0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24, 0x0000: 0.0}
+    got = oracle.half_to_float(np.array(list(cases), dtype=np.uint16))
+    assert got.tolist() == list(cases.values())
+    assert np.signbit(oracle.half_to_float(np.array([0x8000], np.uint16))[0])
+    inf = oracle.half_to_float(np.array([0x7C00, 0xFC00, 0x7E00], np.uint16))
+    assert inf[0] == np.inf and inf[1] == -np.inf and np.isnan(inf[2])
+
+
+def test_f16_norm_weight_path_is_the_widened_f32_path():
+    M, K, N = 3, 256, 5
+    x = inputs.activations(25, 0, 0, M, K)
+    nw16 = inputs.norm_weight(25, 0, 0, K).astype(np.float16)
+    W = inputs.weight(25, 0, 0, N, K)
+    packed, _ = oracle.i2s_pack(W)
+    wide = nw16.astype(np.float32)
+    q16, f16 = oracle.quant(x, nw16, 1e-6)
+    q32, f32 = oracle.quant(x, wide, 1e-6)
+    assert np.array_equal(q16, q32) and np.array_equal(f16, f32)
+    assert np.array_equal(oracle.bitlinear(x, nw16, packed, N, 1e-6),
+                          oracle.bitlinear(x, wide, packed, N, 1e-6))
+    # the widening is not the identity on the f32 weight it came from
+    assert not np.array_equal(wide, inputs.norm_weight(25, 0, 0, K))
