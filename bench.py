@@ -153,10 +153,11 @@ def time_launches(torch, group, steps: int):
     return info, launch_ms
 
 
-def launch_bytes(kind: str, M: int, K: int, N: int, norm: bool = True) -> int:
+def launch_bytes(kind: str, M: int, K: int, N: int, norm=True) -> int:
     """Algorithmic HBM bytes of one BitLinear in a launch of the given kind
-    (norm False: a projection without a norm weight, which is not read)."""
-    nw = 4 * K if norm else 0
+    (norm False: a projection without a norm weight, which is not read;
+    "f16": a float16 norm weight)."""
+    nw = {True: 4 * K, "f16": 2 * K, False: 0}[norm]
     if kind in ("decode", "prefill"):  # packed weights, int8 codes, factor + row sum, fp32 y
         return N * K // 4 + M * K + 8 * M + 4 * M * N
     if kind == "decode_fused":   # packed weights, fp32 x and norm weight, fp32 y
@@ -234,6 +235,8 @@ def bench_decode(torch, bl, args):
     out = run(items, True)
     # the same step with projections that have no norm weight of their own
     out["no_norm"] = run([dict(it, norm_w=None) for it in items], False)
+    # and with float16 norm weights (the pages' stored dtype for norms)
+    out["f16_norm"] = run([dict(it, norm_w=it["norm_w"].half()) for it in items], "f16")
     out.update(R=R, projs=projs, weight_bytes=weight_bytes)
     return out
 
@@ -272,10 +275,14 @@ def bench_prefill(torch, bl, args):
     _, nn_ms = time_launches(torch, group, max(3, args.steps // 2))
     group.close()
     nn_quant_ms = float(sum(nn_ms[:-1]))
+    group = bl.Group([dict(it, norm_w=it["norm_w"].half()) for it in items])
+    _, h_ms = time_launches(torch, group, max(3, args.steps // 2))
+    group.close()
+    f16_quant_ms = float(sum(h_ms[:-1]))
     ops = sum(2 * w.M * p["N"] * p["K"] for p in projs)
     return dict(projs=projs, xs=xs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, ops=ops, M=w.M,
                 tops=ops / (ms * 1e-3) / 1e12, mm_tops=ops / (mm_ms * 1e-3) / 1e12,
-                no_norm_quant_ms=nn_quant_ms)
+                no_norm_quant_ms=nn_quant_ms, f16_quant_ms=f16_quant_ms)
 
 
 def bench_ffn_glue(torch, bl, args):
@@ -509,6 +516,14 @@ def main():
                          "GBps": round(d["GBps"], 1)} for d in nn["per_launch"]],
     }
     log(f"decode without norm weights: {nn['ms']:.3f} ms/step, {nn['value']:.0f} GB/s weights")
+    hf = dec["f16_norm"]
+    out["f16_norm"] = {
+        "workload": "the decode step with float16 norm weights on every projection",
+        "ms_per_step": round(hf["ms"], 5), "value": round(hf["value"], 2), "unit": "GB/s",
+        "launches_us": [{"kind": d["kind"], "K": d["K"], "us": round(d["us"], 2),
+                         "GBps": round(d["GBps"], 1)} for d in hf["per_launch"]],
+    }
+    log(f"decode with float16 norm weights: {hf['ms']:.3f} ms/step, {hf['value']:.0f} GB/s weights")
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline_decode(dec["projs"], args.cpu_seconds)
     del dec
@@ -533,6 +548,8 @@ def main():
             "stages_us": {"quant": round(pre["quant_ms"] * 1e3, 1), "matmul": round(pre["mm_ms"] * 1e3, 1)},
         }
         out["no_norm"]["prefill_quant_us"] = round(pre["no_norm_quant_ms"] * 1e3, 1)
+        out["f16_norm"]["prefill_quant_us"] = round(pre["f16_quant_ms"] * 1e3, 1)
+        log(f"prefill quant with float16 norm weights: {pre['f16_quant_ms']:.3f} ms")
         log(f"prefill quant without norm weights: {pre['no_norm_quant_ms']:.3f} ms")
         if not args.skip_cpu:
             pf["cpu_baseline"] = cpu_baseline_prefill(pre, args.cpu_seconds / 2)

@@ -169,6 +169,27 @@ bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
                                 void* stream);
 
 /*
+ * Float16 norm weights ("BitNet Embeddings GGUF Conversion Implementation",
+ * s3 tensor type table: norm weights are stored as float16; s6.1: the f32
+ * activations are multiplied by them elementwise).  The same four calls with
+ * norm_w given as K IEEE binary16 values (device, 16-byte aligned, or NULL
+ * for no norm).  Each half is widened exactly to float32 on load, so every
+ * result equals the float32 call's on the widened weights, bit for bit.
+ */
+bl_status bitlinear_forward_nwf16(const float* x, const uint16_t* norm_w, const uint8_t* packed_w,
+                                  float w_scale, int64_t M, int64_t K, int64_t N, float eps,
+                                  float* y, void* stream);
+bl_status bitlinear_quant_nwf16(const float* x, const uint16_t* norm_w, int64_t M, int64_t K,
+                                float eps, int8_t* xq, float* x_factor, void* stream);
+bl_status bitlinear_glu_quant_nwf16(const float* gate, const float* up, int32_t act,
+                                    const uint16_t* norm_w, int64_t M, int64_t K, float eps,
+                                    int8_t* xq, float* x_factor, void* stream);
+bl_status bitlinear_glu_forward_nwf16(const float* gate, const float* up, int32_t act,
+                                      const uint16_t* norm_w, const uint8_t* packed_w,
+                                      float w_scale, int64_t M, int64_t K, int64_t N, float eps,
+                                      float* y, void* stream);
+
+/*
  * Grouped execution: many independent projections (for example the seven of
  * a layer, or of many layers) run with few launches: one quantization launch
  * for all of them that need one, then the matmul stage (one decode launch per
@@ -193,12 +214,14 @@ bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
                                     share their x, one pass over x per set */
 typedef struct bl_desc {
     const float* x;          /* device [M][K] */
-    const float* norm_w;     /* device [K], or NULL: no norm */
+    const void* norm_w;      /* device [K] float32 (float16 if norm_w_f16), or NULL: no norm */
     const uint8_t* packed_w; /* device, I2_S */
     float w_scale;
     float eps;
     int64_t M, K, N;
     float* y;                /* device [M][N] */
+    int32_t norm_w_f16;      /* 0: norm_w is float32; 1: IEEE binary16; other values are
+                                BL_ERR_INVALID_ARGUMENT */
 } bl_desc;
 
 typedef struct bl_group bl_group;

@@ -39,7 +39,7 @@ LAUNCH_KINDS = {0: "decode", 1: "prefill", 2: "quant", 3: "decode_fused", 4: "qu
 class BlDesc(ctypes.Structure):
     """Mirror of ``bl_desc``."""
     _fields_ = [("x", _p), ("norm_w", _p), ("packed_w", _p), ("w_scale", _f32), ("eps", _f32),
-                ("M", _i64), ("K", _i64), ("N", _i64), ("y", _p)]
+                ("M", _i64), ("K", _i64), ("N", _i64), ("y", _p), ("norm_w_f16", _i32)]
 
 
 _SIGS = {
@@ -52,6 +52,10 @@ _SIGS = {
     "bitlinear_matmul_i32": ([_p, _p, _i64, _i64, _i64, _p, _p], _i32),
     "bitlinear_glu_quant": ([_p, _p, _i32, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
     "bitlinear_glu_forward": ([_p, _p, _i32, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
+    "bitlinear_forward_nwf16": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
+    "bitlinear_quant_nwf16": ([_p, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
+    "bitlinear_glu_quant_nwf16": ([_p, _p, _i32, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
+    "bitlinear_glu_forward_nwf16": ([_p, _p, _i32, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
     "bl_group_create": ([ctypes.POINTER(BlDesc), _i32, ctypes.POINTER(_p)], _i32),
     "bl_group_forward": ([_p, _p], _i32),
     "bl_group_quant": ([_p, _p], _i32),
@@ -146,8 +150,13 @@ def _dev(t, dtype, name: str, shape=None) -> int:
 
 
 def _norm(norm_w, K):
-    """The norm weight's pointer, or None (no per-projection norm) for None."""
-    return None if norm_w is None else _dev(norm_w, _torch().float32, "norm_w", (K,))
+    """The norm weight's pointer (None: no per-projection norm) and whether it
+    is float16 (the pages' stored dtype for norms) rather than float32."""
+    torch = _torch()
+    if norm_w is None:
+        return None, False
+    f16 = norm_w.dtype == torch.float16
+    return _dev(norm_w, torch.float16 if f16 else torch.float32, "norm_w", (K,)), f16
 
 
 def bitlinear_forward(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y=None,
@@ -157,8 +166,10 @@ def bitlinear_forward(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y
     M, K = x.shape
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    _check(_lib.bitlinear_forward(
-        _dev(x, torch.float32, "x"), _norm(norm_w, K),
+    nw, f16 = _norm(norm_w, K)
+    fn = _lib.bitlinear_forward_nwf16 if f16 else _lib.bitlinear_forward
+    _check(fn(
+        _dev(x, torch.float32, "x"), nw,
         _dev(packed_w, torch.uint8, "packed_w"), w_scale, M, K, N, eps,
         _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)), "bitlinear_forward")
     return y
@@ -172,8 +183,10 @@ def bitlinear_quant(x, norm_w, eps: float, xq=None, x_factor=None, stream=None):
         xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if x_factor is None:
         x_factor = torch.empty((M,), dtype=torch.float32, device=x.device)
-    _check(_lib.bitlinear_quant(
-        _dev(x, torch.float32, "x"), _norm(norm_w, K), M, K, eps,
+    nw, f16 = _norm(norm_w, K)
+    fn = _lib.bitlinear_quant_nwf16 if f16 else _lib.bitlinear_quant
+    _check(fn(
+        _dev(x, torch.float32, "x"), nw, M, K, eps,
         _dev(xq, torch.int8, "xq", (M, K)), _dev(x_factor, torch.float32, "x_factor", (M,)),
         _stream_handle(stream)), "bitlinear_quant")
     return xq, x_factor
@@ -195,8 +208,8 @@ class Group:
     """Many independent projections run as one launch per stage.
 
     ``items`` is a sequence of dicts with keys x, norm_w, packed_w, w_scale,
-    eps, N and y (torch tensors on the GPU where applicable; norm_w None or
-    absent: no per-projection norm).  The tensors are
+    eps, N and y (torch tensors on the GPU where applicable; norm_w float32 or
+    float16, None or absent: no per-projection norm).  The tensors are
     kept referenced for the group's lifetime.
     """
 
@@ -207,11 +220,11 @@ class Group:
         for i, it in enumerate(items):
             x, y = it["x"], it["y"]
             M, K = x.shape
-            descs[i] = BlDesc(_dev(x, torch.float32, "x"),
-                              _norm(it.get("norm_w"), K),
+            nw, f16 = _norm(it.get("norm_w"), K)
+            descs[i] = BlDesc(_dev(x, torch.float32, "x"), nw,
                               _dev(it["packed_w"], torch.uint8, "packed_w"),
                               float(it["w_scale"]), float(it["eps"]), M, K, int(it["N"]),
-                              _dev(y, torch.float32, "y", (M, int(it["N"]))))
+                              _dev(y, torch.float32, "y", (M, int(it["N"]))), int(f16))
             self._keep.append(it)
         handle = _p()
         _check(_lib.bl_group_create(descs, len(items), ctypes.byref(handle)), "bl_group_create")
@@ -321,9 +334,11 @@ def bitlinear_glu_quant(gate, up, act: int, norm_w, eps: float, xq=None, x_facto
         xq = torch.empty((M, K), dtype=torch.int8, device=gate.device)
     if x_factor is None:
         x_factor = torch.empty((M,), dtype=torch.float32, device=gate.device)
-    _check(_lib.bitlinear_glu_quant(
+    nw, f16 = _norm(norm_w, K)
+    fn = _lib.bitlinear_glu_quant_nwf16 if f16 else _lib.bitlinear_glu_quant
+    _check(fn(
         _dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up", (M, K)), act,
-        _norm(norm_w, K), M, K, eps, _dev(xq, torch.int8, "xq", (M, K)),
+        nw, M, K, eps, _dev(xq, torch.int8, "xq", (M, K)),
         _dev(x_factor, torch.float32, "x_factor", (M,)), _stream_handle(stream)),
         "bitlinear_glu_quant")
     return xq, x_factor
@@ -336,9 +351,11 @@ def bitlinear_glu_forward(gate, up, act: int, norm_w, packed_w, w_scale: float, 
     M, K = gate.shape
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=gate.device)
-    _check(_lib.bitlinear_glu_forward(
+    nw, f16 = _norm(norm_w, K)
+    fn = _lib.bitlinear_glu_forward_nwf16 if f16 else _lib.bitlinear_glu_forward
+    _check(fn(
         _dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up", (M, K)), act,
-        _norm(norm_w, K), _dev(packed_w, torch.uint8, "packed_w"),
+        nw, _dev(packed_w, torch.uint8, "packed_w"),
         w_scale, M, K, N, eps, _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)),
         "bitlinear_glu_forward")
     return y

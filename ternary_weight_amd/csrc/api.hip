@@ -37,7 +37,7 @@ bl_status check_eps(float eps) {
   return (std::isfinite(eps) && eps >= 0.0f) ? BL_OK : BL_ERR_INVALID_ARGUMENT;
 }
 
-bl_status check_forward(const float* x, const float* norm_w, const uint8_t* packed_w,
+bl_status check_forward(const float* x, const void* norm_w, const uint8_t* packed_w,
                         float w_scale, int64_t M, int64_t K, int64_t N, float eps, const float* y) {
   bl_status st = check_shape(M, K, N);
   if (st != BL_OK) return st;
@@ -146,16 +146,20 @@ const char* bl_status_string(bl_status s) {
 
 int64_t bl_k_max(void) { return kKMax; }
 
-bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* packed_w,
-                            float w_scale, int64_t M, int64_t K, int64_t N, float eps, float* y,
-                            void* stream) {
+namespace {
+
+// The calls below with a float32 or a float16 norm weight (nw_f16) share these.
+bl_status forward_impl(const float* x, const void* norm_w, bool nw_f16, const uint8_t* packed_w,
+                       float w_scale, int64_t M, int64_t K, int64_t N, float eps, float* y,
+                       void* stream) {
   try {
     bl_status st = check_forward(x, norm_w, packed_w, w_scale, M, K, N, eps, y);
     if (st != BL_OK || M == 0) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Prob p{};
     p.x = x;
-    p.norm_w = norm_w;
+    p.norm_w = static_cast<const float*>(norm_w);
+    p.nw_f16 = nw_f16 ? 1 : 0;
     p.w = packed_w;
     p.y = y;
     p.acc = nullptr;
@@ -180,8 +184,8 @@ bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* 
   }
 }
 
-bl_status bitlinear_quant(const float* x, const float* norm_w, int64_t M, int64_t K, float eps,
-                          int8_t* xq, float* x_factor, void* stream) {
+bl_status quant_impl(const float* x, const void* norm_w, bool nw_f16, int64_t M, int64_t K,
+                     float eps, int8_t* xq, float* x_factor, void* stream) {
   try {
     bl_status st = check_shape(M, K, 1);
     if (st != BL_OK) return st;
@@ -192,7 +196,8 @@ bl_status bitlinear_quant(const float* x, const float* norm_w, int64_t M, int64_
     if (M == 0) return BL_OK;
     Prob p{};
     p.x = x;
-    p.norm_w = norm_w;
+    p.norm_w = static_cast<const float*>(norm_w);
+    p.nw_f16 = nw_f16 ? 1 : 0;
     p.xq = xq;
     p.factor = x_factor;
     p.rowsum = nullptr;
@@ -206,6 +211,8 @@ bl_status bitlinear_quant(const float* x, const float* norm_w, int64_t M, int64_
     return BL_ERR_INTERNAL;
   }
 }
+
+}  // namespace
 
 bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_t M, int64_t K,
                                int64_t N, int32_t* acc, void* stream) {
@@ -235,11 +242,13 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
   }
 }
 
+namespace {
+
 // ---- FFN glue: the down projection fed by act(gate) * up ------------------
 
-bl_status bitlinear_glu_quant(const float* gate, const float* up, int32_t act, const float* norm_w,
-                              int64_t M, int64_t K, float eps, int8_t* xq, float* x_factor,
-                              void* stream) {
+bl_status glu_quant_impl(const float* gate, const float* up, int32_t act, const void* norm_w,
+                         bool nw_f16, int64_t M, int64_t K, float eps, int8_t* xq, float* x_factor,
+                         void* stream) {
   try {
     bl_status st = check_shape(M, K, 1);
     if (st != BL_OK) return st;
@@ -254,7 +263,8 @@ bl_status bitlinear_glu_quant(const float* gate, const float* up, int32_t act, c
     p.x = gate;
     p.up = up;
     p.act = act == BL_ACT_SILU ? kActSilu : kActGeluTanh;
-    p.norm_w = norm_w;
+    p.norm_w = static_cast<const float*>(norm_w);
+    p.nw_f16 = nw_f16 ? 1 : 0;
     p.xq = xq;
     p.factor = x_factor;
     p.rowsum = nullptr;
@@ -269,10 +279,9 @@ bl_status bitlinear_glu_quant(const float* gate, const float* up, int32_t act, c
   }
 }
 
-bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
-                                const float* norm_w, const uint8_t* packed_w, float w_scale,
-                                int64_t M, int64_t K, int64_t N, float eps, float* y,
-                                void* stream) {
+bl_status glu_forward_impl(const float* gate, const float* up, int32_t act, const void* norm_w,
+                           bool nw_f16, const uint8_t* packed_w, float w_scale, int64_t M,
+                           int64_t K, int64_t N, float eps, float* y, void* stream) {
   try {
     bl_status st = check_forward(gate, norm_w, packed_w, w_scale, M, K, N, eps, y);
     if (st != BL_OK) return st;
@@ -288,7 +297,8 @@ bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
     p.x = gate;
     p.up = up;
     p.act = act == BL_ACT_SILU ? kActSilu : kActGeluTanh;
-    p.norm_w = norm_w;
+    p.norm_w = static_cast<const float*>(norm_w);
+    p.nw_f16 = nw_f16 ? 1 : 0;
     p.w = packed_w;
     p.xq = reinterpret_cast<int8_t*>(ws + l.xq);
     p.factor = reinterpret_cast<float*>(ws + l.factor);
@@ -306,6 +316,49 @@ bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
   } catch (...) {
     return BL_ERR_INTERNAL;
   }
+}
+
+}  // namespace
+
+bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* packed_w,
+                            float w_scale, int64_t M, int64_t K, int64_t N, float eps, float* y,
+                            void* stream) {
+  return forward_impl(x, norm_w, false, packed_w, w_scale, M, K, N, eps, y, stream);
+}
+bl_status bitlinear_forward_nwf16(const float* x, const uint16_t* norm_w, const uint8_t* packed_w,
+                                  float w_scale, int64_t M, int64_t K, int64_t N, float eps,
+                                  float* y, void* stream) {
+  return forward_impl(x, norm_w, true, packed_w, w_scale, M, K, N, eps, y, stream);
+}
+bl_status bitlinear_quant(const float* x, const float* norm_w, int64_t M, int64_t K, float eps,
+                          int8_t* xq, float* x_factor, void* stream) {
+  return quant_impl(x, norm_w, false, M, K, eps, xq, x_factor, stream);
+}
+bl_status bitlinear_quant_nwf16(const float* x, const uint16_t* norm_w, int64_t M, int64_t K,
+                                float eps, int8_t* xq, float* x_factor, void* stream) {
+  return quant_impl(x, norm_w, true, M, K, eps, xq, x_factor, stream);
+}
+bl_status bitlinear_glu_quant(const float* gate, const float* up, int32_t act, const float* norm_w,
+                              int64_t M, int64_t K, float eps, int8_t* xq, float* x_factor,
+                              void* stream) {
+  return glu_quant_impl(gate, up, act, norm_w, false, M, K, eps, xq, x_factor, stream);
+}
+bl_status bitlinear_glu_quant_nwf16(const float* gate, const float* up, int32_t act,
+                                    const uint16_t* norm_w, int64_t M, int64_t K, float eps,
+                                    int8_t* xq, float* x_factor, void* stream) {
+  return glu_quant_impl(gate, up, act, norm_w, true, M, K, eps, xq, x_factor, stream);
+}
+bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
+                                const float* norm_w, const uint8_t* packed_w, float w_scale,
+                                int64_t M, int64_t K, int64_t N, float eps, float* y,
+                                void* stream) {
+  return glu_forward_impl(gate, up, act, norm_w, false, packed_w, w_scale, M, K, N, eps, y, stream);
+}
+bl_status bitlinear_glu_forward_nwf16(const float* gate, const float* up, int32_t act,
+                                      const uint16_t* norm_w, const uint8_t* packed_w,
+                                      float w_scale, int64_t M, int64_t K, int64_t N, float eps,
+                                      float* y, void* stream) {
+  return glu_forward_impl(gate, up, act, norm_w, true, packed_w, w_scale, M, K, N, eps, y, stream);
 }
 
 bl_status bl_release_workspace(void) {
@@ -527,6 +580,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
     for (int32_t i = 0; i < count; ++i) {
       const bl_desc& d = descs[i];
       bl_status st = check_forward(d.x, d.norm_w, d.packed_w, d.w_scale, d.M, d.K, d.N, d.eps, d.y);
+      if (st == BL_OK && d.norm_w_f16 != 0 && d.norm_w_f16 != 1) st = BL_ERR_INVALID_ARGUMENT;
       if (st != BL_OK) return st;
       if (d.M == 0) continue;
       if (d.M <= kGemvMaxM)
@@ -562,7 +616,8 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       const bool fused = d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K));
       Prob p{};
       p.x = d.x;
-      p.norm_w = d.norm_w;
+      p.norm_w = static_cast<const float*>(d.norm_w);
+      p.nw_f16 = d.norm_w_f16;
       p.w = d.packed_w;
       if (!fused) {
         const WsLayout l = ws_layout(d.M, d.K);

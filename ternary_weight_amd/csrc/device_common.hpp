@@ -12,6 +12,7 @@ constexpr int kWave = 64;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 // Raw buffer resources: word 3 for the gfx9 family, and an offset past any
 // buffer's records (loads read 0, stores are dropped, no memory access).
@@ -25,7 +26,8 @@ constexpr int kOob = 0x7FFFFFF0;
 // Workspace pointers (xq, factor, rowsum) belong to the library.
 struct Prob {
   const float* x;        // [M][K] f32 activations
-  const float* norm_w;   // [K] f32 norm weight; null: no norm (u = x, r = 1)
+  const float* norm_w;   // [K] norm weight (f32, or binary16 if nw_f16); null: no norm
+                         // (u = x, r = 1)
   const uint8_t* w;      // I2_S codes, row n at byte n*K/4
   int8_t* xq;            // [M][K] int8 codes (workspace or caller's)
   float* factor;         // [M] absmax/127 (workspace or caller's)
@@ -43,6 +45,10 @@ struct Prob {
   // FFN glue: the input row is act(x) * up (kActSilu, kActGeluTanh) instead
   // of x (kActNone).
   int act;
+  // norm_w holds K IEEE binary16 values ("BitNet Embeddings GGUF Conversion
+  // Implementation", s3 tensor types and s6.1: norms are stored as float16),
+  // widened exactly to f32 when loaded.
+  int nw_f16;
 };
 
 constexpr int kActNone = 0, kActSilu = 1, kActGeluTanh = 2;
@@ -181,6 +187,19 @@ __device__ __forceinline__ uint32_t codes4(const f4& u, float amax, int* sum) {
   *sum += a + b + c + d;
   return pack4(a, b, c, d);
 }
+// Four binary16 norm weights (one 8-byte load) widened to f32: exact.
+__device__ __forceinline__ f4 half4(u2 h) {
+  auto cv = [](uint32_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+  };
+  return f4{cv(h.x & 0xffffu), cv(h.x >> 16), cv(h.y & 0xffffu), cv(h.y >> 16)};
+}
+// Norm weight kinds of the quantization variants.
+constexpr int kNwNone = 0, kNwF32 = 1, kNwF16 = 2;
+__device__ __forceinline__ int nw_kind(const Prob& P) {
+  return P.norm_w ? (P.nw_f16 ? kNwF16 : kNwF32) : kNwNone;
+}
+
 // FFN glue ("BitNet Embeddings GGUF Conversion Implementation", s4.5 FFN
 // per-projection norms; activation per the s1 model table): the down
 // projection's input is act(gate) * up.  SiLU(z) = z / (1 + e^-z); the tanh

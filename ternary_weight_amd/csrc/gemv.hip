@@ -173,13 +173,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
       const_cast<int8_t*>(P.xq), 0, FUSED ? 0 : M * K, kBufferDword3);
   const FusedLds fl = fused_lds(M, K, NSB);
   if (FUSED) {
-    // fp32 rows and the norm weight, copied linearly (1 KB per wave
-    // instruction; bytes past either buffer read 0).
+    // fp32 rows and the norm weight (4K bytes, 2K if float16, none without
+    // one), copied linearly (1 KB per wave instruction; bytes past either
+    // buffer read 0).
+    const int nwb = P.norm_w ? K * (P.nw_f16 ? 2 : 4) : 0;
     const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(P.x), 0, M * K * 4, kBufferDword3);
     const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(P.norm_w), 0, P.norm_w ? K * 4 : 0, kBufferDword3);
-    const int ux = (M * K * 4 + 1023) >> 10, un = P.norm_w ? (K * 4 + 1023) >> 10 : 0;
+        const_cast<float*>(P.norm_w), 0, nwb, kBufferDword3);
+    const int ux = (M * K * 4 + 1023) >> 10, un = (nwb + 1023) >> 10;
     for (int i = wave; i < ux + un; i += 4) {
       const bool isx = i < ux;
       const int u = isx ? i : i - ux;
@@ -242,6 +244,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
     const f4* xf = reinterpret_cast<const f4*>(xlds + fl.x);
     const f4* nw = reinterpret_cast<const f4*>(xlds + fl.nw);
     const bool norm = P.norm_w != nullptr;  // else u = x, r = 1
+    const bool nwh = P.nw_f16 != 0;
+    // chunk c of the norm weight, widened from float16 when stored so
+    auto nwc = [&](int c) { return nwh ? half4(reinterpret_cast<const u2*>(xlds + fl.nw)[c]) : nw[c]; };
     float* row_scale = reinterpret_cast<float*>(xlds + fl.rows);
     int* row_sum = reinterpret_cast<int*>(xlds + fl.rows + 64);
     for (int m = wave; m < M; m += 4) {
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
         if (c < nch) {
           const f4 xv = xf[m * nch + c];
           ss += sq4(xv);
-          amax = fmaxf(amax, absmax4(norm ? xv * nw[c] : xv));
+          amax = fmaxf(amax, absmax4(norm ? xv * nwc(c) : xv));
         }
       }
       const double ssd = wave_sum(static_cast<double>(ss));
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
         uint32_t q = 0u;
         if (c < nch) {
           const f4 xv = xf[m * nch + c];
-          q = codes4(norm ? xv * nw[c] : xv, amax, &sum);
+          q = codes4(norm ? xv * nwc(c) : xv, amax, &sum);
         }
         *reinterpret_cast<uint32_t*>(xlds + m * kpad + ((((c >> 2) ^ (m & 7))) << 4) + ((c & 3) << 2)) = q;
       }

@@ -16,7 +16,8 @@
 // weight, an L2 hit).
 //
 // A projection without a norm weight (norm_w null) quantizes x unnormalised:
-// u = x and r = 1 (same kernels, the multiply and the rsqrt skipped).
+// u = x and r = 1 (same kernels, the multiply and the rsqrt skipped).  A
+// float16 norm weight is widened exactly on load and then used as f32.
 //
 // Projections that read the same input (q, k and v of a layer, or gate and
 // up: each normalises the shared x with its own weight, "BitNet Embeddings
@@ -37,14 +38,20 @@ __device__ __forceinline__ void finish_row(const Prob& P, int m, double ss, floa
   }
 }
 
+// Chunk c (4 elements) of the norm weight of kind NW (kNwF32 or kNwF16).
+template <int NW>
+__device__ __forceinline__ f4 nw_chunk(const Prob& P, int c) {
+  if (NW == kNwF16) return half4(gptr<u2>(reinterpret_cast<const uint16_t*>(P.norm_w))[c]);
+  return gptr<f4>(P.norm_w)[c];
+}
+
 // NC: float4 chunks per lane held in registers (K <= 256*NC).  A workgroup
 // owns kQuantRows consecutive rows of one problem, kQuantRowsPerWave per wave.
-// ACT: the row is act(x) * up (FFN glue) instead of x.  NORM: the problem has
-// a norm weight (the rows of both kinds keep their loads in one block).
-template <int NC, int ACT, bool NORM>
+// ACT: the row is act(x) * up (FFN glue) instead of x.  NW: the kind of norm
+// weight (each kind keeps its loads in one block, no per-element branch).
+template <int NC, int ACT, int NW>
 __device__ __forceinline__ void quant_reg_rows(const Prob& P, int m_begin, int lane) {
   const int nch = P.K >> 2;
-  const BL_GLOBAL f4* wr = gptr<f4>(P.norm_w);
   for (int r = 0; r < kQuantRowsPerWave; ++r) {
     const int m = m_begin + r;
     if (m >= P.M) break;
@@ -59,7 +66,7 @@ __device__ __forceinline__ void quant_reg_rows(const Prob& P, int m_begin, int l
       if (c < nch) {
         const f4 xv = ACT == kActNone ? f4(xr[c]) : glu4<ACT>(f4(xr[c]), f4(ur[c]));
         ss += sq4(xv);
-        u[i] = NORM ? xv * wr[c] : xv;
+        u[i] = NW == kNwNone ? xv : xv * nw_chunk<NW>(P, c);
         amax = fmaxf(amax, absmax4(u[i]));
       }
     }
@@ -83,10 +90,11 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
   const int pi = find_prob(set, blockIdx.x, &local);
   const Prob P = prob_at(set, pi);
   const int m_begin = local * kQuantRows + wave_id() * kQuantRowsPerWave;
-  if (P.norm_w)
-    quant_reg_rows<NC, ACT, true>(P, m_begin, lane);
-  else
-    quant_reg_rows<NC, ACT, false>(P, m_begin, lane);
+  switch (nw_kind(P)) {
+    case kNwF32: quant_reg_rows<NC, ACT, kNwF32>(P, m_begin, lane); break;
+    case kNwF16: quant_reg_rows<NC, ACT, kNwF16>(P, m_begin, lane); break;
+    default: quant_reg_rows<NC, ACT, kNwNone>(P, m_begin, lane);
+  }
 }
 
 // Share sets: the workgroup's kQuantRows rows are quantized for every problem
@@ -95,17 +103,16 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
 // waves of a workgroup read the same rows at the same time, so x comes from
 // HBM once and from L2 for the siblings; each wave's Sum(x^2) has the order
 // of the plain variant, hence the same factor.
-template <int NC, bool NORM>
+template <int NC, int NW>
 __device__ __forceinline__ void quant_shared_rows(const Prob& P, const Prob& Q, int m0, int lane) {
   constexpr int R = NC >= 16 ? 1 : (16 / NC >= kQuantRows ? kQuantRows : 16 / NC);
   const int nch = P.K >> 2;
   f4 w[NC];
-  if (NORM) {
-    const BL_GLOBAL f4* wr = gptr<f4>(Q.norm_w);
+  if (NW != kNwNone) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = lane + kWave * i;
-      w[i] = c < nch ? wr[c] : f4{0.f, 0.f, 0.f, 0.f};
+      w[i] = c < nch ? nw_chunk<NW>(Q, c) : f4{0.f, 0.f, 0.f, 0.f};
     }
   }
   for (int r0 = 0; r0 < kQuantRows; r0 += R) {
@@ -132,7 +139,7 @@ __device__ __forceinline__ void quant_shared_rows(const Prob& P, const Prob& Q, 
         u[i] = f4{0.f, 0.f, 0.f, 0.f};
         if (c < nch) {
           ss += sq4(xv[r][i]);
-          u[i] = NORM ? xv[r][i] * w[i] : xv[r][i];
+          u[i] = NW == kNwNone ? xv[r][i] : xv[r][i] * w[i];
           amax = fmaxf(amax, absmax4(u[i]));
         }
       }
@@ -160,10 +167,11 @@ __global__ __launch_bounds__(256) void quant_shared_kernel(ProbSet set) {
   const int m0 = local * kQuantRows;
   for (int p = wave_id(); p < share; p += 4) {
     const Prob Q = p == 0 ? P : prob_at(set, pi + p);
-    if (Q.norm_w)
-      quant_shared_rows<NC, true>(P, Q, m0, lane);
-    else
-      quant_shared_rows<NC, false>(P, Q, m0, lane);
+    switch (nw_kind(Q)) {
+      case kNwF32: quant_shared_rows<NC, kNwF32>(P, Q, m0, lane); break;
+      case kNwF16: quant_shared_rows<NC, kNwF16>(P, Q, m0, lane); break;
+      default: quant_shared_rows<NC, kNwNone>(P, Q, m0, lane);
+    }
   }
 }
 
@@ -196,15 +204,17 @@ __device__ __forceinline__ f4 stream_in(const Prob& P, const BL_GLOBAL f4* xr, i
 __device__ void quant_stream_row(const Prob& P, int m, int lane) {
   const int nch = P.K >> 2;
   const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m) * P.K);
-  const BL_GLOBAL f4* wr = gptr<f4>(P.norm_w);
-  const bool norm = P.norm_w != nullptr;
+  const int nw = nw_kind(P);
+  auto scaled = [&](f4 xv, int c) {
+    return nw == kNwF32 ? xv * nw_chunk<kNwF32>(P, c) : nw == kNwF16 ? xv * nw_chunk<kNwF16>(P, c) : xv;
+  };
 
   double ss = 0.0;
   float amax = 0.f;
   for (int c = lane; c < nch; c += kWave) {
     const f4 xv = stream_in(P, xr, m, c);
     ss += static_cast<double>(sq4(xv));
-    amax = fmaxf(amax, absmax4(norm ? xv * wr[c] : xv));
+    amax = fmaxf(amax, absmax4(scaled(xv, c)));
   }
   ss = wave_sum(ss);
   amax = wave_max(amax);
@@ -212,8 +222,7 @@ __device__ void quant_stream_row(const Prob& P, int m, int lane) {
   BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
   int rs = 0;
   for (int c = lane; c < nch; c += kWave) {
-    const f4 xv = stream_in(P, xr, m, c);
-    qrow[c] = codes4(norm ? xv * wr[c] : xv, amax, &rs);
+    qrow[c] = codes4(scaled(stream_in(P, xr, m, c), c), amax, &rs);
   }
   finish_row(P, m, ss, amax, rs, lane);
 }

@@ -491,6 +491,78 @@ def test_no_norm_glu_forward(act, M, K, N):
     check_factor(host(f), f_ref)
 
 
+# ------------------------------------------------------ f16 norm weights ---
+# Norm weights stored as float16 ("BitNet Embeddings GGUF Conversion
+# Implementation", s3 tensor type table, s6.1): widened exactly on load, so
+# every result equals the float32 path on the widened weights bit for bit,
+# and the oracle's float16 path within the usual criteria.
+
+F16_CASES = [(1, 1024, 3072), (4, 640, 96), (16, 3072, 96), (8, 4096, 48), (17, 2048, 640),
+             (300, 1024, 1024), (5, 8192, 130), (257, 3072, 64)]
+
+
+@pytest.mark.parametrize("M,K,N", F16_CASES)
+def test_f16_norm_weight_equals_widened_f32(M, K, N):
+    # fused decode (M*K small), unfused decode, prefill, streaming (K 8192)
+    x, nw, packed, scale = proj_inputs(26, M, K, M, K, N, heavy=True)
+    if M > 2:
+        x[M // 2] = 0.0
+    nw16 = nw.astype(np.float16)
+    dx, dp = dev(x), dev(packed)
+    d16 = torch.from_numpy(nw16).to(DEV)
+    dwide = dev(nw16.astype(np.float32))
+    y16 = bl.bitlinear_forward(dx, d16, dp, scale, N, EPS)
+    y32 = bl.bitlinear_forward(dx, dwide, dp, scale, N, EPS)
+    assert torch.equal(y16, y32)
+    q16, f16 = bl.bitlinear_quant(dx, d16, EPS)
+    q32, f32 = bl.bitlinear_quant(dx, dwide, EPS)
+    assert torch.equal(q16, q32) and torch.equal(f16, f32)
+    assert rel_l2(host(y16), oracle.bitlinear(x, nw16, packed, N, EPS)) <= 1e-3
+    q_ref, f_ref = oracle.quant(x, nw16, EPS)
+    check_codes(host(q16), q_ref, x, nw16.astype(np.float32))
+    check_factor(host(f16), f_ref)
+
+
+def test_f16_norm_weight_group_mixed_kinds():
+    # One x read by projections with float32, float16 and no norm weights, in
+    # share sets and fused decode launches: equal to separate calls.
+    items, singles = [], []
+    for M in (1, 8, 300):
+        x = dev(inputs.activations(27, M, 0, M, 1024))
+        for i, N in enumerate((256, 128, 96, 64)):
+            W = inputs.weight(27, M, i, N, 1024)
+            packed, scale = oracle.i2s_pack(W)
+            nw = inputs.norm_weight(27, M, i, 1024)
+            nw = [dev(nw), torch.from_numpy(nw.astype(np.float16)).to(DEV), None,
+                  torch.from_numpy(nw.astype(np.float16)).to(DEV)][i]
+            it = dict(x=x, norm_w=nw, packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                      y=torch.full((M, N), float("nan"), device=DEV))
+            items.append(it)
+            singles.append(bl.bitlinear_forward(x, nw, it["packed_w"], scale, N, EPS))
+    with bl.Group(items) as g:
+        kinds = [d["kind"] for d in g.forward_launches()]
+        assert "quant_shared" in kinds and "decode_fused" in kinds and "prefill" in kinds
+        g.forward()
+        torch.cuda.synchronize()
+        for i, (it, ys) in enumerate(zip(items, singles)):
+            assert torch.equal(it["y"], ys), i
+
+
+@pytest.mark.parametrize("act,M,K,N", [(bl.ACT_SILU, 1, 3072, 1024), (bl.ACT_GELU_TANH, 300, 2048, 640),
+                                       (bl.ACT_SILU, 6, 8192, 96)])
+def test_f16_norm_weight_glu(act, M, K, N):
+    gate, up, nw, packed, scale = glu_inputs(act, M, K, N, seed=3)
+    nw16 = nw.astype(np.float16)
+    dg, du, dp = dev(gate), dev(up), dev(packed)
+    d16, dwide = torch.from_numpy(nw16).to(DEV), dev(nw16.astype(np.float32))
+    y16 = bl.bitlinear_glu_forward(dg, du, act, d16, dp, scale, N, EPS)
+    assert torch.equal(y16, bl.bitlinear_glu_forward(dg, du, act, dwide, dp, scale, N, EPS))
+    q16, f16 = bl.bitlinear_glu_quant(dg, du, act, d16, EPS)
+    q32, f32 = bl.bitlinear_glu_quant(dg, du, act, dwide, EPS)
+    assert torch.equal(q16, q32) and torch.equal(f16, f32)
+    assert rel_l2(host(y16), oracle.glu_bitlinear(gate, up, act, nw16, packed, N, EPS)) <= 1e-3
+
+
 # ---------------------------------------------------------------- FFN glue ---
 # The down projection fed by act(gate) * up ("BitNet Embeddings GGUF
 # Conversion Implementation", s4.5 FFN per-projection norms): the GPU forms

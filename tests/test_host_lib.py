@@ -203,3 +203,26 @@ def test_group_validation():
     assert lib.bl_group_forward_launches(None) == -1
     assert lib.bl_group_forward_launch(None, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_group_forward_launch_info(None, 0, None, None, None) == bl.BL_ERR_INVALID_ARGUMENT
+
+
+def test_f16_norm_weight_validation():
+    # the float16 norm weight calls validate exactly as their float32 twins
+    f, q = bl.lib.bitlinear_forward_nwf16, bl.lib.bitlinear_quant_nwf16
+    gq, gf = bl.lib.bitlinear_glu_quant_nwf16, bl.lib.bitlinear_glu_forward_nwf16
+    S = bl.ACT_SILU
+    assert f(0, A, A, 1.0, 4, 128, 8, 1e-6, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert f(A, MIS, A, 1.0, 4, 128, 8, 1e-6, A, None) == bl.BL_ERR_MISALIGNED
+    assert f(A, A, A, 1.0, 4, 192, 8, 1e-6, A, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, 0, A, 1.0, 0, 128, 8, 1e-6, A, None) == bl.BL_OK          # M = 0, no norm
+    assert q(A, MIS, 4, 128, 1e-6, A, A, None) == bl.BL_ERR_MISALIGNED
+    assert q(A, A, 4, 128, -1.0, A, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert gq(A, A, 5, A, 4, 128, 1e-6, A, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert gq(A, A, S, MIS, 4, 128, 1e-6, A, A, None) == bl.BL_ERR_MISALIGNED
+    assert gf(A, A, S, MIS, A, 1.0, 4, 128, 8, 1e-6, A, None) == bl.BL_ERR_MISALIGNED
+    assert gf(A, A, S, A, A, 1.0, 0, 128, 8, 1e-6, A, None) == bl.BL_OK
+    h = ctypes.c_void_p()
+    d = (bl.BlDesc * 2)()
+    d[0] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, A, 1)
+    d[1] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, A, 2)   # unknown norm dtype
+    assert bl.lib.bl_group_create(d, 2, ctypes.byref(h)) == bl.BL_ERR_INVALID_ARGUMENT
+    assert not h.value
