@@ -237,7 +237,10 @@ typedef struct bl_group bl_group;
 bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out);
 
 /* Both stages for every descriptor, enqueued on stream (quant, then matmul).
- * Fused decode launches (they need no quantization launch) run side by side:
+ * Fused decode problems (they need no quantization launch) of up to 12
+ * superblocks ceil(K/256) run as one merged launch, units with the most
+ * superblocks first.  Fused decode launches (the merged one and one per
+ * larger superblock count) run side by side:
  * the first on stream, the others on up to three streams the group owns
  * (default priority), forked from stream and joined back into it with
  * events, so all of the forward is ordered after earlier work on stream and
@@ -256,9 +259,12 @@ bl_status bl_group_quant(bl_group* g, void* stream);
  * bl_group_forward). */
 bl_status bl_group_matmul(bl_group* g, void* stream);
 /* The matmul stage as individual launches, for callers that time or
- * interleave them: the decode problems (M <= 16) run as one launch per
- * superblock count ceil(K/256) and kind (unfused before fused), in increasing
- * superblock count, then all prefill problems (M > 16) as one launch.
+ * interleave them, in this order: the unfused decode problems (M <= 16) with
+ * more than 16 superblocks (bucket 0); the merged fused decode launch of up
+ * to 12 superblocks (kind BL_LAUNCH_DECODE_FUSED, bucket 0); then one launch
+ * per superblock count ceil(K/256) and kind (unfused before fused), in
+ * increasing superblock count; then all prefill problems (M > 16) as one
+ * launch.
  * bl_group_matmul == every launch in order.
  *   bl_group_matmul_launches: number of launches (>= 0; -1 for a NULL group).
  *   bl_group_matmul_launch_info: kind BL_LAUNCH_DECODE or

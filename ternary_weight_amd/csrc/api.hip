@@ -396,6 +396,7 @@ struct GroupStage {
   int count = 0;  // problems
   int max_m = 0, max_k = 0;
   bool fused = false;  // decode stages: stage 1 runs inside the launch
+  bool merged = false; // fused decode stage of several superblock counts (one launch)
   bool shared = false; // quantization stages: every unit heads a share set
   int chunks = 0;      // quantization stages: float4 chunks per lane (0: streaming)
 };
@@ -455,11 +456,11 @@ struct StageHost {
   std::vector<int2> units;
   std::vector<FatUnit> fat_units;
   int max_m = 0, max_k = 0;
-  void add(const Prob& p, int nunits) {
+  void add(const Prob& p, int nunits, int nsb = 0) {
     ++nprobs;
     const int idx = static_cast<int>(probs.size());
     if (fat) {
-      for (int u = 0; u < nunits; ++u) fat_units.push_back(FatUnit{p, u, 0});
+      for (int u = 0; u < nunits; ++u) fat_units.push_back(FatUnit{p, u, nsb});
     } else {
       probs.push_back(p);
       for (int u = 0; u < nunits; ++u) units.push_back(int2{idx, u});
@@ -607,7 +608,9 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
 
     std::vector<Prob> qprobs;
     StageHost hm;
-    std::map<std::pair<int, bool>, StageHost> hv;  // decode problems by (bucket, fused)
+    // Decode problems by (bucket, fused); fused ones of up to kGemvMergedMaxNsb
+    // superblocks share one merged launch, keyed (0, true).
+    std::map<std::pair<int, bool>, StageHost> hv;
     uint8_t* ws = static_cast<uint8_t*>(g->workspace);
     size_t off = 0;
     for (int32_t i = 0; i < count; ++i) {
@@ -635,13 +638,22 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       p.N = static_cast<int>(d.N);
       if (!fused) qprobs.push_back(p);
       if (p.M <= kGemvMaxM) {
-        StageHost& sh = hv[{gemv_bucket(p.K), fused}];
+        const int b = gemv_bucket(p.K);
+        const bool merge = fused && b >= 1 && b <= kGemvMergedMaxNsb;
+        StageHost& sh = hv[{merge ? 0 : b, fused}];
         sh.fat = true;
-        sh.add(p, gemv_units(p.N, gemv_bucket(p.K)));
+        sh.add(p, gemv_units(p.N, b), merge ? b : 0);
       }
       else hm.add(p, gemm_units(p.M, p.N));
     }
     std::map<QuantKey, StageHost> hqs = build_quant_stages(qprobs);
+    {
+      // Merged decode launch: units with the most superblocks first.
+      auto it = hv.find({0, true});
+      if (it != hv.end())
+        std::stable_sort(it->second.fat_units.begin(), it->second.fat_units.end(),
+                         [](const FatUnit& a, const FatUnit& b) { return a.nsb > b.nsb; });
+    }
     interleave_gemm_units(hm);
 
     // One device buffer for every table.
@@ -661,6 +673,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
     for (auto& kv : hv) {
       g->gemv[bi].first = kv.first.first;
       g->gemv[bi].second.fused = kv.first.second;
+      g->gemv[bi].second.merged = kv.first.first == 0 && kv.first.second;
       hosts.push_back(&kv.second);
       stages.push_back(&g->gemv[bi].second);
       ++bi;
@@ -774,6 +787,7 @@ bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (i < static_cast<int32_t>(g->gemv.size())) {
       const GroupStage& gs = g->gemv[i].second;
+      if (gs.merged) return from_hip(launch_gemv_merged(gs.fat, gs.total, gs.max_m, gs.max_k, s));
       GemvLaunch L{};
       L.units = gs.fat;
       L.total = gs.total;

@@ -69,7 +69,7 @@ struct ProbSet {
 struct FatUnit {
   Prob p;
   int local;
-  int pad;
+  int nsb;  // superblocks ceil(K/256) of a merged decode launch's unit (0 otherwise)
 };
 
 // Address-space qualified views.  Pointers read from a problem record are
@@ -111,7 +111,8 @@ __device__ __forceinline__ Prob prob_at(const ProbSet& s, int p) {
 }
 
 // Problem record and local unit of work unit u from a FatUnit table.
-__device__ __forceinline__ Prob fat_unit_at(const FatUnit* units, int u, int* local) {
+__device__ __forceinline__ Prob fat_unit_at(const FatUnit* units, int u, int* local,
+                                            int* nsb = nullptr) {
   static_assert(sizeof(FatUnit) % 4 == 0, "FatUnit is copied as dwords");
   FatUnit out;
   const BL_CONST uint32_t* src = (const BL_CONST uint32_t*)(units + u);
@@ -119,6 +120,7 @@ __device__ __forceinline__ Prob fat_unit_at(const FatUnit* units, int u, int* lo
 #pragma unroll
   for (int i = 0; i < static_cast<int>(sizeof(FatUnit) / 4); ++i) dst[i] = src[i];
   *local = out.local;
+  if (nsb) *nsb = out.nsb;
   return out.p;
 }
 

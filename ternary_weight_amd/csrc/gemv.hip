@@ -132,11 +132,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// NSB > 0: exactly NSB superblocks per tile.  NSB == 0: any K, streamed.
-// The launch covers the by-value problem in `single` (units == nullptr) or
-// the FatUnit table `units`.
+// One workgroup's work: `unit` of problem P.  NSB > 0: exactly NSB
+// superblocks per tile.  NSB == 0: any K, streamed.
 template <bool RAW, bool FROM_LDS, int NSB, bool FUSED>
-__global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* units) {
+__device__ __forceinline__ void gemv_body(const Prob& P, const int unit) {
   static_assert(!FUSED || (FROM_LDS && !RAW && NSB > 0), "fused: forward, staged, specialised K");
   constexpr int T = gemv_tiles(NSB);
   constexpr int D = gemv_depth(NSB);
@@ -148,8 +147,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
-  int unit = blockIdx.x;
-  const Prob P = units ? fat_unit_at(units, blockIdx.x, &unit) : single;
   const int M = P.M, K = P.K, N = P.N;
   const int rowbytes = K >> 2;
   const int nsb = NSB > 0 ? NSB : (K + 255) >> 8;
@@ -372,6 +369,35 @@ __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* u
   }
 }
 
+// The launch covers the by-value problem in `single` (units == nullptr) or
+// the FatUnit table `units`.
+template <bool RAW, bool FROM_LDS, int NSB, bool FUSED>
+__global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* units) {
+  int unit = blockIdx.x;
+  const Prob P = units ? fat_unit_at(units, blockIdx.x, &unit) : single;
+  gemv_body<RAW, FROM_LDS, NSB, FUSED>(P, unit);
+}
+
+// Fused decode units of several superblock counts (1..kGemvMergedMaxNsb) in
+// one launch: each workgroup runs the body specialised for its unit's count.
+// The table lists the units with the most superblocks first, so the longest
+// workgroups start first and the many short ones fill the end of the launch
+// instead of each bucket's last round idling the GPU.
+__global__ __launch_bounds__(256) void gemv_fused_merged_kernel(const FatUnit* units) {
+  int unit, nsb;
+  const Prob P = fat_unit_at(units, blockIdx.x, &unit, &nsb);
+  switch (nsb) {
+#define BL_MERGED_CASE(n) \
+  case n: gemv_body<false, true, n, true>(P, unit); break;
+    BL_MERGED_CASE(1) BL_MERGED_CASE(2) BL_MERGED_CASE(3) BL_MERGED_CASE(4)
+    BL_MERGED_CASE(5) BL_MERGED_CASE(6) BL_MERGED_CASE(7) BL_MERGED_CASE(8)
+    BL_MERGED_CASE(9) BL_MERGED_CASE(10) BL_MERGED_CASE(11) BL_MERGED_CASE(12)
+#undef BL_MERGED_CASE
+    default: break;
+  }
+  static_assert(kGemvMergedMaxNsb == 12, "cases above");
+}
+
 int gemv_bucket(int K) {
   const int nsb = (K + 255) >> 8;
   return nsb <= kMaxNsb ? nsb : 0;
@@ -424,6 +450,16 @@ bool gemv_fusable(int M, int K) {
   const int b = gemv_bucket(K);
   return M >= 1 && M <= kGemvMaxM && b > 0 &&
          fused_lds(M, K, b).bytes <= kGemvFusedLdsBytes;
+}
+
+hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int max_k,
+                              hipStream_t stream) {
+  if (total <= 0) return hipSuccess;
+  const int b = gemv_bucket(max_k);
+  if (b <= 0 || b > kGemvMergedMaxNsb) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemv_fused_merged_kernel, dim3(total), dim3(256),
+                     fused_lds(max_m, max_k, b).bytes, stream, units);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,

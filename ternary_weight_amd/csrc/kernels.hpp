@@ -52,6 +52,12 @@ struct GemvLaunch {
   int total;
 };
 bool gemv_fusable(int M, int K);
+// Fused decode problems of up to kGemvMergedMaxNsb superblocks in one launch
+// over a FatUnit table whose records carry each unit's superblock count
+// (FatUnit::nsb), longest first.  max_m, max_k: the largest M and K.
+constexpr int kGemvMergedMaxNsb = 12;
+hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int max_k,
+                              hipStream_t stream);
 hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,
                        bool fused, hipStream_t stream);
 // Stage 2, M > kGemvMaxM: LDS-tiled MFMA kernel.

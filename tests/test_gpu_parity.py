@@ -226,9 +226,10 @@ def test_forward_matches_hooks_bitwise(M, K):
 
 def test_group_forward_launch_kinds_and_order():
     # The forward as launches: quantization of the problems not fused (by
-    # chunk count: K 1024 -> 4, 4096 -> 16), decode launches by increasing
-    # superblock count (3 and 4 fused: their fp32 rows fit the on-chip
-    # staging; 16 not), then the prefill launch.
+    # chunk count: K 1024 -> 4, 4096 -> 16), the merged fused decode launch
+    # (3 and 4 superblocks: their fp32 rows fit the on-chip staging; bucket
+    # reported as 0), the unfused decode launch (16 superblocks), then the
+    # prefill launch.
     specs = [(1, 1024, 64), (8, 640, 40), (16, 4096, 32), (3, 1024, 48), (40, 1024, 72),
              (2, 4096, 24)]
     items, singles = [], []
@@ -240,10 +241,9 @@ def test_group_forward_launch_kinds_and_order():
         singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, N, EPS))
     with bl.Group(items) as g:
         info = g.forward_launches()
-        assert [d["kind"] for d in info] == ["quant", "quant", "decode_fused", "decode_fused", "decode",
-                                             "prefill"]
-        assert [d["bucket"] for d in info] == [4, 16, 3, 4, 16, 0]
-        assert [d["count"] for d in info] == [1, 2, 1, 2, 2, 1]
+        assert [d["kind"] for d in info] == ["quant", "quant", "decode_fused", "decode", "prefill"]
+        assert [d["bucket"] for d in info] == [4, 16, 0, 16, 0]
+        assert [d["count"] for d in info] == [1, 2, 3, 2, 1]
         for i in range(len(info)):
             g.forward_launch(i)
         torch.cuda.synchronize()
@@ -320,13 +320,14 @@ def test_group_matches_separate_calls():
         torch.cuda.synchronize()
         for it, ys in zip(items, singles):
             assert torch.equal(it["y"], ys)
-        # The matmul stage launch by launch: decode buckets (K 1024, 2048,
-        # 3072 -> 4, 8, 12 superblocks) in order, the M = 8 problem unfused
-        # (its fp32 rows exceed the on-chip staging) before the fused M = 1
-        # ones, then prefill.
+        # The matmul stage launch by launch: the fused M = 1 problems (K 1024,
+        # 2048, 3072 -> 4, 8, 12 superblocks) in one merged launch, the M = 8
+        # problem unfused (its fp32 rows exceed the on-chip staging), then
+        # prefill.
         info = g.launches()
-        assert [d["kind"] for d in info] == ["decode"] + ["decode_fused"] * 3 + ["prefill"]
-        assert [d["bucket"] for d in info[:4]] == [4, 4, 8, 12]
+        assert [d["kind"] for d in info] == ["decode_fused", "decode", "prefill"]
+        assert [d["bucket"] for d in info[:2]] == [0, 4]
+        assert info[0]["count"] == 7
         assert sum(d["count"] for d in info) == len(items)
         for it in items:
             it["y"].fill_(float("nan"))
@@ -374,13 +375,14 @@ def test_group_shared_input_quantization():
 
 
 def test_group_forward_in_cuda_graph():
-    # The group forward captured into a graph: the fused decode launches fork
-    # onto the group's own streams and join back inside the capture.  Every
-    # replay (eager work and synchronisation between replays) must reproduce
+    # The group forward captured into a graph: the fused decode launches (the
+    # merged one and a 13-superblock one, which stays separate) fork onto the
+    # group's own streams and join back inside the capture.  Every replay
+    # (eager work and synchronisation between replays) must reproduce
     # separate forward calls bit for bit.
     items, singles = [], []
     specs = [(1, 1024, 2048), (1, 2048, 1024), (1, 3072, 1024), (2, 640, 256), (8, 1024, 96),
-             (20, 1024, 160)]
+             (20, 1024, 160), (1, 3328, 520)]
     for i, (M, K, N) in enumerate(specs):
         x, nw, packed, scale = proj_inputs(19, i, 0, M, K, N)
         it = dict(x=dev(x), norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
@@ -389,7 +391,7 @@ def test_group_forward_in_cuda_graph():
         singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, N, EPS))
     with bl.Group(items) as g:
         kinds = [d["kind"] for d in g.forward_launches()]
-        assert kinds.count("decode_fused") == 4 and "quant" in kinds and "prefill" in kinds
+        assert kinds.count("decode_fused") == 2 and "quant" in kinds and "prefill" in kinds
         g.forward()  # warm-up outside the capture
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
