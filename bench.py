@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="decode layer copies (0 = enough for 1 GiB)")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-variants", action="store_true",
+                    help="skip the no-norm and float16-norm repeats (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     return ap.parse_args()
 
@@ -235,9 +237,10 @@ def bench_decode(torch, bl, args):
 
     out = run(items, True)
     # the same step with projections that have no norm weight of their own
-    out["no_norm"] = run([dict(it, norm_w=None) for it in items], False)
-    # and with float16 norm weights (the pages' stored dtype for norms)
-    out["f16_norm"] = run([dict(it, norm_w=it["norm_w"].half()) for it in items], "f16")
+    if not args.skip_variants:
+        out["no_norm"] = run([dict(it, norm_w=None) for it in items], False)
+        # and with float16 norm weights (the pages' stored dtype for norms)
+        out["f16_norm"] = run([dict(it, norm_w=it["norm_w"].half()) for it in items], "f16")
     out.update(R=R, projs=projs, weight_bytes=weight_bytes)
     return out
 
@@ -271,15 +274,17 @@ def bench_prefill(torch, bl, args):
     assert [d["kind"] for d in info][-1] == "prefill" and all(
         d["kind"].startswith("quant") for d in info[:-1]), info
     quant_ms, mm_ms = float(sum(launch_ms[:-1])), launch_ms[-1]
-    # the quantization stage for projections without a norm weight
-    group = bl.Group([dict(it, norm_w=None) for it in items])
-    _, nn_ms = time_launches(torch, group, max(3, args.steps // 2))
-    group.close()
-    nn_quant_ms = float(sum(nn_ms[:-1]))
-    group = bl.Group([dict(it, norm_w=it["norm_w"].half()) for it in items])
-    _, h_ms = time_launches(torch, group, max(3, args.steps // 2))
-    group.close()
-    f16_quant_ms = float(sum(h_ms[:-1]))
+    nn_quant_ms = f16_quant_ms = None
+    if not args.skip_variants:
+        # the quantization stage for projections without a norm weight
+        group = bl.Group([dict(it, norm_w=None) for it in items])
+        _, nn_ms = time_launches(torch, group, max(3, args.steps // 2))
+        group.close()
+        nn_quant_ms = float(sum(nn_ms[:-1]))
+        group = bl.Group([dict(it, norm_w=it["norm_w"].half()) for it in items])
+        _, h_ms = time_launches(torch, group, max(3, args.steps // 2))
+        group.close()
+        f16_quant_ms = float(sum(h_ms[:-1]))
     ops = sum(2 * w.M * p["N"] * p["K"] for p in projs)
     return dict(projs=projs, xs=xs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, ops=ops, M=w.M,
                 tops=ops / (ms * 1e-3) / 1e12, mm_tops=ops / (mm_ms * 1e-3) / 1e12,
@@ -511,22 +516,23 @@ def main():
         "measured_peaks": peaks,
     }
     out["roofline"]["frac_of_measured"] = round(dom["GBps"] / peaks["hbm_read_GBps"], 4)
-    nn = dec["no_norm"]
-    out["no_norm"] = {
-        "workload": "the decode step with norm_w NULL on every projection (no per-projection norm)",
-        "ms_per_step": round(nn["ms"], 5), "value": round(nn["value"], 2), "unit": "GB/s",
-        "launches_us": [{"kind": d["kind"], "K": d["K"], "us": round(d["us"], 2),
-                         "GBps": round(d["GBps"], 1)} for d in nn["per_launch"]],
-    }
-    log(f"decode without norm weights: {nn['ms']:.3f} ms/step, {nn['value']:.0f} GB/s weights")
-    hf = dec["f16_norm"]
-    out["f16_norm"] = {
-        "workload": "the decode step with float16 norm weights on every projection",
-        "ms_per_step": round(hf["ms"], 5), "value": round(hf["value"], 2), "unit": "GB/s",
-        "launches_us": [{"kind": d["kind"], "K": d["K"], "us": round(d["us"], 2),
-                         "GBps": round(d["GBps"], 1)} for d in hf["per_launch"]],
-    }
-    log(f"decode with float16 norm weights: {hf['ms']:.3f} ms/step, {hf['value']:.0f} GB/s weights")
+    if not args.skip_variants:
+        nn = dec["no_norm"]
+        out["no_norm"] = {
+            "workload": "the decode step with norm_w NULL on every projection (no per-projection norm)",
+            "ms_per_step": round(nn["ms"], 5), "value": round(nn["value"], 2), "unit": "GB/s",
+            "launches_us": [{"kind": d["kind"], "K": d["K"], "us": round(d["us"], 2),
+                             "GBps": round(d["GBps"], 1)} for d in nn["per_launch"]],
+        }
+        log(f"decode without norm weights: {nn['ms']:.3f} ms/step, {nn['value']:.0f} GB/s weights")
+        hf = dec["f16_norm"]
+        out["f16_norm"] = {
+            "workload": "the decode step with float16 norm weights on every projection",
+            "ms_per_step": round(hf["ms"], 5), "value": round(hf["value"], 2), "unit": "GB/s",
+            "launches_us": [{"kind": d["kind"], "K": d["K"], "us": round(d["us"], 2),
+                             "GBps": round(d["GBps"], 1)} for d in hf["per_launch"]],
+        }
+        log(f"decode with float16 norm weights: {hf['ms']:.3f} ms/step, {hf['value']:.0f} GB/s weights")
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline_decode(dec["projs"], args.cpu_seconds)
     del dec
@@ -550,10 +556,11 @@ def main():
             },
             "stages_us": {"quant": round(pre["quant_ms"] * 1e3, 1), "matmul": round(pre["mm_ms"] * 1e3, 1)},
         }
-        out["no_norm"]["prefill_quant_us"] = round(pre["no_norm_quant_ms"] * 1e3, 1)
-        out["f16_norm"]["prefill_quant_us"] = round(pre["f16_quant_ms"] * 1e3, 1)
-        log(f"prefill quant with float16 norm weights: {pre['f16_quant_ms']:.3f} ms")
-        log(f"prefill quant without norm weights: {pre['no_norm_quant_ms']:.3f} ms")
+        if not args.skip_variants:
+            out["no_norm"]["prefill_quant_us"] = round(pre["no_norm_quant_ms"] * 1e3, 1)
+            out["f16_norm"]["prefill_quant_us"] = round(pre["f16_quant_ms"] * 1e3, 1)
+            log(f"prefill quant with float16 norm weights: {pre['f16_quant_ms']:.3f} ms")
+            log(f"prefill quant without norm weights: {pre['no_norm_quant_ms']:.3f} ms")
         if not args.skip_cpu:
             pf["cpu_baseline"] = cpu_baseline_prefill(pre, args.cpu_seconds / 2)
         out["prefill"] = pf
