@@ -449,6 +449,34 @@ void free_group(bl_group* g) {
   delete g;
 }
 
+// Unit order of the merged decode launch.  Units with the most superblocks
+// go first (the longest workgroups start first, the short ones fill the
+// end).  Consecutive workgroups are dealt to the XCDs in turn, each with its
+// own L2, so the units of one problem are dealt to one XCD: its workgroups
+// after the first then find the problem's x and norm weight in that L2.
+// Whole problems go to the XCD with the fewest units so far.
+void order_merged_units(std::vector<FatUnit>& units) {
+  constexpr int kXcd = 8;
+  std::stable_sort(units.begin(), units.end(),
+                   [](const FatUnit& a, const FatUnit& b) { return a.nsb > b.nsb; });
+  std::vector<std::vector<FatUnit>> per_xcd(kXcd);
+  for (size_t i = 0; i < units.size();) {
+    size_t j = i + 1;
+    while (j < units.size() && units[j].p.w == units[i].p.w && units[j].p.y == units[i].p.y) ++j;
+    size_t x = 0;
+    for (size_t k = 1; k < per_xcd.size(); ++k)
+      if (per_xcd[k].size() < per_xcd[x].size()) x = k;
+    per_xcd[x].insert(per_xcd[x].end(), units.begin() + i, units.begin() + j);
+    i = j;
+  }
+  std::vector<FatUnit> out;
+  out.reserve(units.size());
+  for (size_t k = 0; out.size() < units.size(); ++k)
+    for (const auto& l : per_xcd)
+      if (k < l.size()) out.push_back(l[k]);
+  units.swap(out);
+}
+
 // Host image of one stage before upload.
 struct StageHost {
   bool fat = false;
@@ -648,11 +676,8 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
     }
     std::map<QuantKey, StageHost> hqs = build_quant_stages(qprobs);
     {
-      // Merged decode launch: units with the most superblocks first.
       auto it = hv.find({0, true});
-      if (it != hv.end())
-        std::stable_sort(it->second.fat_units.begin(), it->second.fat_units.end(),
-                         [](const FatUnit& a, const FatUnit& b) { return a.nsb > b.nsb; });
+      if (it != hv.end()) order_merged_units(it->second.fat_units);
     }
     interleave_gemm_units(hm);
 
