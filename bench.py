@@ -116,22 +116,29 @@ def time_steps(torch, group, steps: int, warmup: int):
     A step is one bl_group_forward on the current stream (the fused decode
     launches run side by side on the group's own streams, forked from and
     joined back into this one).  The timed region is bracketed by
-    synchronisations; returns the wall-clock ms per step and the mean of HIP
-    events around each step.
+    synchronisations and holds nothing but the steps: a timing event recorded
+    between two steps makes the second kernel wait for the first one's
+    completion signal and costs several microseconds per step.  A second,
+    untimed-by-wall pass records one pair of HIP events around the same
+    number of steps as a device-side cross-check.  Returns the wall-clock ms
+    per step and the events' ms per step.
     """
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         group.forward()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    for _ in range(steps):
         group.forward()
-        b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        group.forward()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return wall * 1e3 / steps, a.elapsed_time(b) / steps
 
 
 def time_launches(torch, group, steps: int):

@@ -349,8 +349,31 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit) {
       if (t > 0) finish(t - 1);
     }
     finish(T - 1);
+    // Fused: the fp32 rows and the norm weight are dead since the
+    // quantization barrier, so the workgroup's results are gathered there
+    // (row m of the workgroup's 64*T output columns at m*64*T) and written
+    // as whole 16-byte chunks by consecutive lanes: at M = 1 two full-wave
+    // stores instead of one four-lane store per tile and wave.
+    const int span = 64 * T;
+    if (FUSED && M * span * 4 <= fl.bytes - fl.x) {
+      int32_t* ol = reinterpret_cast<int32_t*>(xlds + fl.x);
+      if (r16 < M) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) gemv_store<RAW>(P, res[t], tile0 + 64 * t + 4 * g, r16);
+        for (int t = 0; t < T; ++t)
+          *reinterpret_cast<v4i*>(ol + r16 * span + 64 * t + 16 * wave + 4 * g) = res[t];
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int base = unit * span;
+      for (int c = threadIdx.x; c < M * (span / 4); c += 256) {
+        const int m = c / (span / 4), j = c - m * (span / 4);
+        gemv_store<RAW>(P, *reinterpret_cast<const v4i*>(ol + m * span + 4 * j), base + 4 * j, m);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < T; ++t) gemv_store<RAW>(P, res[t], tile0 + 64 * t + 4 * g, r16);
+    }
   } else {
     // Generic K, one tile: two superblocks in flight, pairs processed
     // unconditionally (past nsb both operands are zero: loads read 0,
