@@ -345,6 +345,38 @@ def bench_ffn_glue(torch, bl, args):
     }
 
 
+def bench_device_pack(torch, bl, args):
+    """i2s_pack_device on a [16384, 4096] float32 weight (268 MB, beyond the
+    MALL): absmean reduction + packing against the HBM roofline.  Algorithmic
+    bytes: the weights read twice (reduction, packing) and the codes written
+    once, 8.25 bytes per weight."""
+    N, K = 16384, 4096
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(20)
+    w = torch.randn((N, K), generator=g, device=dev) * 0.02
+    packed = torch.empty((bl.i2s_packed_bytes(K, N),), dtype=torch.uint8, device=dev)
+    reps = max(3, args.steps // 5)
+    for _ in range(max(1, args.warmup // 10)):
+        bl.i2s_pack_device(w, packed, read_scale=False)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        bl.i2s_pack_device(w, packed, read_scale=False)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = 8 * N * K + N * K // 4 + 4
+    return {"workload": f"device-side absmean + I2_S packing of a [{N}, {K}] float32 weight",
+            "us": round(ms * 1e3, 1),
+            "roofline": {"bound": "hbm", "kernels": "absmean_partial_kernel + absmean_final_kernel + "
+                         "i2s_pack_kernel", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_call": nbytes}}
+
+
 def measure_peaks(torch, bl):
     """Sustained HBM read / copy bandwidth and int8 MFMA rate of this GPU (probes)."""
     dev = torch.device("cuda")
@@ -579,6 +611,9 @@ def main():
         log(f"ffn glue: glue+quant {glue['glue_quant_us']:.1f} us ({glue['roofline']['achieved']:.0f} GB/s), "
             f"glue-fed down forward {glue['forward_ms']:.3f} ms ({glue['forward_TOPS']:.0f} TOPS)")
         out["ffn_glue"] = glue
+    dp = bench_device_pack(torch, bl, args)
+    log(f"device pack: {dp['us']:.1f} us ({dp['roofline']['achieved']:.0f} GB/s)")
+    out["device_pack"] = dp
     print(json.dumps(out), flush=True)
 
 

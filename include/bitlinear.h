@@ -90,6 +90,31 @@ bl_status i2s_pack(const float* w, int64_t K, int64_t N, uint8_t* packed, size_t
                    float* w_scale_out);
 
 /*
+ * i2s_pack_device — the same absmean ternary quantization and I2_S packing on
+ * the GPU, for weights already in device memory (same pages and sections as
+ * i2s_pack).
+ *   w            device, [N][K] float32, 16-byte aligned.
+ *   packed       device output, at least i2s_packed_bytes(K, N) bytes, 16-byte
+ *                aligned; fully written (codes, then the scale).
+ *   packed_bytes size of the packed buffer.
+ *   w_scale_out  host output, or NULL.  Given: the call waits for the stream,
+ *                reads the scale back and returns BL_ERR_NONFINITE if it is
+ *                not finite (an inf or NaN in w; packed is then unspecified).
+ *                NULL: the call only enqueues work and checks nothing on the
+ *                device side.
+ *   stream       hipStream_t (NULL: the default stream).
+ * Codes and byte layout are those of i2s_pack.  The mean is accumulated in
+ * double in a fixed parallel order (the same on every run) instead of memory
+ * order, so the float32 scale equals i2s_pack's unless 1/mean lies within the
+ * two sums' rounding difference of a float32 rounding boundary.  Scratch (8 KB)
+ * comes from the library workspace of (device, stream); growing it is refused
+ * during graph capture (BL_ERR_UNSUPPORTED).
+ * Errors: as i2s_pack, plus BL_ERR_MISALIGNED and BL_ERR_HIP.
+ */
+bl_status i2s_pack_device(const float* w, int64_t K, int64_t N, uint8_t* packed,
+                          size_t packed_bytes, float* w_scale_out, void* stream);
+
+/*
  * bitlinear_forward — the whole path for one projection on the GPU
  * ("BitNet Embeddings GGUF Conversion Implementation", s1 and s4.5;
  * "BitNet Inference Framework", "Quantization (W1.58A8)").

@@ -47,6 +47,7 @@ _SIGS = {
     "bl_k_max": ([], _i64),
     "i2s_packed_bytes": ([_i64, _i64], ctypes.c_size_t),
     "i2s_pack": ([_p, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
+    "i2s_pack_device": ([_p, _i64, _i64, _p, ctypes.c_size_t, _p, _p], _i32),
     "bitlinear_forward": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
     "bitlinear_quant": ([_p, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
     "bitlinear_matmul_i32": ([_p, _p, _i64, _i64, _i64, _p, _p], _i32),
@@ -157,6 +158,24 @@ def _norm(norm_w, K):
         return None, False
     f16 = norm_w.dtype == torch.float16
     return _dev(norm_w, torch.float16 if f16 else torch.float32, "norm_w", (K,)), f16
+
+
+def i2s_pack_device(w, packed=None, read_scale: bool = True, stream=None):
+    """Device packing: float32 [N, K] GPU tensor -> (uint8 I2_S GPU tensor,
+    scale).  read_scale False only enqueues the work (the scale is then None;
+    it is the buffer's last four bytes)."""
+    torch = _torch()
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    N, K = w.shape
+    nbytes = i2s_packed_bytes(K, N)
+    if packed is None:
+        packed = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=w.device)
+    scale = ctypes.c_float(0.0)
+    _check(_lib.i2s_pack_device(
+        _dev(w, torch.float32, "w"), K, N, _dev(packed, torch.uint8, "packed"), packed.numel(),
+        ctypes.byref(scale) if read_scale else None, _stream_handle(stream)), "i2s_pack_device")
+    return packed, (float(scale.value) if read_scale else None)
 
 
 def bitlinear_forward(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y=None,

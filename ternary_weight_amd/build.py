@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "api.hip", "probe.hip"]
+HIP_SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "pack_device.hip", "api.hip", "probe.hip"]
 CXX_SOURCES = ["pack.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result"]

@@ -330,6 +330,37 @@ bl_status bitlinear_forward_nwf16(const float* x, const uint16_t* norm_w, const 
                                   float* y, void* stream) {
   return forward_impl(x, norm_w, true, packed_w, w_scale, M, K, N, eps, y, stream);
 }
+bl_status i2s_pack_device(const float* w, int64_t K, int64_t N, uint8_t* packed,
+                          size_t packed_bytes, float* w_scale_out, void* stream) {
+  try {
+    if (!w || !packed || K <= 0 || N <= 0) return BL_ERR_INVALID_ARGUMENT;
+    if (K % 128 != 0) return BL_ERR_UNSUPPORTED;
+    const size_t need = i2s_packed_bytes(K, N);
+    if (need == 0 || N > INT64_MAX / 64 / K) return BL_ERR_UNSUPPORTED;
+    if (packed_bytes < need) return BL_ERR_INVALID_ARGUMENT;
+    if (!aligned16(w) || !aligned16(packed)) return BL_ERR_MISALIGNED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = nullptr;
+    bl_status st = acquire_ws(s, kPackPartials * sizeof(double) + kAlign, &ws);
+    if (st != BL_OK) return st;
+    float* scale_dev = reinterpret_cast<float*>(ws + kPackPartials * sizeof(double));
+    if ((st = from_hip(launch_i2s_pack_device(w, K, N, packed, reinterpret_cast<double*>(ws),
+                                              scale_dev, s))) != BL_OK)
+      return st;
+    if (w_scale_out) {
+      float scale = 0.0f;
+      if (hipMemcpyAsync(&scale, scale_dev, sizeof(float), hipMemcpyDeviceToHost, s) != hipSuccess ||
+          hipStreamSynchronize(s) != hipSuccess)
+        return BL_ERR_HIP;
+      if (!std::isfinite(scale)) return BL_ERR_NONFINITE;
+      *w_scale_out = scale;
+    }
+    return BL_OK;
+  } catch (...) {
+    return BL_ERR_INTERNAL;
+  }
+}
+
 bl_status bitlinear_quant(const float* x, const float* norm_w, int64_t M, int64_t K, float eps,
                           int8_t* xq, float* x_factor, void* stream) {
   return quant_impl(x, norm_w, false, M, K, eps, xq, x_factor, stream);

@@ -60,6 +60,13 @@ hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int ma
                               hipStream_t stream);
 hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,
                        bool fused, hipStream_t stream);
+// Device-side absmean ternary quantization and I2_S packing of w (device,
+// [N][K] float32, 16-byte aligned) into packed (device, N*K/4 + 4 bytes):
+// codes, then the scale.  partial: kPackPartials doubles of scratch;
+// scale_dev: one float, receives the scale as well.
+constexpr int kPackPartials = 1024;
+hipError_t launch_i2s_pack_device(const float* w, int64_t K, int64_t N, uint8_t* packed,
+                                  double* partial, float* scale_dev, hipStream_t stream);
 // Stage 2, M > kGemvMaxM: LDS-tiled MFMA kernel.
 hipError_t launch_gemm(const ProbSet& set, bool raw, hipStream_t stream);
 

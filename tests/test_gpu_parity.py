@@ -697,3 +697,78 @@ def test_workload5_full_size_sampled_rows():
         log(f"workload 5 {name}: {flips} flips in {q_ref.size} sampled codes")
     worst = _sampled_check(5, 16, items, refs)
     log(f"workload 5: worst rel L2 {worst:.2e}")
+
+
+# ------------------------------------------------------- device-side packing ---
+# i2s_pack_device against the oracle's packing: the same bytes and the same
+# float32 scale (the byte layout is pinned in the oracle's own tests).
+
+def _pack_dev_check(W, tag):
+    packed, scale = bl.i2s_pack_device(dev(W))
+    p_ref, s_ref = oracle.i2s_pack(W)
+    assert scale == s_ref, f"{tag}: scale {scale} vs {s_ref}"
+    assert np.array_equal(host(packed), p_ref), f"{tag}: bytes differ"
+    return packed, scale
+
+
+def test_pack_device_worked_examples():
+    pat = np.array([0.5, -0.5, 0.125, -0.125, 0.375, -0.0625, 0.1875, -0.125], np.float32)
+    W = np.stack([np.tile(pat, 16), -np.tile(pat, 16)])
+    packed, scale = _pack_dev_check(W, "W1")
+    assert scale == 4.0 and host(packed)[:8].tolist() == [0xAA, 0x00, 0x55, 0x55, 0xAA, 0x55, 0xAA, 0x55]
+    # one-hot rows at every position of a block: mean|W| = 1/128, scale 128
+    _pack_dev_check(np.eye(128, dtype=np.float32), "one-hot family")
+    _pack_dev_check(np.zeros((3, 256), np.float32), "all zero")
+
+
+SHAPES_DEV = sorted({(N, K) for w in inputs.WORKLOADS.values() for (_, K, N) in w.projs})
+
+
+@pytest.mark.parametrize("N,K", SHAPES_DEV)
+def test_pack_device_workload_shapes(N, K):
+    _pack_dev_check(inputs.weight(8, 0, K + N, N, K), f"N={N} K={K}")
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 8192), (7, 384), (4099, 256), (3072, 3072)])
+def test_pack_device_ragged_and_large(N, K):
+    W = inputs.weight(8, 2, N, N, K)
+    W[::5, ::3] = 0.0
+    _pack_dev_check(W, f"N={N} K={K}")
+
+
+def test_pack_device_ties_and_determinism():
+    ties = np.tile(np.array([0.5, -0.5, 1.5, -1.5, 2.5, 0.25, -0.25, 1.0], np.float32), 16)
+    _pack_dev_check(np.stack([ties, ties * 2, -ties]), "ties")
+    W = dev(inputs.weight(8, 3, 0, 1024, 1280))
+    a, sa = bl.i2s_pack_device(W)
+    b, sb = bl.i2s_pack_device(W)
+    assert sa == sb and torch.equal(a, b)
+
+
+def test_pack_device_async_tail_and_nonfinite():
+    W = inputs.weight(8, 4, 0, 256, 1024)
+    packed, scale = bl.i2s_pack_device(dev(W), read_scale=False)
+    assert scale is None
+    p_ref, s_ref = oracle.i2s_pack(W)
+    got = host(packed)
+    assert np.array_equal(got, p_ref)
+    assert got[-4:].view(np.float32)[0] == s_ref
+    for bad in (np.nan, np.inf, -np.inf):
+        Wb = W.copy()
+        Wb[17, 5] = bad
+        with pytest.raises(bl.BitLinearError) as e:
+            bl.i2s_pack_device(dev(Wb))
+        assert e.value.status == bl.BL_ERR_NONFINITE
+
+
+def test_forward_with_device_packed_weights():
+    M, K, N = 300, 1024, 640
+    W = inputs.weight(8, 5, 0, N, K)
+    x = inputs.activations(8, 5, 0, M, K)
+    nw = inputs.norm_weight(8, 5, 0, K)
+    pd, sd = bl.i2s_pack_device(dev(W))
+    ph, sh = oracle.i2s_pack(W)
+    y_d = host(bl.bitlinear_forward(dev(x), dev(nw), pd, sd, N, EPS))
+    y_h = host(bl.bitlinear_forward(dev(x), dev(nw), dev(ph), sh, N, EPS))
+    assert np.array_equal(y_d, y_h)
+    assert rel_l2(y_d, oracle.bitlinear(x, nw, ph, N, EPS)) <= 1e-3

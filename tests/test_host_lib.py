@@ -110,6 +110,20 @@ def test_pack_errors():
 A, MIS = 0x10000, 0x10004
 
 
+def test_pack_device_argument_errors():
+    """i2s_pack_device rejects bad arguments before any HIP call."""
+    lib = bl.lib
+    nb = bl.i2s_packed_bytes(128, 2)
+    assert lib.i2s_pack_device(None, 128, 2, A, nb, None, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.i2s_pack_device(A, 128, 2, None, nb, None, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.i2s_pack_device(A, 128, 0, A, nb, None, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.i2s_pack_device(A, 0, 2, A, nb, None, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.i2s_pack_device(A, 100, 2, A, nb, None, None) == bl.BL_ERR_UNSUPPORTED
+    assert lib.i2s_pack_device(A, 128, 2, A, nb - 1, None, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.i2s_pack_device(MIS, 128, 2, A, nb, None, None) == bl.BL_ERR_MISALIGNED
+    assert lib.i2s_pack_device(A, 128, 2, MIS, nb, None, None) == bl.BL_ERR_MISALIGNED
+
+
 @pytest.mark.parametrize("args,code", [
     ((0, A, A, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # null x
     ((0, 0, A, 1.0, 4, 128, 8, 1e-6, A), bl.BL_ERR_INVALID_ARGUMENT),        # null x, no norm
