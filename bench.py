@@ -57,7 +57,9 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    # 500 decode steps (about 0.1 s): with 100 the fixed cost of starting and
+    # draining the timed region moved the wall-clock step by up to 3%.
+    ap.add_argument("--steps", type=int, default=500)
     # A short warmup leaves the first timed steps slow (the decode step then
     # measured 0.229 ms against 0.204 ms later in the same process).
     ap.add_argument("--warmup", type=int, default=100)
@@ -254,6 +256,12 @@ def bench_decode(torch, bl, args):
     return out
 
 
+def prefill_steps(args) -> int:
+    """Steps of the prefill-sized measurements (13 ms each): half the decode
+    steps, between 3 and 50."""
+    return max(3, min(50, args.steps // 2))
+
+
 def bench_prefill(torch, bl, args):
     w = inputs.WORKLOADS[4]
     t0 = time.time()
@@ -277,8 +285,8 @@ def bench_prefill(torch, bl, args):
                           eps=inputs.EPS, N=p["N"],
                           y=torch.empty((w.M, p["N"]), dtype=torch.float32, device=dev)))
     group = bl.Group(items)
-    ms, _ = time_steps(torch, group, max(3, args.steps // 2), max(1, args.warmup // 2))
-    info, launch_ms = time_launches(torch, group, max(3, args.steps // 2))
+    ms, _ = time_steps(torch, group, prefill_steps(args), max(1, args.warmup // 2))
+    info, launch_ms = time_launches(torch, group, prefill_steps(args))
     group.close()
     assert [d["kind"] for d in info][-1] == "prefill" and all(
         d["kind"].startswith("quant") for d in info[:-1]), info
@@ -287,11 +295,11 @@ def bench_prefill(torch, bl, args):
     if not args.skip_variants:
         # the quantization stage for projections without a norm weight
         group = bl.Group([dict(it, norm_w=None) for it in items])
-        _, nn_ms = time_launches(torch, group, max(3, args.steps // 2))
+        _, nn_ms = time_launches(torch, group, prefill_steps(args))
         group.close()
         nn_quant_ms = float(sum(nn_ms[:-1]))
         group = bl.Group([dict(it, norm_w=it["norm_w"].half()) for it in items])
-        _, h_ms = time_launches(torch, group, max(3, args.steps // 2))
+        _, h_ms = time_launches(torch, group, prefill_steps(args))
         group.close()
         f16_quant_ms = float(sum(h_ms[:-1]))
     ops = sum(2 * w.M * p["N"] * p["K"] for p in projs)
@@ -327,7 +335,7 @@ def bench_ffn_glue(torch, bl, args):
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
-    reps = max(3, args.steps // 2)
+    reps = prefill_steps(args)
     q_ms = timed(lambda: bl.bitlinear_glu_quant(gate, up, bl.ACT_SILU, nw, inputs.EPS, xq=xq, x_factor=f), reps)
     fwd_ms = timed(lambda: bl.bitlinear_glu_forward(gate, up, bl.ACT_SILU, nw, pw, scale, N, inputs.EPS, y=y), reps)
     q_bytes = 8 * M * K + M * K + 8 * M + 4 * K     # gate + up in, codes + factor + row sum out
@@ -587,6 +595,7 @@ def main():
             "workload": "prefill M=16384 through the 28-layer Qwen3-0.6B projection stack (196 BitLinears)",
             "value": round(pre["tops"], 2), "unit": "TOPS (int8-equivalent)",
             "ms_per_step": round(pre["ms"], 4),
+            "steps": prefill_steps(args),
             "roofline": {
                 "bound": "mfma", "kernel": "gemm_kernel (prefill, M>16)",
                 "achieved": round(pre["mm_tops"], 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
