@@ -296,6 +296,26 @@ def bench_prefill(torch, bl, args):
     assert [d["kind"] for d in info][-1] == "prefill" and all(
         d["kind"].startswith("quant") for d in info[:-1]), info
     quant_ms, mm_ms = float(sum(launch_ms[:-1])), launch_ms[-1]
+    # Algorithmic bytes of each quantization launch: a share set (projections
+    # reading one x) reads x once and writes each member's codes, factor and
+    # row sum; the launch of a set of P members at K reads 4MK + 4PK (norm
+    # weights) and writes P(MK + 8M).  Sets go to launches by chunk count
+    # (K = 1024: 4, 2048: 8, 3072: 12) and by sharing.
+    sets = {}
+    for p in projs:
+        sets.setdefault(p["xkey"], []).append(p)
+    qbytes = {}
+    for members in sets.values():
+        K = members[0]["K"]
+        key = ("quant_shared" if len(members) > 1 else "quant", (K + 255) // 256)
+        P = len(members)
+        qbytes[key] = qbytes.get(key, 0) + 4 * w.M * K + 4 * P * K + P * (w.M * K + 8 * w.M)
+    quant_launches = []
+    for d, t in zip(info[:-1], launch_ms[:-1]):
+        nb = qbytes.get((d["kind"], d["bucket"]))
+        quant_launches.append(dict(kind=d["kind"], chunks=d["bucket"], bitlinears=d["count"],
+                                   us=round(t * 1e3, 1), bytes=nb,
+                                   GBps=round(nb / (t * 1e-3) / 1e9, 1) if nb else None))
     nn_quant_ms = f16_quant_ms = None
     if not args.skip_variants:
         # the quantization stage for projections without a norm weight
@@ -309,6 +329,7 @@ def bench_prefill(torch, bl, args):
         f16_quant_ms = float(sum(h_ms[:-1]))
     ops = sum(2 * w.M * p["N"] * p["K"] for p in projs)
     return dict(projs=projs, xs=xs, ms=ms, quant_ms=quant_ms, mm_ms=mm_ms, ops=ops, M=w.M,
+                quant_launches=quant_launches,
                 tops=ops / (ms * 1e-3) / 1e12, mm_tops=ops / (mm_ms * 1e-3) / 1e12,
                 no_norm_quant_ms=nn_quant_ms, f16_quant_ms=f16_quant_ms)
 
@@ -596,6 +617,9 @@ def main():
         pre = bench_prefill(torch, bl, args)
         log(f"prefill: {pre['ms']:.3f} ms/step, {pre['tops']:.1f} TOPS; MFMA kernel "
             f"{pre['mm_ms']:.3f} ms ({pre['mm_tops']:.1f} TOPS), quant {pre['quant_ms']:.3f} ms")
+        log("prefill quant launches: " + "; ".join(
+            f"{q['kind']} chunks={q['chunks']} x{q['bitlinears']}: {q['us']:.0f} us {q['GBps']} GB/s"
+            for q in pre["quant_launches"]))
         pf = {
             "workload": "prefill M=16384 through the 28-layer Qwen3-0.6B projection stack (196 BitLinears)",
             "value": round(pre["tops"], 2), "unit": "TOPS (int8-equivalent)",
@@ -611,6 +635,7 @@ def main():
                 "frac_of_measured": round(pre["mm_tops"] / peaks["mfma_i8_TOPS"], 4),
             },
             "stages_us": {"quant": round(pre["quant_ms"] * 1e3, 1), "matmul": round(pre["mm_ms"] * 1e3, 1)},
+            "quant_launches": pre["quant_launches"],
         }
         if not args.skip_variants:
             out["no_norm"]["prefill_quant_us"] = round(pre["no_norm_quant_ms"] * 1e3, 1)

@@ -561,10 +561,23 @@ std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs)
     }
     sets[found].push_back(static_cast<int>(i));
   }
-  std::map<QuantKey, StageHost> out;
+  // Sets larger than the register-resident share kernel holds are split
+  // (each part reads x once).
+  std::vector<std::vector<int>> parts;
   for (const auto& set : sets) {
+    const size_t cap = static_cast<size_t>(quant_set_max(quant_chunks(probs[set[0]].K)));
+    if (cap == 0 || set.size() <= cap) {
+      parts.push_back(set);
+      continue;
+    }
+    for (size_t b = 0; b < set.size(); b += cap)
+      parts.emplace_back(set.begin() + b, set.begin() + std::min(set.size(), b + cap));
+  }
+  std::map<QuantKey, StageHost> out;
+  for (const auto& set : parts) {
     const Prob& lead = probs[set[0]];
-    StageHost& h = out[QuantKey{quant_chunks(lead.K), set.size() > 1}];
+    const int nc = quant_chunks(lead.K);
+    StageHost& h = out[QuantKey{nc, set.size() > 1}];
     const int first = static_cast<int>(h.probs.size());
     for (size_t k = 0; k < set.size(); ++k) {
       Prob p = probs[set[k]];
@@ -572,7 +585,8 @@ std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs)
       h.probs.push_back(p);
       ++h.nprobs;
     }
-    for (int u = 0; u < quant_units(lead.M); ++u) h.units.push_back(int2{first, u});
+    const int units = set.size() > 1 && nc > 0 ? quant_set_units(lead.M) : quant_units(lead.M);
+    for (int u = 0; u < units; ++u) h.units.push_back(int2{first, u});
     h.max_m = std::max(h.max_m, lead.M);
     h.max_k = std::max(h.max_k, lead.K);
   }

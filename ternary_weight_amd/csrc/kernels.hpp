@@ -22,6 +22,13 @@ constexpr int kGemvMaxM = 16;
 constexpr int kQuantRowsPerWave = 1;
 constexpr int kQuantRows = 4 * kQuantRowsPerWave;
 inline int quant_units(int M) { return (M + kQuantRows - 1) / kQuantRows; }
+// Share-set launches (shared && quant_chunks(K) > 0): kSetRows rows per
+// workgroup, kSetRowsPerWave per wave, and at most quant_set_max(chunks)
+// problems per set (larger sets are split by the caller).
+constexpr int kSetRowsPerWave = 4;
+constexpr int kSetRows = 4 * kSetRowsPerWave;
+inline int quant_set_units(int M) { return (M + kSetRows - 1) / kSetRows; }
+int quant_set_max(int nc);
 // Decode kernel: a workgroup owns 64 weight rows of one problem.  Problems
 // are launched in buckets of equal superblock count ceil(K/256) (1..16; 0 =
 // the generic variant for longer K).

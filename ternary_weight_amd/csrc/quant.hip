@@ -97,83 +97,104 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
   }
 }
 
-// Share sets: the workgroup's kQuantRows rows are quantized for every problem
-// of the set, wave w taking problems w, w+4, ...: it keeps that problem's
-// norm weight in registers and has R rows of x in flight at once.  The
-// waves of a workgroup read the same rows at the same time, so x comes from
-// HBM once and from L2 for the siblings; each wave's Sum(x^2) has the order
-// of the plain variant, hence the same factor.
-template <int NC, int NW>
-__device__ __forceinline__ void quant_shared_rows(const Prob& P, const Prob& Q, int m0, int lane) {
-  constexpr int R = NC >= 16 ? 1 : (16 / NC >= kQuantRows ? kQuantRows : 16 / NC);
+// Share sets whose norm weights fit in registers alongside the row
+// (share <= quant_set_max(NC)): each wave owns kSetRowsPerWave rows of the
+// set, reads each row once (the next row's loads in flight while the current
+// one is processed), computes its Sum(x^2) once, and emits every problem's
+// codes from the same registers; the set's norm weights are loaded once per
+// wave and widened to f32 (1 where a problem has none: u = x * 1 = x).  Each
+// row's Sum(x^2), max|u| and codes follow the plain variant's order and
+// arithmetic, so results are bit-identical to unshared quantization.
+template <int NC, int SMAX>
+__global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int local;
+  const int pi = find_prob(set, blockIdx.x, &local);
+  const Prob P = prob_at(set, pi);
+  const int share = P.share > 1 ? (P.share < SMAX ? P.share : SMAX) : 1;
   const int nch = P.K >> 2;
-  f4 w[NC];
-  if (NW != kNwNone) {
+  int8_t* xq[SMAX];
+  float* fac[SMAX];
+  int32_t* rsum[SMAX];
+  bool norm[SMAX];
+  f4 w[SMAX][NC];
+#pragma unroll
+  for (int p = 0; p < SMAX; ++p) {
+    if (p >= share) break;
+    const Prob Q = p == 0 ? P : prob_at(set, pi + p);
+    xq[p] = Q.xq;
+    fac[p] = Q.factor;
+    rsum[p] = Q.rowsum;
+    norm[p] = Q.norm_w != nullptr;
+    const int kind = nw_kind(Q);
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = lane + kWave * i;
-      w[i] = c < nch ? nw_chunk<NW>(Q, c) : f4{0.f, 0.f, 0.f, 0.f};
+      f4 v = f4{1.f, 1.f, 1.f, 1.f};
+      if (c >= nch) v = f4{0.f, 0.f, 0.f, 0.f};
+      else if (kind == kNwF32) v = nw_chunk<kNwF32>(Q, c);
+      else if (kind == kNwF16) v = nw_chunk<kNwF16>(Q, c);
+      w[p][i] = v;
     }
   }
-  for (int r0 = 0; r0 < kQuantRows; r0 += R) {
-    f4 xv[R][NC];
+  const int m0 = local * kSetRows + wave_id() * kSetRowsPerWave;
+  auto load_row = [&](int m, f4 (&xv)[NC]) {
+    const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m < P.M ? m : 0) * P.K);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int m = m0 + r0 + r;
-      const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m < P.M ? m : 0) * P.K);
-#pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c = lane + kWave * i;
-        xv[r][i] = (m < P.M && c < nch) ? xr[c] : f4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      xv[i] = (m < P.M && c < nch) ? xr[c] : f4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+  f4 xa[NC], xb[NC];
+  load_row(m0, xa);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int m = m0 + r0 + r;
-      if (m >= P.M) break;
-      float ss = 0.f, amax = 0.f;
+  for (int r = 0; r < kSetRowsPerWave; ++r) {
+    const int m = m0 + r;
+    f4(&xv)[NC] = (r & 1) ? xb : xa;
+    f4(&xn)[NC] = (r & 1) ? xa : xb;
+    if (r + 1 < kSetRowsPerWave) load_row(m + 1, xn);
+    if (m >= P.M) break;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      if (c < nch) ss += sq4(xv[i]);
+    }
+    const double ssd = wave_sum(static_cast<double>(ss));
+#pragma unroll
+    for (int p = 0; p < SMAX; ++p) {
+      if (p >= share) break;
+      float amax = 0.f;
       f4 u[NC];
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
-        const int c = lane + kWave * i;
-        u[i] = f4{0.f, 0.f, 0.f, 0.f};
-        if (c < nch) {
-          ss += sq4(xv[r][i]);
-          u[i] = NW == kNwNone ? xv[r][i] : xv[r][i] * w[i];
-          amax = fmaxf(amax, absmax4(u[i]));
-        }
+        u[i] = xv[i] * w[p][i];
+        amax = fmaxf(amax, absmax4(u[i]));
       }
-      const double ssd = wave_sum(static_cast<double>(ss));
       amax = wave_max(amax);
-      BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(Q.xq + static_cast<int64_t>(m) * Q.K);
+      BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(xq[p] + static_cast<int64_t>(m) * P.K);
       int rs = 0;
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
         const int c = lane + kWave * i;
         if (c < nch) qrow[c] = codes4(u[i], amax, &rs);
       }
-      finish_row(Q, m, ssd, amax, rs, lane);
+      rs = wave_sum(rs);
+      if (lane == 0) {
+        gptr_out<float>(fac[p])[m] = quant_factor(ssd, P.K, P.eps, amax, norm[p]);
+        if (rsum[p]) gptr_out<int32_t>(rsum[p])[m] = rs;
+      }
     }
   }
 }
 
-template <int NC>
-__global__ __launch_bounds__(256) void quant_shared_kernel(ProbSet set) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int local;
-  const int pi = find_prob(set, blockIdx.x, &local);
-  const Prob P = prob_at(set, pi);
-  const int share = P.share > 1 ? P.share : 1;
-  const int m0 = local * kQuantRows;
-  for (int p = wave_id(); p < share; p += 4) {
-    const Prob Q = p == 0 ? P : prob_at(set, pi + p);
-    switch (nw_kind(Q)) {
-      case kNwF32: quant_shared_rows<NC, kNwF32>(P, Q, m0, lane); break;
-      case kNwF16: quant_shared_rows<NC, kNwF16>(P, Q, m0, lane); break;
-      default: quant_shared_rows<NC, kNwNone>(P, Q, m0, lane);
-    }
-  }
-}
+// Problems per set of the register-resident kernel: their norm weights take
+// at most 16 float4 per lane, and at most 3 problems (a layer's q, k and v;
+// a fourth norm weight would cost the K = 1024 kernel its fourth wave per
+// SIMD).
+constexpr int set_max(int nc) { return nc <= 0 ? 0 : (16 / nc < 3 ? (16 / nc < 1 ? 1 : 16 / nc) : 3); }
+int quant_set_max(int nc) { return set_max(nc); }
 
 // Rows longer than the register budget: two streaming passes over the row.
 __device__ void quant_stream_row(const Prob& P, int m, int lane);
@@ -270,8 +291,19 @@ hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hip
   if (shared && act != kActNone) return hipErrorInvalidValue;
   const int nc = quant_chunks(max_k);
   const dim3 grid(set.total), block(256);
-  if (shared) {
-    BL_QUANT_SWITCH(quant_shared_kernel)
+  if (shared && nc > 0) {
+    switch (nc) {
+#define BL_QUANT_SET(n)                                                                          \
+  case n:                                                                                        \
+    hipLaunchKernelGGL((quant_set_kernel<n, set_max(n)>), grid, block, 0, stream, set);          \
+    break;
+      BL_QUANT_SET(1) BL_QUANT_SET(2) BL_QUANT_SET(3) BL_QUANT_SET(4) BL_QUANT_SET(6)
+      BL_QUANT_SET(8)
+#undef BL_QUANT_SET
+      default: return hipErrorInvalidValue;  // longer rows hold one problem: never shared
+    }
+  } else if (shared) {
+    hipLaunchKernelGGL(quant_stream_kernel, grid, block, 0, stream, set);
   } else if (act == kActSilu) {
     BL_QUANT_SWITCH(quant_reg_kernel, , kActSilu)
   } else if (act == kActGeluTanh) {

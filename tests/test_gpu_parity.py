@@ -374,6 +374,36 @@ def test_group_shared_input_quantization():
         assert rel_l2(host(items[i]["y"]), ref) <= 1e-3
 
 
+def test_group_large_share_sets_split():
+    # Share sets larger than the register-resident share kernel holds (3
+    # problems at K <= 1024, 2 at K = 2048) are split; every part still reads
+    # x once and gives bit-identical results to separate calls, with norm
+    # weights of every kind (float32, float16, none) inside one set.
+    M = 260
+    x = dev(inputs.activations(27, 0, 0, M, 1024))
+    x2 = dev(inputs.activations(27, 0, 1, M, 2048))
+    specs = [(x, 1024, 64 * (i + 1), ("f32", "f16", "none")[i % 3]) for i in range(6)] + \
+            [(x2, 2048, 96 * (i + 1), ("f32", "none", "f16")[i]) for i in range(3)]
+    items, singles = [], []
+    for i, (xx, K, N, kind) in enumerate(specs):
+        packed, scale = oracle.i2s_pack(inputs.weight(27, 1, i, N, K))
+        nw = dev(inputs.norm_weight(27, 1, i, K))
+        nw = None if kind == "none" else (nw.half() if kind == "f16" else nw)
+        it = dict(x=xx, norm_w=nw, packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                  y=torch.full((M, N), float("nan"), device=DEV))
+        items.append(it)
+        singles.append(bl.bitlinear_forward(xx, nw, it["packed_w"], scale, N, EPS))
+    with bl.Group(items) as g:
+        q = sorted((d["kind"], d["bucket"], d["count"]) for d in g.forward_launches()
+                   if d["kind"].startswith("quant"))
+        # K = 1024: two parts of 3, one launch; K = 2048: a part of 2 and a single
+        assert q == [("quant", 8, 1), ("quant_shared", 4, 6), ("quant_shared", 8, 2)], q
+        g.forward()
+        torch.cuda.synchronize()
+        for i, (it, ys) in enumerate(zip(items, singles)):
+            assert torch.equal(it["y"], ys), i
+
+
 def test_group_forward_in_cuda_graph():
     # The group forward captured into a graph: the fused decode launches (the
     # merged one and a 13-superblock one, which stays separate) fork onto the
