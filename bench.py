@@ -180,6 +180,24 @@ def launch_bytes(kind: str, M: int, K: int, N: int, norm=True) -> int:
     raise ValueError(kind)
 
 
+def profile_value(name: str, field: str, source: str):
+    """A number recorded in a committed rocprofv3 summary (profiles/<name>.md),
+    or None when the summary is missing or the kernel source changed since it
+    was taken (the summary names the source's sha256)."""
+    path = os.path.join(ROOT, "profiles", f"{name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_v = re.search(field + r":\s*([0-9.eE+-]+)", text)
+    if not (m_sha and m_v):
+        return None
+    src = open(os.path.join(ROOT, "ternary_weight_amd", "csrc", source), "rb").read()
+    if hashlib.sha256(src).hexdigest() != m_sha.group(1):
+        return None
+    return float(m_v.group(1))
+
+
 def traffic_from_profiles(kernel_tag: str, source: str):
     """HBM bytes per launch from a committed rocprofv3 PMC summary, or None.
 
@@ -630,6 +648,12 @@ def main():
                 "achieved": round(pre["mm_tops"], 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": round(pre["mm_tops"] / INT8_PEAK_TOPS, 4),
                 "traffic": traffic_from_profiles("gemm_prefill_qwen3_stack", "gemm.hip"),
+                # rocprofv3 counters of the same launch: SQ_VALU_MFMA_BUSY_CYCLES over
+                # GRBM_GUI_ACTIVE x SIMDs, and the shader clock GRBM_GUI_ACTIVE implies
+                "mfma_busy_from_counters": profile_value("gemm_prefill_qwen3_stack_mfma",
+                                                         "mfma_busy_fraction", "gemm.hip"),
+                "clock_GHz_from_counters": profile_value("gemm_prefill_qwen3_stack_mfma",
+                                                         "effective_clock_GHz", "gemm.hip"),
                 "algorithmic_ops_per_launch": pre["ops"],
                 "avg_launch_us": round(pre["mm_ms"] * 1e3, 1),
                 "frac_of_measured": round(pre["mm_tops"] / peaks["mfma_i8_TOPS"], 4),
