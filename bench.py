@@ -384,6 +384,12 @@ def bench_ffn_glue(torch, bl, args):
     fwd_ms = timed(lambda: bl.bitlinear_glu_forward(gate, up, bl.ACT_SILU, nw, pw, scale, N, inputs.EPS, y=y), reps)
     q_bytes = 8 * M * K + M * K + 8 * M + 4 * K     # gate + up in, codes + factor + row sum out
     unfused = q_bytes + 8 * M * K                     # the product written and read back in fp32
+    # Decode size (M = 1): glue, RMSNorm, quantization and the product in the
+    # one fused decode launch, no workspace.
+    g1, u1, y1 = gate[:1].contiguous(), up[:1].contiguous(), y[:1].contiguous()
+    dec_us = 1e3 * timed(lambda: bl.bitlinear_glu_forward(g1, u1, bl.ACT_SILU, nw, pw, scale, N, inputs.EPS,
+                                                          y=y1), reps)
+    dec_bytes = N * K // 4 + 8 * K + 4 * K + 4 * N
     return {
         "workload": f"Qwen3 FFN down projection fed by SiLU(gate)*up, M={M}, K={K} -> N={N}",
         "glue_quant_us": round(q_ms * 1e3, 1),
@@ -394,6 +400,8 @@ def bench_ffn_glue(torch, bl, args):
         "bytes_saved_vs_storing_the_product": round(1 - q_bytes / unfused, 3),
         "forward_ms": round(fwd_ms, 4),
         "forward_TOPS": round(2 * M * N * K / (fwd_ms * 1e-3) / 1e12, 1),
+        "decode_M1_forward_us": round(dec_us, 2),
+        "decode_M1_GBs": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),
     }
 
 
@@ -672,7 +680,8 @@ def main():
         del pre
         glue = bench_ffn_glue(torch, bl, args)
         log(f"ffn glue: glue+quant {glue['glue_quant_us']:.1f} us ({glue['roofline']['achieved']:.0f} GB/s), "
-            f"glue-fed down forward {glue['forward_ms']:.3f} ms ({glue['forward_TOPS']:.0f} TOPS)")
+            f"glue-fed down forward {glue['forward_ms']:.3f} ms ({glue['forward_TOPS']:.0f} TOPS); "
+            f"M=1 one-launch glue forward {glue['decode_M1_forward_us']:.1f} us")
         out["ffn_glue"] = glue
     dp = bench_device_pack(torch, bl, args)
     log(f"device pack: {dp['us']:.1f} us ({dp['roofline']['achieved']:.0f} GB/s)")

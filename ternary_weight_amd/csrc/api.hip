@@ -114,14 +114,17 @@ ProbSet single_set(const Prob& p, int total) {
 }
 
 // Stage 2 for one problem: the decode kernel for M <= kGemvMaxM (fused:
-// with stage 1 inside it), else the tiled MFMA kernel.
+// with stage 1, and the FFN glue when p.act is set, inside it), else the
+// tiled MFMA kernel.
 hipError_t launch_matmul_single(const Prob& p, bool raw, bool fused, hipStream_t stream) {
   if (p.M <= kGemvMaxM) {
     GemvLaunch L{};
     L.single = p;
     L.units = nullptr;
-    L.total = gemv_units(p.N, gemv_bucket(p.K));
-    return launch_gemv(L, raw, gemv_bucket(p.K), p.M, p.K, fused, stream);
+    L.tiles = gemv_single_tiles(p.N, gemv_bucket(p.K));
+    L.total = gemv_units(p.N, gemv_bucket(p.K), L.tiles);
+    return launch_gemv(L, raw, gemv_bucket(p.K), p.M, p.K, fused, stream,
+                       fused && p.act != kActNone);
   }
   return launch_gemm(single_set(p, gemm_units(p.M, p.N)), raw, stream);
 }
@@ -290,9 +293,6 @@ bl_status glu_forward_impl(const float* gate, const float* up, int32_t act, cons
     if (M > 0 && !aligned16(up)) return BL_ERR_MISALIGNED;
     if (M == 0) return BL_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const WsLayout l = ws_layout(M, K);
-    uint8_t* ws = nullptr;
-    if ((st = acquire_ws(s, l.bytes, &ws)) != BL_OK) return st;
     Prob p{};
     p.x = gate;
     p.up = up;
@@ -300,9 +300,6 @@ bl_status glu_forward_impl(const float* gate, const float* up, int32_t act, cons
     p.norm_w = static_cast<const float*>(norm_w);
     p.nw_f16 = nw_f16 ? 1 : 0;
     p.w = packed_w;
-    p.xq = reinterpret_cast<int8_t*>(ws + l.xq);
-    p.factor = reinterpret_cast<float*>(ws + l.factor);
-    p.rowsum = reinterpret_cast<int32_t*>(ws + l.rowsum);
     p.y = y;
     p.acc = nullptr;
     p.w_scale = w_scale;
@@ -310,6 +307,14 @@ bl_status glu_forward_impl(const float* gate, const float* up, int32_t act, cons
     p.M = static_cast<int>(M);
     p.K = static_cast<int>(K);
     p.N = static_cast<int>(N);
+    // Decode sizes whose gate and up rows fit on chip: one launch, no workspace.
+    if (gemv_fusable(p.M, p.K, true)) return from_hip(launch_matmul_single(p, false, true, s));
+    const WsLayout l = ws_layout(M, K);
+    uint8_t* ws = nullptr;
+    if ((st = acquire_ws(s, l.bytes, &ws)) != BL_OK) return st;
+    p.xq = reinterpret_cast<int8_t*>(ws + l.xq);
+    p.factor = reinterpret_cast<float*>(ws + l.factor);
+    p.rowsum = reinterpret_cast<int32_t*>(ws + l.rowsum);
     if ((st = from_hip(launch_quant(single_set(p, quant_units(p.M)), p.K, false, p.act, s))) != BL_OK)
       return st;
     return from_hip(launch_matmul_single(p, false, false, s));

@@ -52,19 +52,23 @@ namespace bl {
 constexpr int kGemvLdsBytes = 64 * 1024;   // activation staging limit per workgroup
 constexpr int kMaxNsb = 16;                // specialised superblock counts 1..16
 constexpr int kGemvFusedLdsBytes = 32 * 1024;  // fused-variant staging limit per workgroup
+constexpr int kGemvGlueLdsBytes = 48 * 1024;   // the same with the FFN glue's up rows staged too
 
 // LDS layout of the fused variant (byte offsets): the staged codes (M rows of
 // nsb superblocks), a row table (epilogue scale and row sum of up to 16
-// rows), the fp32 rows and the norm weight, each 1 KB aligned.  Monotonic in
-// M and K, so a launch sized for its largest problem fits every problem.
+// rows), the fp32 rows, with the FFN glue (glue) the fp32 up rows, and the
+// norm weight, each 1 KB aligned.  Monotonic in M and K, so a launch sized
+// for its largest problem fits every problem.
 struct FusedLds {
-  int rows, x, nw, bytes;
+  int rows, x, up, nw, bytes;
 };
-__host__ __device__ inline FusedLds fused_lds(int M, int K, int nsb) {
+__host__ __device__ inline FusedLds fused_lds(int M, int K, int nsb, bool glue) {
   FusedLds l;
+  const int xb = (M * K * 4 + 1023) & ~1023;
   l.rows = (M * nsb * 256 + 1023) & ~1023;
   l.x = l.rows + 1024;
-  l.nw = l.x + ((M * K * 4 + 1023) & ~1023);
+  l.up = l.x + xb;
+  l.nw = l.up + (glue ? xb : 0);
   l.bytes = l.nw + ((K * 4 + 1023) & ~1023);
   return l;
 }
@@ -133,10 +137,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One workgroup's work: `unit` of problem P.  NSB > 0: exactly NSB
-// superblocks per tile.  NSB == 0: any K, streamed.
-template <bool RAW, bool FROM_LDS, int NSB, bool FUSED>
-__device__ __forceinline__ void gemv_body(const Prob& P, const int unit) {
+// superblocks per tile.  NSB == 0: any K, streamed.  GLUE (fused only): the
+// input rows are the FFN glue act(x) * up (P.act, P.up).  tpu: 16-row tiles
+// per wave (1..T); below T a workgroup owns 64*tpu rows, so that a launch of
+// one small problem still spreads over many workgroups (the window then runs
+// on zero-filled loads past tile tpu-1, which store nothing).
+template <bool RAW, bool FROM_LDS, int NSB, bool FUSED, bool GLUE = false>
+__device__ __forceinline__ void gemv_body(const Prob& P, const int unit, const int tpu) {
   static_assert(!FUSED || (FROM_LDS && !RAW && NSB > 0), "fused: forward, staged, specialised K");
+  static_assert(!GLUE || FUSED, "glue: fused only");
   constexpr int T = gemv_tiles(NSB);
   constexpr int D = gemv_depth(NSB);
   constexpr int kHeld = NSB > 0 ? NSB : 2;
@@ -168,24 +177,28 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit) {
   // codes 0 anyway).
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(P.xq), 0, FUSED ? 0 : M * K, kBufferDword3);
-  const FusedLds fl = fused_lds(M, K, NSB);
+  constexpr bool glue = GLUE;
+  const FusedLds fl = fused_lds(M, K, NSB, glue);
   if (FUSED) {
-    // fp32 rows and the norm weight (4K bytes, 2K if float16, none without
-    // one), copied linearly (1 KB per wave instruction; bytes past either
-    // buffer read 0).
+    // fp32 rows, with the glue the up rows, and the norm weight (4K bytes,
+    // 2K if float16, none without one), copied linearly (1 KB per wave
+    // instruction; bytes past each buffer read 0).
     const int nwb = P.norm_w ? K * (P.nw_f16 ? 2 : 4) : 0;
     const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(P.x), 0, M * K * 4, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t urs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(P.up), 0, glue ? M * K * 4 : 0, kBufferDword3);
     const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(P.norm_w), 0, nwb, kBufferDword3);
-    const int ux = (M * K * 4 + 1023) >> 10, un = (nwb + 1023) >> 10;
-    for (int i = wave; i < ux + un; i += 4) {
-      const bool isx = i < ux;
-      const int u = isx ? i : i - ux;
+    const int ux = (M * K * 4 + 1023) >> 10, uu = glue ? ux : 0, un = (nwb + 1023) >> 10;
+    for (int i = wave; i < ux + uu + un; i += 4) {
+      const int part = i < ux ? 0 : (i < ux + uu ? 1 : 2);
+      const int u = i - (part == 0 ? 0 : (part == 1 ? ux : ux + uu));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          isx ? frs : nrs,
-          (__attribute__((address_space(3))) void*)(xlds + (isx ? fl.x : fl.nw) + 1024 * u), 16,
-          1024 * u + 16 * lane, 0, 0, 0);
+          part == 0 ? frs : (part == 1 ? urs : nrs),
+          (__attribute__((address_space(3))) void*)(xlds + (part == 0 ? fl.x : (part == 1 ? fl.up : fl.nw)) +
+                                                     1024 * u),
+          16, 1024 * u + 16 * lane, 0, 0, 0);
     }
   } else if (FROM_LDS) {
     const int row_slots = kpad >> 4;
@@ -211,10 +224,10 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit) {
   // Weight loads: lane reads 16 bytes of row tile0 + 64t + r16 at superblock sb.
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(P.w), 0, N * rowbytes, kBufferDword3);
-  const int tile0 = (unit * 4 * T + wave) * 16;
+  const int tile0 = (unit * 4 * tpu + wave) * 16;
   const int wbase = (tile0 + r16) * rowbytes + 16 * g;
   auto wload = [&](int t, int sb) -> v4i {
-    const bool ok = (t < T) & (tile0 + 64 * t + r16 < N) & (sb < nsb) & (64 * sb + 16 * g < rowbytes);
+    const bool ok = (t < tpu) & (tile0 + 64 * t + r16 < N) & (sb < nsb) & (64 * sb + 16 * g < rowbytes);
     return __builtin_amdgcn_raw_buffer_load_b128(
         wrs, ok ? wbase + 64 * t * rowbytes + 64 * sb : kOob, 0, 0);
   };
@@ -246,6 +259,23 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit) {
     auto nwc = [&](int c) { return nwh ? half4(reinterpret_cast<const u2*>(xlds + fl.nw)[c]) : nw[c]; };
     float* row_scale = reinterpret_cast<float*>(xlds + fl.rows);
     int* row_sum = reinterpret_cast<int*>(xlds + fl.rows + 64);
+    if (glue) {
+      // FFN glue: each wave replaces its rows by act(gate) * up in place,
+      // with the quantization kernel's per-element arithmetic (glu4).
+      f4* xw = reinterpret_cast<f4*>(xlds + fl.x);
+      const f4* uf = reinterpret_cast<const f4*>(xlds + fl.up);
+      const bool silu = P.act == kActSilu;
+      for (int m = wave; m < M; m += 4) {
+#pragma unroll
+        for (int j = 0; j < NSB; ++j) {
+          const int c = lane + kWave * j;
+          if (c < nch) {
+            const f4 gv = xw[m * nch + c], uv = uf[m * nch + c];
+            xw[m * nch + c] = silu ? glu4<kActSilu>(gv, uv) : glu4<kActGeluTanh>(gv, uv);
+          }
+        }
+      }
+    }
     for (int m = wave; m < M; m += 4) {
       // Two passes over the staged row (no per-lane copy held in registers,
       // which the weight loads in flight need).
@@ -356,6 +386,7 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit) {
     // stores instead of one four-lane store per tile and wave.
     const int span = 64 * T;
     if (FUSED && M * span * 4 <= fl.bytes - fl.x) {
+      // (rows of the tiles past tpu are gathered but not written)
       int32_t* ol = reinterpret_cast<int32_t*>(xlds + fl.x);
       if (r16 < M) {
 #pragma unroll
@@ -365,14 +396,16 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      const int base = unit * span;
-      for (int c = threadIdx.x; c < M * (span / 4); c += 256) {
-        const int m = c / (span / 4), j = c - m * (span / 4);
+      const int base = unit * 64 * tpu;
+      const int q = 16 * tpu;  // 16-byte chunks per output row
+      for (int c = threadIdx.x; c < M * q; c += 256) {
+        const int m = c / q, j = c - m * q;
         gemv_store<RAW>(P, *reinterpret_cast<const v4i*>(ol + m * span + 4 * j), base + 4 * j, m);
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < T; ++t) gemv_store<RAW>(P, res[t], tile0 + 64 * t + 4 * g, r16);
+      for (int t = 0; t < T; ++t)
+        if (t < tpu) gemv_store<RAW>(P, res[t], tile0 + 64 * t + 4 * g, r16);
     }
   } else {
     // Generic K, one tile: two superblocks in flight, pairs processed
@@ -394,11 +427,13 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit) {
 
 // The launch covers the by-value problem in `single` (units == nullptr) or
 // the FatUnit table `units`.
-template <bool RAW, bool FROM_LDS, int NSB, bool FUSED>
-__global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* units) {
+// tiles: 16-row tiles per wave, 0 = the bucket's full count.
+template <bool RAW, bool FROM_LDS, int NSB, bool FUSED, bool GLUE>
+__global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* units, int tiles) {
   int unit = blockIdx.x;
   const Prob P = units ? fat_unit_at(units, blockIdx.x, &unit) : single;
-  gemv_body<RAW, FROM_LDS, NSB, FUSED>(P, unit);
+  constexpr int T = gemv_tiles(NSB);
+  gemv_body<RAW, FROM_LDS, NSB, FUSED, GLUE>(P, unit, tiles > 0 && tiles < T ? tiles : T);
 }
 
 // Fused decode units of several superblock counts (1..kGemvMergedMaxNsb) in
@@ -411,7 +446,7 @@ __global__ __launch_bounds__(256) void gemv_fused_merged_kernel(const FatUnit* u
   const Prob P = fat_unit_at(units, blockIdx.x, &unit, &nsb);
   switch (nsb) {
 #define BL_MERGED_CASE(n) \
-  case n: gemv_body<false, true, n, true>(P, unit); break;
+  case n: gemv_body<false, true, n, true>(P, unit, gemv_tiles(n)); break;
     BL_MERGED_CASE(1) BL_MERGED_CASE(2) BL_MERGED_CASE(3) BL_MERGED_CASE(4)
     BL_MERGED_CASE(5) BL_MERGED_CASE(6) BL_MERGED_CASE(7) BL_MERGED_CASE(8)
     BL_MERGED_CASE(9) BL_MERGED_CASE(10) BL_MERGED_CASE(11) BL_MERGED_CASE(12)
@@ -426,9 +461,17 @@ int gemv_bucket(int K) {
   return nsb <= kMaxNsb ? nsb : 0;
 }
 
-int gemv_units(int N, int bucket) {
-  const int rows = 64 * gemv_tiles(bucket);
+int gemv_units(int N, int bucket, int tiles) {
+  const int T = gemv_tiles(bucket);
+  const int rows = 64 * (tiles > 0 && tiles < T ? tiles : T);
   return (N + rows - 1) / rows;
+}
+
+int gemv_single_tiles(int N, int bucket) {
+  // Fewest tiles per wave that still give about two workgroups per CU.
+  const int T = gemv_tiles(bucket);
+  const int want = (N + 64 * kGemvSingleUnits - 1) / (64 * kGemvSingleUnits);
+  return want < 1 ? 1 : (want > T ? T : want);
 }
 
 namespace {
@@ -443,13 +486,13 @@ size_t gemv_lds_bytes(int bucket, int max_m, int max_k) {
   return (bytes + 1023) / 1024 * 1024;
 }
 
-template <bool RAW, bool LDS, bool FUSED>
+template <bool RAW, bool LDS, bool FUSED, bool GLUE = false>
 hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStream_t stream) {
   const dim3 grid(L.total), block(256);
 #define BL_GEMV_CASE(n)                                                                           \
   case n:                                                                                         \
-    hipLaunchKernelGGL((gemv_kernel<RAW, LDS, n, FUSED>), grid, block, shmem, stream, L.single,   \
-                       L.units);                                                                  \
+    hipLaunchKernelGGL((gemv_kernel<RAW, LDS, n, FUSED, GLUE>), grid, block, shmem, stream,       \
+                       L.single, L.units, L.tiles);                                               \
     break;
   switch (bucket) {
     BL_GEMV_CASE(1) BL_GEMV_CASE(2) BL_GEMV_CASE(3) BL_GEMV_CASE(4) BL_GEMV_CASE(5)
@@ -458,8 +501,8 @@ hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStrea
     BL_GEMV_CASE(16)
     default:
       if constexpr (!FUSED)
-        hipLaunchKernelGGL((gemv_kernel<RAW, LDS, 0, false>), grid, block, shmem, stream, L.single,
-                           L.units);
+        hipLaunchKernelGGL((gemv_kernel<RAW, LDS, 0, false, false>), grid, block, shmem, stream,
+                           L.single, L.units, 0);
       else
         return hipErrorInvalidValue;
   }
@@ -469,10 +512,10 @@ hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStrea
 
 }  // namespace
 
-bool gemv_fusable(int M, int K) {
+bool gemv_fusable(int M, int K, bool glue) {
   const int b = gemv_bucket(K);
   return M >= 1 && M <= kGemvMaxM && b > 0 &&
-         fused_lds(M, K, b).bytes <= kGemvFusedLdsBytes;
+         fused_lds(M, K, b, glue).bytes <= (glue ? kGemvGlueLdsBytes : kGemvFusedLdsBytes);
 }
 
 hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int max_k,
@@ -481,17 +524,18 @@ hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int ma
   const int b = gemv_bucket(max_k);
   if (b <= 0 || b > kGemvMergedMaxNsb) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemv_fused_merged_kernel, dim3(total), dim3(256),
-                     fused_lds(max_m, max_k, b).bytes, stream, units);
+                     fused_lds(max_m, max_k, b, false).bytes, stream, units);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,
-                       bool fused, hipStream_t stream) {
+                       bool fused, hipStream_t stream, bool glue) {
   if (L.total <= 0) return hipSuccess;
   if (fused) {
     if (raw || bucket <= 0) return hipErrorInvalidValue;
-    return launch_bucket<false, true, true>(L, bucket, fused_lds(max_m, max_k, bucket).bytes,
-                                            stream);
+    const size_t shmem = fused_lds(max_m, max_k, bucket, glue).bytes;
+    return glue ? launch_bucket<false, true, true, true>(L, bucket, shmem, stream)
+                : launch_bucket<false, true, true>(L, bucket, shmem, stream);
   }
   const size_t shmem = gemv_lds_bytes(bucket, max_m, max_k);
   const bool lds = shmem <= static_cast<size_t>(kGemvLdsBytes);

@@ -32,7 +32,12 @@ int quant_set_max(int nc);
 // Decode kernel: a workgroup owns 64 weight rows of one problem.  Problems
 // are launched in buckets of equal superblock count ceil(K/256) (1..16; 0 =
 // the generic variant for longer K).
-int gemv_units(int N, int bucket);
+// tiles: 16-row tiles per wave of each workgroup (0 = the bucket's full
+// count, 2 * depth); a single-problem launch takes gemv_single_tiles(N,
+// bucket), which keeps about kGemvSingleUnits workgroups busy.
+constexpr int kGemvSingleUnits = 512;
+int gemv_units(int N, int bucket, int tiles = 0);
+int gemv_single_tiles(int N, int bucket);
 int gemv_bucket(int K);
 int gemm_units(int M, int N);
 
@@ -52,13 +57,16 @@ hipError_t launch_rowsum(const Prob& p, hipStream_t stream);
 // staging).  fused: the kernel also runs stage 1 for its rows (RMSNorm +
 // int8 quantization from x and norm_w, same arithmetic as launch_quant), so
 // no quantization launch and no workspace are needed; only for problems
-// with gemv_fusable(M, K) and the forward epilogue.
+// with gemv_fusable(M, K, glue) and the forward epilogue.  glue: the
+// problems' input is the FFN glue act(x) * up (Prob::act, Prob::up), which
+// the fused kernel forms in LDS.
 struct GemvLaunch {
   Prob single;
   const FatUnit* units;
   int total;
+  int tiles;  // 16-row tiles per wave, 0 = the bucket's full count
 };
-bool gemv_fusable(int M, int K);
+bool gemv_fusable(int M, int K, bool glue = false);
 // Fused decode problems of up to kGemvMergedMaxNsb superblocks in one launch
 // over a FatUnit table whose records carry each unit's superblock count
 // (FatUnit::nsb), longest first.  max_m, max_k: the largest M and K.
@@ -66,7 +74,7 @@ constexpr int kGemvMergedMaxNsb = 12;
 hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int max_k,
                               hipStream_t stream);
 hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,
-                       bool fused, hipStream_t stream);
+                       bool fused, hipStream_t stream, bool glue = false);
 // Device-side absmean ternary quantization and I2_S packing of w (device,
 // [N][K] float32, 16-byte aligned) into packed (device, N*K/4 + 4 bytes):
 // codes, then the scale.  partial: kPackPartials doubles of scratch;
