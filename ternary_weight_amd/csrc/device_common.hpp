@@ -129,18 +129,41 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 }
 
-// ---- wave64 butterfly reductions (every lane ends with the result) --------
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// ---- wave64 reductions (every lane ends with the result; call them with
+// the whole wave active) -----------------------------------------------------
+// Order-free ones (max, integer sum): four DPP steps inside each row of 16
+// lanes (swap neighbours, swap pairs, mirror 8, mirror 16), then the four row
+// results read into scalars; no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+__device__ __forceinline__ float fmax_dpp(float v, int bits) {
+  return fmaxf(v, __builtin_bit_cast(float, bits));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmax_dpp(v, dpp_mov<kDppSwap1>(__builtin_bit_cast(int, v)));
+  v = fmax_dpp(v, dpp_mov<kDppSwap2>(__builtin_bit_cast(int, v)));
+  v = fmax_dpp(v, dpp_mov<kDppHalfMirror>(__builtin_bit_cast(int, v)));
+  v = fmax_dpp(v, dpp_mov<kDppMirror>(__builtin_bit_cast(int, v)));
+  const int b = __builtin_bit_cast(int, v);
+  return fmaxf(fmax_dpp(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                        __builtin_amdgcn_readlane(b, 16)),
+               fmax_dpp(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                        __builtin_amdgcn_readlane(b, 48)));
 }
 __device__ __forceinline__ int wave_sum(int v) {
+  v += dpp_mov<kDppSwap1>(v);
+  v += dpp_mov<kDppSwap2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  v += dpp_mov<kDppMirror>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+// The double sum keeps its butterfly order (its rounding depends on it; the
+// pairs are added commutatively, so every lane gets the same bits).
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;

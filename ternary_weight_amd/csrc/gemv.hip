@@ -51,22 +51,26 @@ namespace bl {
 
 constexpr int kGemvLdsBytes = 64 * 1024;   // activation staging limit per workgroup
 constexpr int kMaxNsb = 16;                // specialised superblock counts 1..16
-constexpr int kGemvFusedLdsBytes = 32 * 1024;  // fused-variant staging limit per workgroup
-constexpr int kGemvGlueLdsBytes = 48 * 1024;   // the same with the FFN glue's up rows staged too
+constexpr int kGemvFusedLdsBytes = 40 * 1024;  // fused-variant staging limit per workgroup
+constexpr int kGemvGlueLdsBytes = 56 * 1024;   // the same with the FFN glue's up rows staged too
 
 // LDS layout of the fused variant (byte offsets): the staged codes (M rows of
-// nsb superblocks), a row table (epilogue scale and row sum of up to 16
-// rows), the fp32 rows, with the FFN glue (glue) the fp32 up rows, and the
-// norm weight, each 1 KB aligned.  Monotonic in M and K, so a launch sized
-// for its largest problem fits every problem.
+// nsb superblocks) at 0, a table (epilogue scale of up to 16 rows, then the
+// absmax and the code sum of each (row, chunk column) unit, see gemv_body),
+// the lanes' partial sums of squares (one float per lane and unit, as many
+// bytes as the codes), the fp32 rows, with the FFN glue (glue) the fp32 up
+// rows, and the norm weight, each 1 KB aligned.  Monotonic in M and K, so a
+// launch sized for its largest problem fits every problem.
 struct FusedLds {
-  int rows, x, up, nw, bytes;
+  int tab, sq, x, up, nw, bytes;
 };
 __host__ __device__ inline FusedLds fused_lds(int M, int K, int nsb, bool glue) {
   FusedLds l;
+  const int cb = (M * nsb * 256 + 1023) & ~1023;
   const int xb = (M * K * 4 + 1023) & ~1023;
-  l.rows = (M * nsb * 256 + 1023) & ~1023;
-  l.x = l.rows + 1024;
+  l.tab = cb;
+  l.sq = l.tab + ((64 + 8 * M * nsb + 1023) & ~1023);
+  l.x = l.sq + cb;
   l.up = l.x + xb;
   l.nw = l.up + (glue ? xb : 0);
   l.bytes = l.nw + ((K * 4 + 1023) & ~1023);
@@ -246,72 +250,83 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit, const i
     asm volatile("" ::: "memory");
   }
   if (FUSED) {
-    // RMSNorm + absmax int8 quantization of the <= 16 rows, wave w taking
-    // rows w, w+4, ..., while the weight loads are in flight: the codes go
-    // to the staged activation layout (zeros up to the padded length), the
-    // row sum and the epilogue scale to the row table.
+    // RMSNorm + absmax int8 quantization of the <= 16 rows while the weight
+    // loads are in flight, spread over all four waves: unit i = (row m,
+    // chunk column j) covers chunks c = lane + 64j of row m, and wave w takes
+    // units w, w+4, ...  Pass 1 (glue first, when set) leaves each lane's
+    // sum of squares of its chunk and the unit's absmax in LDS; after a
+    // barrier, row m's factor is formed by wave m % 4 with the quantization
+    // kernel's order of operations (the lane's squares added in chunk order,
+    // then a double reduction), so factors and codes are bit-identical to
+    // it; pass 2 writes the codes to the staged layout (zeros up to the
+    // padded length) and the unit's code sum to the table.
     const int nch = K >> 2;
-    const f4* xf = reinterpret_cast<const f4*>(xlds + fl.x);
+    const int units = M * NSB;
+    f4* xf = reinterpret_cast<f4*>(xlds + fl.x);
     const f4* nw = reinterpret_cast<const f4*>(xlds + fl.nw);
     const bool norm = P.norm_w != nullptr;  // else u = x, r = 1
     const bool nwh = P.nw_f16 != 0;
     // chunk c of the norm weight, widened from float16 when stored so
     auto nwc = [&](int c) { return nwh ? half4(reinterpret_cast<const u2*>(xlds + fl.nw)[c]) : nw[c]; };
-    float* row_scale = reinterpret_cast<float*>(xlds + fl.rows);
-    int* row_sum = reinterpret_cast<int*>(xlds + fl.rows + 64);
-    if (glue) {
-      // FFN glue: each wave replaces its rows by act(gate) * up in place,
-      // with the quantization kernel's per-element arithmetic (glu4).
-      f4* xw = reinterpret_cast<f4*>(xlds + fl.x);
-      const f4* uf = reinterpret_cast<const f4*>(xlds + fl.up);
-      const bool silu = P.act == kActSilu;
-      for (int m = wave; m < M; m += 4) {
-#pragma unroll
-        for (int j = 0; j < NSB; ++j) {
-          const int c = lane + kWave * j;
-          if (c < nch) {
-            const f4 gv = xw[m * nch + c], uv = uf[m * nch + c];
-            xw[m * nch + c] = silu ? glu4<kActSilu>(gv, uv) : glu4<kActGeluTanh>(gv, uv);
-          }
+    float* row_scale = reinterpret_cast<float*>(xlds + fl.tab);
+    float* unit_max = reinterpret_cast<float*>(xlds + fl.tab + 64);
+    int* unit_sum = reinterpret_cast<int*>(xlds + fl.tab + 64 + 4 * units);
+    float* sq = reinterpret_cast<float*>(xlds + fl.sq);
+    for (int i = wave; i < units; i += 4) {
+      const int m = i / NSB, c = lane + kWave * (i - m * NSB);
+      float s2 = 0.f, a = 0.f;
+      if (c < nch) {
+        f4 xv = xf[m * nch + c];
+        if (GLUE) {
+          // FFN glue in place: act(gate) * up with the quantization kernel's
+          // per-element arithmetic (glu4).
+          const f4 uv = reinterpret_cast<const f4*>(xlds + fl.up)[m * nch + c];
+          xv = P.act == kActSilu ? glu4<kActSilu>(xv, uv) : glu4<kActGeluTanh>(xv, uv);
+          xf[m * nch + c] = xv;
         }
+        s2 = sq4(xv);
+        a = absmax4(norm ? xv * nwc(c) : xv);
       }
-    }
-    for (int m = wave; m < M; m += 4) {
-      // Two passes over the staged row (no per-lane copy held in registers,
-      // which the weight loads in flight need).
-      float ss = 0.f, amax = 0.f;
-#pragma unroll
-      for (int j = 0; j < NSB; ++j) {
-        const int c = lane + kWave * j;
-        if (c < nch) {
-          const f4 xv = xf[m * nch + c];
-          ss += sq4(xv);
-          amax = fmaxf(amax, absmax4(norm ? xv * nwc(c) : xv));
-        }
-      }
-      const double ssd = wave_sum(static_cast<double>(ss));
-      amax = wave_max(amax);
-      int sum = 0;
-#pragma unroll
-      for (int j = 0; j < NSB; ++j) {
-        const int c = lane + kWave * j;  // dword c of the padded row
-        uint32_t q = 0u;
-        if (c < nch) {
-          const f4 xv = xf[m * nch + c];
-          q = codes4(norm ? xv * nwc(c) : xv, amax, &sum);
-        }
-        *reinterpret_cast<uint32_t*>(xlds + m * kpad + ((((c >> 2) ^ (m & 7))) << 4) + ((c & 3) << 2)) = q;
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        row_scale[m] = quant_factor(ssd, K, P.eps, amax, norm) / P.w_scale;
-        row_sum[m] = sum;
-      }
+      sq[i * kWave + lane] = s2;
+      a = wave_max(a);
+      if (lane == 0) unit_max[i] = a;
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    rs = row_sum[xrow];
+    auto row_max = [&](int m) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < NSB; ++j) a = fmaxf(a, unit_max[m * NSB + j]);
+      return a;
+    };
+    for (int m = wave; m < M; m += 4) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < NSB; ++j) ss += sq[(m * NSB + j) * kWave + lane];
+      const double ssd = wave_sum(static_cast<double>(ss));
+      const float amax = row_max(m);
+      if (lane == 0) row_scale[m] = quant_factor(ssd, K, P.eps, amax, norm) / P.w_scale;
+    }
+    for (int i = wave; i < units; i += 4) {
+      const int m = i / NSB, c = lane + kWave * (i - m * NSB);  // dword c of the padded row
+      const float amax = row_max(m);
+      int sum = 0;
+      uint32_t q = 0u;
+      if (c < nch) {
+        const f4 xv = xf[m * nch + c];
+        q = codes4(norm ? xv * nwc(c) : xv, amax, &sum);
+      }
+      *reinterpret_cast<uint32_t*>(xlds + m * kpad + ((((c >> 2) ^ (m & 7))) << 4) + ((c & 3) << 2)) = q;
+      sum = wave_sum(sum);
+      if (lane == 0) unit_sum[i] = sum;
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    rs = 0;
+#pragma unroll
+    for (int j = 0; j < NSB; ++j) rs += unit_sum[xrow * NSB + j];
     scale = row_scale[xrow];
   }
 
@@ -367,18 +382,22 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit, const i
     for (int t = 0; t < T; ++t) {
       // The activation fragments are re-read from LDS for every tile rather
       // than held in registers: registers are worth more as load buffers.
+      // Tiles from tpu on hold no rows: their products are skipped (a
+      // uniform branch; the merged launch has tpu == T and none).
       asm volatile("" ::: "memory");
+      if (t < tpu) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) acc[t & 1][f] = v4i{0, 0, 0, 0};
+        for (int f = 0; f < 4; ++f) acc[t & 1][f] = v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int sb = 0; sb < kHeld; ++sb) process(acc[t & 1], buf[t % D][sb], sb);
+        for (int sb = 0; sb < kHeld; ++sb) process(acc[t & 1], buf[t % D][sb], sb);
+      }
       if (t + D < T) {
 #pragma unroll
         for (int sb = 0; sb < kHeld; ++sb) buf[t % D][sb] = wload(t + D, sb);
       }
-      if (t > 0) finish(t - 1);
+      if (t > 0 && t - 1 < tpu) finish(t - 1);
     }
-    finish(T - 1);
+    if (T - 1 < tpu) finish(T - 1);
     // Fused: the fp32 rows and the norm weight are dead since the
     // quantization barrier, so the workgroup's results are gathered there
     // (row m of the workgroup's 64*T output columns at m*64*T) and written
@@ -425,15 +444,19 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit, const i
   }
 }
 
-// The launch covers the by-value problem in `single` (units == nullptr) or
-// the FatUnit table `units`.
-// tiles: 16-row tiles per wave, 0 = the bucket's full count.
-template <bool RAW, bool FROM_LDS, int NSB, bool FUSED, bool GLUE>
+// SINGLE: the launch covers the by-value problem `single`, `tiles` 16-row
+// tiles per wave (1..T).  Else the FatUnit table `units`, the full T tiles
+// per wave (a compile-time count: no tile branches).
+template <bool RAW, bool FROM_LDS, int NSB, bool FUSED, bool GLUE, bool SINGLE>
 __global__ __launch_bounds__(256) void gemv_kernel(Prob single, const FatUnit* units, int tiles) {
-  int unit = blockIdx.x;
-  const Prob P = units ? fat_unit_at(units, blockIdx.x, &unit) : single;
   constexpr int T = gemv_tiles(NSB);
-  gemv_body<RAW, FROM_LDS, NSB, FUSED, GLUE>(P, unit, tiles > 0 && tiles < T ? tiles : T);
+  if (SINGLE) {
+    gemv_body<RAW, FROM_LDS, NSB, FUSED, GLUE>(single, blockIdx.x, tiles > 0 && tiles < T ? tiles : T);
+  } else {
+    int unit;
+    const Prob P = fat_unit_at(units, blockIdx.x, &unit);
+    gemv_body<RAW, FROM_LDS, NSB, FUSED, GLUE>(P, unit, T);
+  }
 }
 
 // Fused decode units of several superblock counts (1..kGemvMergedMaxNsb) in
@@ -486,13 +509,13 @@ size_t gemv_lds_bytes(int bucket, int max_m, int max_k) {
   return (bytes + 1023) / 1024 * 1024;
 }
 
-template <bool RAW, bool LDS, bool FUSED, bool GLUE = false>
+template <bool RAW, bool LDS, bool FUSED, bool GLUE, bool SINGLE>
 hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStream_t stream) {
   const dim3 grid(L.total), block(256);
 #define BL_GEMV_CASE(n)                                                                           \
   case n:                                                                                         \
-    hipLaunchKernelGGL((gemv_kernel<RAW, LDS, n, FUSED, GLUE>), grid, block, shmem, stream,       \
-                       L.single, L.units, L.tiles);                                               \
+    hipLaunchKernelGGL((gemv_kernel<RAW, LDS, n, FUSED, GLUE, SINGLE>), grid, block, shmem,       \
+                       stream, L.single, L.units, L.tiles);                                       \
     break;
   switch (bucket) {
     BL_GEMV_CASE(1) BL_GEMV_CASE(2) BL_GEMV_CASE(3) BL_GEMV_CASE(4) BL_GEMV_CASE(5)
@@ -501,8 +524,8 @@ hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStrea
     BL_GEMV_CASE(16)
     default:
       if constexpr (!FUSED)
-        hipLaunchKernelGGL((gemv_kernel<RAW, LDS, 0, false, false>), grid, block, shmem, stream,
-                           L.single, L.units, 0);
+        hipLaunchKernelGGL((gemv_kernel<RAW, LDS, 0, false, false, SINGLE>), grid, block, shmem,
+                           stream, L.single, L.units, 0);
       else
         return hipErrorInvalidValue;
   }
@@ -531,20 +554,27 @@ hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int ma
 hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,
                        bool fused, hipStream_t stream, bool glue) {
   if (L.total <= 0) return hipSuccess;
+  const bool single = L.units == nullptr;
+  // Tables (groups) carry forward problems without the glue only.
+  if (!single && (raw || glue)) return hipErrorInvalidValue;
   if (fused) {
     if (raw || bucket <= 0) return hipErrorInvalidValue;
     const size_t shmem = fused_lds(max_m, max_k, bucket, glue).bytes;
-    return glue ? launch_bucket<false, true, true, true>(L, bucket, shmem, stream)
-                : launch_bucket<false, true, true>(L, bucket, shmem, stream);
+    if (glue) return launch_bucket<false, true, true, true, true>(L, bucket, shmem, stream);
+    return single ? launch_bucket<false, true, true, false, true>(L, bucket, shmem, stream)
+                  : launch_bucket<false, true, true, false, false>(L, bucket, shmem, stream);
   }
   const size_t shmem = gemv_lds_bytes(bucket, max_m, max_k);
   const bool lds = shmem <= static_cast<size_t>(kGemvLdsBytes);
   if (raw) {
-    return lds ? launch_bucket<true, true, false>(L, bucket, shmem, stream)
-               : launch_bucket<true, false, false>(L, bucket, 0, stream);
+    return lds ? launch_bucket<true, true, false, false, true>(L, bucket, shmem, stream)
+               : launch_bucket<true, false, false, false, true>(L, bucket, 0, stream);
   }
-  return lds ? launch_bucket<false, true, false>(L, bucket, shmem, stream)
-             : launch_bucket<false, false, false>(L, bucket, 0, stream);
+  if (single)
+    return lds ? launch_bucket<false, true, false, false, true>(L, bucket, shmem, stream)
+               : launch_bucket<false, false, false, false, true>(L, bucket, 0, stream);
+  return lds ? launch_bucket<false, true, false, false, false>(L, bucket, shmem, stream)
+             : launch_bucket<false, false, false, false, false>(L, bucket, 0, stream);
 }
 
 }  // namespace bl
