@@ -228,8 +228,10 @@ bl_status bitlinear_glu_forward_nwf16(const float* gate, const float* up, int32_
  * Descriptors with the same x (pointer, M, K and eps), such as the q, k and v
  * of a layer or gate and up, share one pass over x in the quantization launch:
  * the input is read once, and each gets its own codes from its own norm_w.
- * Results are bit-identical to separate bitlinear_forward calls on the same
- * inputs.
+ * Descriptors with up set (the FFN glue) are never shared; they are
+ * quantized by glue launches, or fused into decode launches of their own.
+ * Results are bit-identical to separate bitlinear_forward (with up:
+ * bitlinear_glu_forward) calls on the same inputs.
  */
 
 /* Kinds of launch reported by the per-launch calls below. */
@@ -240,6 +242,9 @@ bl_status bitlinear_glu_forward_nwf16(const float* gate, const float* up, int32_
                                     launch (M <= 16 with on-chip staging) */
 #define BL_LAUNCH_QUANT_SHARED 4 /* RMSNorm + int8 quantization of descriptors that
                                     share their x, one pass over x per set */
+#define BL_LAUNCH_QUANT_GLUE 5   /* FFN glue + RMSNorm + int8 quantization of unfused
+                                    descriptors with up set (one activation per launch) */
+#define BL_LAUNCH_DECODE_FUSED_GLUE 6 /* BL_LAUNCH_DECODE_FUSED for descriptors with up set */
 typedef struct bl_desc {
     const float* x;          /* device [M][K] */
     const void* norm_w;      /* device [K] float32 (float16 if norm_w_f16), or NULL: no norm */
@@ -250,6 +255,11 @@ typedef struct bl_desc {
     float* y;                /* device [M][N] */
     int32_t norm_w_f16;      /* 0: norm_w is float32; 1: IEEE binary16; other values are
                                 BL_ERR_INVALID_ARGUMENT */
+    const float* up;         /* NULL: the input is x.  Else the FFN glue, as in
+                                bitlinear_glu_forward: device [M][K] float32, 16-byte
+                                aligned, and the input is act(x) * up with x the gate */
+    int32_t act;             /* with up: BL_ACT_SILU or BL_ACT_GELU_TANH, other values are
+                                BL_ERR_INVALID_ARGUMENT; ignored without up */
 } bl_desc;
 
 typedef struct bl_group bl_group;
@@ -279,7 +289,8 @@ bl_status bl_group_forward(bl_group* g, void* stream);
  * into the group's workspace (a no-op when every descriptor is fused): one
  * launch per register-resident chunk count ceil(K/256) class (1, 2, 3, 4, 6,
  * 8, 12, 16 chunks of 256; 0 = rows longer than 4096) and kind (single
- * descriptors, then share sets), in increasing chunk count. */
+ * descriptors, glue descriptors with SiLU, with GELU-tanh, then share sets),
+ * in increasing chunk count. */
 bl_status bl_group_quant(bl_group* g, void* stream);
 /* Stage 2 only: integer product + epilogue for every descriptor, reading the
  * workspace written by the last bl_group_quant on the same stream (fused
@@ -290,14 +301,15 @@ bl_status bl_group_matmul(bl_group* g, void* stream);
  * interleave them, in this order: the unfused decode problems (M <= 16) with
  * more than 16 superblocks (bucket 0); the merged fused decode launch of up
  * to 12 superblocks (kind BL_LAUNCH_DECODE_FUSED, bucket 0); then one launch
- * per superblock count ceil(K/256) and kind (unfused before fused), in
- * increasing superblock count; then all prefill problems (M > 16) as one
- * launch.
+ * per superblock count ceil(K/256) and kind (unfused, fused, fused with the
+ * glue), in increasing superblock count; then all prefill problems (M > 16)
+ * as one launch.
  * bl_group_matmul == every launch in order.
  *   bl_group_matmul_launches: number of launches (>= 0; -1 for a NULL group).
- *   bl_group_matmul_launch_info: kind BL_LAUNCH_DECODE or
- *     BL_LAUNCH_DECODE_FUSED (bucket = its superblock count, 0 for
- *     K > 4096) or BL_LAUNCH_PREFILL (bucket = 0); count = problems in the
+ *   bl_group_matmul_launch_info: kind BL_LAUNCH_DECODE,
+ *     BL_LAUNCH_DECODE_FUSED or BL_LAUNCH_DECODE_FUSED_GLUE (bucket = its
+ *     superblock count, 0 for K > 4096 and for the merged launch) or
+ *     BL_LAUNCH_PREFILL (bucket = 0); count = problems in the
  *     launch.  Null outputs are skipped.
  *   bl_group_matmul_launch: enqueue launch i (0-based) on stream. */
 int32_t bl_group_matmul_launches(const bl_group* g);
@@ -305,8 +317,9 @@ bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kin
                                       int32_t* count);
 bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream);
 /* The whole forward as individual launches: first the quantization launches
- * of bl_group_quant (kind BL_LAUNCH_QUANT or BL_LAUNCH_QUANT_SHARED, bucket =
- * the chunk count, count = descriptors quantized), then the matmul launches.
+ * of bl_group_quant (kind BL_LAUNCH_QUANT, BL_LAUNCH_QUANT_GLUE or
+ * BL_LAUNCH_QUANT_SHARED, bucket = the chunk count, count = descriptors
+ * quantized), then the matmul launches.
  * bl_group_forward == every forward launch in order.
  *   bl_group_forward_launches: number of launches (-1 for a NULL group). */
 int32_t bl_group_forward_launches(const bl_group* g);

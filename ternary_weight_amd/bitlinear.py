@@ -33,13 +33,15 @@ BL_ERR_INTERNAL = -7
 _p, _i64, _f32, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32
 
 # BL_LAUNCH_* of include/bitlinear.h
-LAUNCH_KINDS = {0: "decode", 1: "prefill", 2: "quant", 3: "decode_fused", 4: "quant_shared"}
+LAUNCH_KINDS = {0: "decode", 1: "prefill", 2: "quant", 3: "decode_fused", 4: "quant_shared",
+                5: "quant_glue", 6: "decode_fused_glue"}
 
 
 class BlDesc(ctypes.Structure):
     """Mirror of ``bl_desc``."""
     _fields_ = [("x", _p), ("norm_w", _p), ("packed_w", _p), ("w_scale", _f32), ("eps", _f32),
-                ("M", _i64), ("K", _i64), ("N", _i64), ("y", _p), ("norm_w_f16", _i32)]
+                ("M", _i64), ("K", _i64), ("N", _i64), ("y", _p), ("norm_w_f16", _i32),
+                ("up", _p), ("act", _i32)]
 
 
 _SIGS = {
@@ -228,8 +230,10 @@ class Group:
 
     ``items`` is a sequence of dicts with keys x, norm_w, packed_w, w_scale,
     eps, N and y (torch tensors on the GPU where applicable; norm_w float32 or
-    float16, None or absent: no per-projection norm).  The tensors are
-    kept referenced for the group's lifetime.
+    float16, None or absent: no per-projection norm), and optionally up and
+    act: the FFN glue, the input is then act(x) * up with x the gate (act
+    ACT_SILU or ACT_GELU_TANH).  The tensors are kept referenced for the
+    group's lifetime.
     """
 
     def __init__(self, items):
@@ -240,10 +244,13 @@ class Group:
             x, y = it["x"], it["y"]
             M, K = x.shape
             nw, f16 = _norm(it.get("norm_w"), K)
+            up = it.get("up")
             descs[i] = BlDesc(_dev(x, torch.float32, "x"), nw,
                               _dev(it["packed_w"], torch.uint8, "packed_w"),
                               float(it["w_scale"]), float(it["eps"]), M, K, int(it["N"]),
-                              _dev(y, torch.float32, "y", (M, int(it["N"]))), int(f16))
+                              _dev(y, torch.float32, "y", (M, int(it["N"]))), int(f16),
+                              None if up is None else _dev(up, torch.float32, "up", (M, K)),
+                              int(it.get("act", ACT_SILU)) if up is not None else 0)
             self._keep.append(it)
         handle = _p()
         _check(_lib.bl_group_create(descs, len(items), ctypes.byref(handle)), "bl_group_create")

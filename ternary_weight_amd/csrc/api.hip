@@ -9,6 +9,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <new>
 #include <utility>
 #include <vector>
@@ -435,6 +436,8 @@ struct GroupStage {
   bool merged = false; // fused decode stage of several superblock counts (one launch)
   bool shared = false; // quantization stages: every unit heads a share set
   int chunks = 0;      // quantization stages: float4 chunks per lane (0: streaming)
+  int act = kActNone;  // quantization stages: the FFN glue of every problem (kActNone: none)
+  bool glue = false;   // decode stages: fused with the FFN glue (Prob::act per problem)
 };
 
 // Fused decode launches depend on nothing but the caller's earlier work, so
@@ -542,12 +545,15 @@ struct StageHost {
 // quantizes the rows for every problem of the set.  Sets of two or more go
 // to launches of the shared kernel variant, single problems to the plain
 // one, each by the register-resident chunk count of their K.  Sets keep the
-// order of their first problem.
+// order of their first problem.  Glue problems (act(x) * up) never share;
+// they go to launches of their own per activation.
 struct QuantKey {
   int chunks;
   bool shared;
+  int act;
   bool operator<(const QuantKey& o) const {
-    return chunks != o.chunks ? chunks < o.chunks : shared < o.shared;
+    if (chunks != o.chunks) return chunks < o.chunks;
+    return shared != o.shared ? shared < o.shared : act < o.act;
   }
 };
 
@@ -558,7 +564,9 @@ std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs)
     int found = -1;
     for (size_t j = 0; j < sets.size() && found < 0; ++j) {
       const Prob& q = probs[sets[j][0]];
-      if (q.x == p.x && q.M == p.M && q.K == p.K && q.eps == p.eps) found = static_cast<int>(j);
+      if (p.act == kActNone && q.act == kActNone && q.x == p.x && q.M == p.M && q.K == p.K &&
+          q.eps == p.eps)
+        found = static_cast<int>(j);
     }
     if (found < 0) {
       found = static_cast<int>(sets.size());
@@ -582,7 +590,7 @@ std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs)
   for (const auto& set : parts) {
     const Prob& lead = probs[set[0]];
     const int nc = quant_chunks(lead.K);
-    StageHost& h = out[QuantKey{nc, set.size() > 1}];
+    StageHost& h = out[QuantKey{nc, set.size() > 1, lead.act}];
     const int first = static_cast<int>(h.probs.size());
     for (size_t k = 0; k < set.size(); ++k) {
       Prob p = probs[set[k]];
@@ -660,12 +668,17 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       const bl_desc& d = descs[i];
       bl_status st = check_forward(d.x, d.norm_w, d.packed_w, d.w_scale, d.M, d.K, d.N, d.eps, d.y);
       if (st == BL_OK && d.norm_w_f16 != 0 && d.norm_w_f16 != 1) st = BL_ERR_INVALID_ARGUMENT;
+      if (st == BL_OK && d.up && d.act != BL_ACT_SILU && d.act != BL_ACT_GELU_TANH)
+        st = BL_ERR_INVALID_ARGUMENT;
+      if (st == BL_OK && d.M > 0 && d.up && !aligned16(d.up)) st = BL_ERR_MISALIGNED;
       if (st != BL_OK) return st;
       if (d.M == 0) continue;
       if (d.M <= kGemvMaxM)
         units_v += gemv_units(static_cast<int>(d.N), gemv_bucket(static_cast<int>(d.K)));
       else units_m += gemm_units(static_cast<int>(d.M), static_cast<int>(d.N));
-      if (d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K))) continue;
+      if (d.M <= kGemvMaxM &&
+          gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), d.up != nullptr))
+        continue;
       units_q += quant_units(static_cast<int>(d.M));
       ws_bytes += ws_layout(d.M, d.K).bytes;
     }
@@ -686,17 +699,24 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
 
     std::vector<Prob> qprobs;
     StageHost hm;
-    // Decode problems by (bucket, fused); fused ones of up to kGemvMergedMaxNsb
-    // superblocks share one merged launch, keyed (0, true).
-    std::map<std::pair<int, bool>, StageHost> hv;
+    // Decode problems by (bucket, fused, glue); fused ones of up to
+    // kGemvMergedMaxNsb superblocks without the glue share one merged launch,
+    // keyed (0, true, false).
+    std::map<std::tuple<int, bool, bool>, StageHost> hv;
     uint8_t* ws = static_cast<uint8_t*>(g->workspace);
     size_t off = 0;
     for (int32_t i = 0; i < count; ++i) {
       const bl_desc& d = descs[i];
       if (d.M == 0) continue;
-      const bool fused = d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K));
+      const bool glue = d.up != nullptr;
+      const bool fused =
+          d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), glue);
       Prob p{};
       p.x = d.x;
+      if (glue) {
+        p.up = d.up;
+        p.act = d.act == BL_ACT_SILU ? kActSilu : kActGeluTanh;
+      }
       p.norm_w = static_cast<const float*>(d.norm_w);
       p.nw_f16 = d.norm_w_f16;
       p.w = d.packed_w;
@@ -717,8 +737,9 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       if (!fused) qprobs.push_back(p);
       if (p.M <= kGemvMaxM) {
         const int b = gemv_bucket(p.K);
-        const bool merge = fused && b >= 1 && b <= kGemvMergedMaxNsb;
-        StageHost& sh = hv[{merge ? 0 : b, fused}];
+        const bool merge = fused && !glue && b >= 1 && b <= kGemvMergedMaxNsb;
+        // (unfused glue problems read their codes like any other: plain stages)
+        StageHost& sh = hv[{merge ? 0 : b, fused, fused && glue}];
         sh.fat = true;
         sh.add(p, gemv_units(p.N, b), merge ? b : 0);
       }
@@ -726,7 +747,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
     }
     std::map<QuantKey, StageHost> hqs = build_quant_stages(qprobs);
     {
-      auto it = hv.find({0, true});
+      auto it = hv.find({0, true, false});
       if (it != hv.end()) order_merged_units(it->second.fat_units);
     }
     interleave_gemm_units(hm);
@@ -740,15 +761,17 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
     for (auto& kv : hqs) {
       g->quant[qi].shared = kv.first.shared;
       g->quant[qi].chunks = kv.first.chunks;
+      g->quant[qi].act = kv.first.act;
       hosts.push_back(&kv.second);
       stages.push_back(&g->quant[qi]);
       ++qi;
     }
     size_t bi = 0;
     for (auto& kv : hv) {
-      g->gemv[bi].first = kv.first.first;
-      g->gemv[bi].second.fused = kv.first.second;
-      g->gemv[bi].second.merged = kv.first.first == 0 && kv.first.second;
+      g->gemv[bi].first = std::get<0>(kv.first);
+      g->gemv[bi].second.fused = std::get<1>(kv.first);
+      g->gemv[bi].second.glue = std::get<2>(kv.first);
+      g->gemv[bi].second.merged = std::get<0>(kv.first) == 0 && std::get<1>(kv.first);
       hosts.push_back(&kv.second);
       stages.push_back(&g->gemv[bi].second);
       ++bi;
@@ -818,7 +841,7 @@ namespace {
 
 bl_status quant_launch(bl_group* g, size_t i, hipStream_t s) {
   const GroupStage& q = g->quant[i];
-  return from_hip(launch_quant(stage_set(q), q.max_k, q.shared, kActNone, s));
+  return from_hip(launch_quant(stage_set(q), q.max_k, q.shared, q.act, s));
 }
 
 }  // namespace
@@ -846,9 +869,13 @@ bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kin
                                       int32_t* count) {
   if (!g || i < 0 || i >= bl_group_matmul_launches(g)) return BL_ERR_INVALID_ARGUMENT;
   const bool decode = i < static_cast<int32_t>(g->gemv.size());
-  if (kind)
-    *kind = decode ? (g->gemv[i].second.fused ? BL_LAUNCH_DECODE_FUSED : BL_LAUNCH_DECODE)
-                   : BL_LAUNCH_PREFILL;
+  if (kind) {
+    const GroupStage* st = decode ? &g->gemv[i].second : nullptr;
+    *kind = !decode ? BL_LAUNCH_PREFILL
+                    : (!st->fused ? BL_LAUNCH_DECODE
+                                  : (st->glue ? BL_LAUNCH_DECODE_FUSED_GLUE
+                                                         : BL_LAUNCH_DECODE_FUSED));
+  }
   if (bucket) *bucket = decode ? g->gemv[i].first : 0;
   if (count) *count = decode ? g->gemv[i].second.count : g->gemm.count;
   return BL_OK;
@@ -866,7 +893,8 @@ bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream) {
       GemvLaunch L{};
       L.units = gs.fat;
       L.total = gs.total;
-      return from_hip(launch_gemv(L, false, g->gemv[i].first, gs.max_m, gs.max_k, gs.fused, s));
+      return from_hip(launch_gemv(L, false, g->gemv[i].first, gs.max_m, gs.max_k, gs.fused, s,
+                                  gs.glue));
     }
     return from_hip(launch_gemm(stage_set(g->gemm), false, s));
   } catch (...) {
@@ -941,7 +969,9 @@ bl_status bl_group_forward_launch_info(const bl_group* g, int32_t i, int32_t* ki
   if (!g || i < 0 || i >= bl_group_forward_launches(g)) return BL_ERR_INVALID_ARGUMENT;
   const int32_t q = static_cast<int32_t>(g->quant.size());
   if (i >= q) return bl_group_matmul_launch_info(g, i - q, kind, bucket, count);
-  if (kind) *kind = g->quant[i].shared ? BL_LAUNCH_QUANT_SHARED : BL_LAUNCH_QUANT;
+  if (kind)
+    *kind = g->quant[i].shared ? BL_LAUNCH_QUANT_SHARED
+                               : (g->quant[i].act != kActNone ? BL_LAUNCH_QUANT_GLUE : BL_LAUNCH_QUANT);
   if (bucket) *bucket = g->quant[i].chunks;
   if (count) *count = g->quant[i].count;
   return BL_OK;

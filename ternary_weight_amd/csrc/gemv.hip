@@ -555,12 +555,14 @@ hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int
                        bool fused, hipStream_t stream, bool glue) {
   if (L.total <= 0) return hipSuccess;
   const bool single = L.units == nullptr;
-  // Tables (groups) carry forward problems without the glue only.
-  if (!single && (raw || glue)) return hipErrorInvalidValue;
+  // Tables (groups) carry forward problems only; the glue is fused only.
+  if ((!single && raw) || (glue && !fused)) return hipErrorInvalidValue;
   if (fused) {
     if (raw || bucket <= 0) return hipErrorInvalidValue;
     const size_t shmem = fused_lds(max_m, max_k, bucket, glue).bytes;
-    if (glue) return launch_bucket<false, true, true, true, true>(L, bucket, shmem, stream);
+    if (glue)
+      return single ? launch_bucket<false, true, true, true, true>(L, bucket, shmem, stream)
+                    : launch_bucket<false, true, true, true, false>(L, bucket, shmem, stream);
     return single ? launch_bucket<false, true, true, false, true>(L, bucket, shmem, stream)
                   : launch_bucket<false, true, true, false, false>(L, bucket, shmem, stream);
   }

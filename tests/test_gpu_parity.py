@@ -677,6 +677,51 @@ def test_glu_forward_parity_and_hooks(act, M, K, N):
     assert torch.equal(y, y2)
 
 
+def test_group_ffn_glue_descriptors():
+    # Glue descriptors in a group beside plain ones: fused decode with the glue
+    # (M = 1, K = 3072, SiLU; M = 2, K = 2048, GELU-tanh), unfused decode
+    # (M = 8), prefill (M = 300), a fused plain M = 1 problem and a plain pair
+    # sharing its input.  Every output equals its single call bit for bit.
+    nan = float("nan")
+    items, singles = [], []
+    for i, (act, M, K, N) in enumerate([(bl.ACT_SILU, 1, 3072, 1024), (bl.ACT_GELU_TANH, 2, 2048, 640),
+                                        (bl.ACT_SILU, 8, 2048, 640), (bl.ACT_GELU_TANH, 300, 3072, 200)]):
+        gate, up, nw, packed, scale = glu_inputs(act, M, K, N, seed=20 + i)
+        it = dict(x=dev(gate), up=dev(up), act=act, norm_w=dev(nw), packed_w=dev(packed), w_scale=scale,
+                  eps=EPS, N=N, y=torch.full((M, N), nan, device=DEV))
+        items.append(it)
+        singles.append(bl.bitlinear_glu_forward(it["x"], it["up"], act, it["norm_w"], it["packed_w"],
+                                                scale, N, EPS))
+        if M in (2, 300):
+            ref = oracle.glu_bitlinear(gate, up, act, nw, packed, N, EPS)
+            assert rel_l2(host(singles[-1]), ref) <= 1e-3
+    x1, nw1, p1, s1 = proj_inputs(21, 0, 0, 1, 1024, 256)
+    x3, nw3, p3, s3 = proj_inputs(21, 1, 0, 300, 1024, 128)
+    _, nw4, p4, s4 = proj_inputs(21, 1, 1, 300, 1024, 96)
+    dx3 = dev(x3)
+    for x, nw, packed, scale, N in ((dev(x1), nw1, p1, s1, 256), (dx3, nw3, p3, s3, 128), (dx3, nw4, p4, s4, 96)):
+        it = dict(x=x, norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                  y=torch.full((x.shape[0], N), nan, device=DEV))
+        items.append(it)
+        singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, N, EPS))
+    with bl.Group(items) as g:
+        g.forward()
+        torch.cuda.synchronize()
+        for i, (it, ys) in enumerate(zip(items, singles)):
+            assert torch.equal(it["y"], ys), i
+        info = g.forward_launches()
+        assert [d["kind"] for d in info] == ["quant_shared", "quant_glue", "quant_glue", "decode_fused",
+                                            "decode", "decode_fused_glue", "decode_fused_glue", "prefill"]
+        assert [d["bucket"] for d in info] == [4, 8, 12, 0, 8, 8, 12, 0]
+        for it in items:
+            it["y"].fill_(nan)
+        for i in range(len(info)):
+            g.forward_launch(i)
+        torch.cuda.synchronize()
+        for i, (it, ys) in enumerate(zip(items, singles)):
+            assert torch.equal(it["y"], ys), i
+
+
 def test_glu_forward_qwen_down_full_size_sampled_rows():
     # The Qwen3 FFN down projection at the long-context size (M = 32768,
     # K = 3072 -> N = 1024, SiLU), checked on sampled rows.

@@ -207,6 +207,12 @@ def test_group_validation():
     assert not h.value
     d[1] = bl.BlDesc(A, A, MIS, 1.0, 1e-6, 4, 128, 8, A)
     assert lib.bl_group_create(d, 2, ctypes.byref(h)) == bl.BL_ERR_MISALIGNED
+    # FFN glue descriptors: a known activation with up, up 16-byte aligned
+    d[1] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, A, 0, A, 7)
+    assert lib.bl_group_create(d, 2, ctypes.byref(h)) == bl.BL_ERR_INVALID_ARGUMENT
+    d[1] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, A, 0, MIS, bl.ACT_GELU_TANH)
+    assert lib.bl_group_create(d, 2, ctypes.byref(h)) == bl.BL_ERR_MISALIGNED
+    assert not h.value
     assert lib.bl_group_create(d, 0, ctypes.byref(h)) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_group_create(d, 2, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_group_forward(None, None) == bl.BL_ERR_INVALID_ARGUMENT
