@@ -172,7 +172,7 @@ bl_status forward_impl(const float* x, const void* norm_w, bool nw_f16, const ui
     p.M = static_cast<int>(M);
     p.K = static_cast<int>(K);
     p.N = static_cast<int>(N);
-    if (gemv_fusable(p.M, p.K, false, true)) return from_hip(launch_matmul_single(p, false, true, s));
+    if (gemv_fusable(p.M, p.K)) return from_hip(launch_matmul_single(p, false, true, s));
     const WsLayout l = ws_layout(M, K);
     uint8_t* ws = nullptr;
     if ((st = acquire_ws(s, l.bytes, &ws)) != BL_OK) return st;
@@ -309,7 +309,7 @@ bl_status glu_forward_impl(const float* gate, const float* up, int32_t act, cons
     p.K = static_cast<int>(K);
     p.N = static_cast<int>(N);
     // Decode sizes whose gate and up rows fit on chip: one launch, no workspace.
-    if (gemv_fusable(p.M, p.K, true, true)) return from_hip(launch_matmul_single(p, false, true, s));
+    if (gemv_fusable(p.M, p.K, true)) return from_hip(launch_matmul_single(p, false, true, s));
     const WsLayout l = ws_layout(M, K);
     uint8_t* ws = nullptr;
     if ((st = acquire_ws(s, l.bytes, &ws)) != BL_OK) return st;
@@ -677,7 +677,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
         units_v += gemv_units(static_cast<int>(d.N), gemv_bucket(static_cast<int>(d.K)));
       else units_m += gemm_units(static_cast<int>(d.M), static_cast<int>(d.N));
       if (d.M <= kGemvMaxM &&
-          gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), d.up != nullptr, false))
+          gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), d.up != nullptr))
         continue;
       units_q += quant_units(static_cast<int>(d.M));
       ws_bytes += ws_layout(d.M, d.K).bytes;
@@ -710,7 +710,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       if (d.M == 0) continue;
       const bool glue = d.up != nullptr;
       const bool fused =
-          d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), glue, false);
+          d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), glue);
       Prob p{};
       p.x = d.x;
       if (glue) {

@@ -53,9 +53,6 @@ constexpr int kGemvLdsBytes = 64 * 1024;   // activation staging limit per workg
 constexpr int kMaxNsb = 16;                // specialised superblock counts 1..16
 constexpr int kGemvFusedLdsBytes = 40 * 1024;  // fused-variant staging limit per workgroup
 constexpr int kGemvGlueLdsBytes = 56 * 1024;   // the same with the FFN glue's up rows staged too
-// Single-problem launches are latency-bound (a few dozen workgroups), so they
-// may stage more: occupancy does not matter there.
-constexpr int kGemvSingleLdsBytes = 64 * 1024;
 
 // LDS layout of the fused variant (byte offsets): the staged codes (M rows of
 // nsb superblocks) at 0, a table (epilogue scale of up to 16 rows, then the
@@ -538,10 +535,10 @@ hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStrea
 
 }  // namespace
 
-bool gemv_fusable(int M, int K, bool glue, bool single) {
+bool gemv_fusable(int M, int K, bool glue) {
   const int b = gemv_bucket(K);
-  const int budget = single ? kGemvSingleLdsBytes : (glue ? kGemvGlueLdsBytes : kGemvFusedLdsBytes);
-  return M >= 1 && M <= kGemvMaxM && b > 0 && fused_lds(M, K, b, glue).bytes <= budget;
+  return M >= 1 && M <= kGemvMaxM && b > 0 &&
+         fused_lds(M, K, b, glue).bytes <= (glue ? kGemvGlueLdsBytes : kGemvFusedLdsBytes);
 }
 
 hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int max_k,

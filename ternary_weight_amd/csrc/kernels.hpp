@@ -57,17 +57,16 @@ hipError_t launch_rowsum(const Prob& p, hipStream_t stream);
 // staging).  fused: the kernel also runs stage 1 for its rows (RMSNorm +
 // int8 quantization from x and norm_w, same arithmetic as launch_quant), so
 // no quantization launch and no workspace are needed; only for problems
-// with gemv_fusable(M, K, glue, single) and the forward epilogue.  glue: the
+// with gemv_fusable(M, K, glue) and the forward epilogue.  glue: the
 // problems' input is the FFN glue act(x) * up (Prob::act, Prob::up), which
-// the fused kernel forms in LDS.  single: a launch of this one problem (a
-// larger staging budget than a table launch, whose occupancy matters).
+// the fused kernel forms in LDS.
 struct GemvLaunch {
   Prob single;
   const FatUnit* units;
   int total;
   int tiles;  // 16-row tiles per wave, 0 = the bucket's full count
 };
-bool gemv_fusable(int M, int K, bool glue, bool single);
+bool gemv_fusable(int M, int K, bool glue = false);
 // Fused decode problems of up to kGemvMergedMaxNsb superblocks in one launch
 // over a FatUnit table whose records carry each unit's superblock count
 // (FatUnit::nsb), longest first.  max_m, max_k: the largest M and K.
