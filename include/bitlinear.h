@@ -133,11 +133,11 @@ bl_status i2s_pack_device(const float* w, int64_t K, int64_t N, uint8_t* packed,
  * in the codes), factor = max|RMSNorm(x)*norm_w| / 127, an all-zero row gives
  * zero codes and factor 0; y = (sum_k code*ternary) * factor / w_scale.
  * M <= 16 takes the weight-streaming decode kernel, larger M the tiled MFMA
- * kernel; both share the same integer result.  When the decode kernel can
- * stage the fp32 rows on chip (about M*(4*K + 2*256*ceil(K/256)) + 4*K bytes,
- * each part rounded up to 1 KB, plus a 1-3 KB table, within its 40 KB budget;
- * K <= 4096), the quantization runs inside it: one launch, no workspace,
- * results bit-identical to the two-stage path.
+ * kernel; both share the same integer result.  For M <= 3 when the decode
+ * kernel can stage the fp32 rows on chip (about M*(4*K + 2*256*ceil(K/256)) +
+ * 4*K bytes, each part rounded up to 1 KB, plus a 1-3 KB table, within its
+ * 40 KB budget; K <= 4096), the quantization runs inside it: one launch, no
+ * workspace, results bit-identical to the two-stage path.
  * Otherwise the codes go through a library-owned workspace (M*K + 8*M bytes)
  * per (device, stream); the workspace is grown with hipMalloc when needed,
  * which is not allowed while the stream is being captured into a graph
@@ -181,10 +181,10 @@ bl_status bitlinear_matmul_i32(const int8_t* xq, const uint8_t* packed_w, int64_
  * Everything else as in bitlinear_quant and bitlinear_forward (K is the down
  * projection's input width, the FFN size; norm_w its norm weight or NULL); an
  * unknown act is BL_ERR_INVALID_ARGUMENT.  bitlinear_glu_forward returns
- * y = BitLinear_down(act(gate) * up); at decode sizes whose gate and up rows
- * fit on chip (the bitlinear_forward budget with 4*M*K more bytes, within
- * 56 KB) it is one launch with no workspace, bit-identical to the two-stage
- * path; otherwise it uses the library workspace and two launches.
+ * y = BitLinear_down(act(gate) * up); for M <= 3 whose gate and up rows fit
+ * on chip (the bitlinear_forward budget with 4*M*K more bytes, within 56 KB)
+ * it is one launch with no workspace, bit-identical to the two-stage path;
+ * otherwise it uses the library workspace and two launches.
  */
 #define BL_ACT_SILU 0
 #define BL_ACT_GELU_TANH 1

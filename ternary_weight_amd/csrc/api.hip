@@ -172,7 +172,8 @@ bl_status forward_impl(const float* x, const void* norm_w, bool nw_f16, const ui
     p.M = static_cast<int>(M);
     p.K = static_cast<int>(K);
     p.N = static_cast<int>(N);
-    if (gemv_fusable(p.M, p.K)) return from_hip(launch_matmul_single(p, false, true, s));
+    if (p.M <= kGemvSingleFusedMaxM && gemv_fusable(p.M, p.K))
+      return from_hip(launch_matmul_single(p, false, true, s));
     const WsLayout l = ws_layout(M, K);
     uint8_t* ws = nullptr;
     if ((st = acquire_ws(s, l.bytes, &ws)) != BL_OK) return st;
@@ -309,7 +310,8 @@ bl_status glu_forward_impl(const float* gate, const float* up, int32_t act, cons
     p.K = static_cast<int>(K);
     p.N = static_cast<int>(N);
     // Decode sizes whose gate and up rows fit on chip: one launch, no workspace.
-    if (gemv_fusable(p.M, p.K, true)) return from_hip(launch_matmul_single(p, false, true, s));
+    if (p.M <= kGemvSingleFusedMaxM && gemv_fusable(p.M, p.K, true))
+      return from_hip(launch_matmul_single(p, false, true, s));
     const WsLayout l = ws_layout(M, K);
     uint8_t* ws = nullptr;
     if ((st = acquire_ws(s, l.bytes, &ws)) != BL_OK) return st;

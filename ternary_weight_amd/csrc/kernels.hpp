@@ -67,6 +67,12 @@ struct GemvLaunch {
   int tiles;  // 16-row tiles per wave, 0 = the bucket's full count
 };
 bool gemv_fusable(int M, int K, bool glue = false);
+// A single call fuses only up to this many rows: each workgroup stages and
+// quantizes all M rows, about 1 us more per row, while the separate
+// quantization kernel spreads rows over workgroups (measured per call at
+// K = 640..2048: fused wins at M <= 2, breaks even at M = 3, loses from 4).
+// Groups fuse by staging budget alone (many workgroups hide it).
+constexpr int kGemvSingleFusedMaxM = 3;
 // Fused decode problems of up to kGemvMergedMaxNsb superblocks in one launch
 // over a FatUnit table whose records carry each unit's superblock count
 // (FatUnit::nsb), longest first.  max_m, max_k: the largest M and K.
