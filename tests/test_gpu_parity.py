@@ -458,6 +458,44 @@ def test_group_forward_in_cuda_graph():
                 assert torch.equal(it["y"], ys), f"replay {rep}"
 
 
+def test_group_with_glue_in_cuda_graph():
+    # A group with FFN-glue descriptors (fused glue decode, glue quantization
+    # for an unfused decode and a prefill problem) beside a plain fused one,
+    # captured into a graph; every replay equals the single calls bit for bit.
+    nan = float("nan")
+    items, singles = [], []
+    for i, (act, M, K, N) in enumerate([(bl.ACT_SILU, 1, 3072, 1024), (bl.ACT_GELU_TANH, 8, 2048, 640),
+                                        (bl.ACT_SILU, 40, 1024, 160)]):
+        gate, up, nw, packed, scale = glu_inputs(act, M, K, N, seed=30 + i)
+        it = dict(x=dev(gate), up=dev(up), act=act, norm_w=dev(nw), packed_w=dev(packed), w_scale=scale,
+                  eps=EPS, N=N, y=torch.full((M, N), nan, device=DEV))
+        items.append(it)
+        singles.append(bl.bitlinear_glu_forward(it["x"], it["up"], act, it["norm_w"], it["packed_w"],
+                                                scale, N, EPS))
+    x, nw, packed, scale = proj_inputs(31, 0, 0, 1, 1024, 512)
+    it = dict(x=dev(x), norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS, N=512,
+              y=torch.full((1, 512), nan, device=DEV))
+    items.append(it)
+    singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, 512, EPS))
+    with bl.Group(items) as g:
+        kinds = [d["kind"] for d in g.forward_launches()]
+        assert kinds == ["quant_glue", "quant_glue", "decode_fused", "decode", "decode_fused_glue",
+                         "prefill"], kinds
+        g.forward()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            g.forward()
+        for rep in range(3):
+            for it in items:
+                it["y"].fill_(nan)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for i, (it, ys) in enumerate(zip(items, singles)):
+                assert torch.equal(it["y"], ys), (rep, i)
+
+
 # ------------------------------------------------------------ no norm ---
 # A projection without its own norm weight ("BitNet Embeddings GGUF
 # Conversion Implementation", s4.5: the shared input feeds the projection
