@@ -243,6 +243,14 @@ def test_forward_matches_hooks_bitwise(M, K):
     y2 = acc.to(torch.float32) * (f / torch.tensor(scale, dtype=torch.float32, device=DEV))[:, None]
     assert torch.equal(y, y2)
     assert rel_l2(host(y), oracle.bitlinear(x, nw, packed, N, EPS)) <= 1e-3
+    # A group fuses every decode problem whose rows fit on chip (single calls
+    # only up to M = 3): its in-kernel quantization must give the same bits.
+    it = dict(x=dx, norm_w=dn, packed_w=dp, w_scale=scale, eps=EPS, N=N,
+              y=torch.full((M, N), float("nan"), device=DEV))
+    with bl.Group([it]) as g:
+        g.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(it["y"], y2)
 
 
 def test_group_forward_launch_kinds_and_order():
