@@ -440,6 +440,7 @@ struct GroupStage {
   int chunks = 0;      // quantization stages: float4 chunks per lane (0: streaming)
   int act = kActNone;  // quantization stages: the FFN glue of every problem (kActNone: none)
   bool glue = false;   // decode stages: fused with the FFN glue (Prob::act per problem)
+  size_t shmem = 0;    // fused decode stages: LDS bytes, the largest of the problems' own
 };
 
 // Fused decode launches depend on nothing but the caller's earlier work, so
@@ -521,6 +522,7 @@ void order_merged_units(std::vector<FatUnit>& units) {
 // Host image of one stage before upload.
 struct StageHost {
   bool fat = false;
+  size_t shmem = 0;  // fused decode stages: the largest per-problem LDS staging
   std::vector<Prob> probs;
   std::vector<int2> units;
   std::vector<FatUnit> fat_units;
@@ -679,7 +681,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
         units_v += gemv_units(static_cast<int>(d.N), gemv_bucket(static_cast<int>(d.K)));
       else units_m += gemm_units(static_cast<int>(d.M), static_cast<int>(d.N));
       if (d.M <= kGemvMaxM &&
-          gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), d.up != nullptr))
+          gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), d.up != nullptr, true))
         continue;
       units_q += quant_units(static_cast<int>(d.M));
       ws_bytes += ws_layout(d.M, d.K).bytes;
@@ -712,7 +714,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       if (d.M == 0) continue;
       const bool glue = d.up != nullptr;
       const bool fused =
-          d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), glue);
+          d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), glue, true);
       Prob p{};
       p.x = d.x;
       if (glue) {
@@ -744,6 +746,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
         StageHost& sh = hv[{merge ? 0 : b, fused, fused && glue}];
         sh.fat = true;
         sh.add(p, gemv_units(p.N, b), merge ? b : 0);
+        if (fused) sh.shmem = std::max(sh.shmem, gemv_fused_lds_bytes(p.M, p.K, glue));
       }
       else hm.add(p, gemm_units(p.M, p.N));
     }
@@ -817,6 +820,7 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       stages[k]->count = hosts[k]->nprobs;
       stages[k]->max_m = hosts[k]->max_m;
       stages[k]->max_k = hosts[k]->max_k;
+      stages[k]->shmem = hosts[k]->shmem;
     }
     int nfused = 0;
     for (const auto& st : g->gemv) nfused += st.second.fused ? 1 : 0;
@@ -891,10 +895,11 @@ bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (i < static_cast<int32_t>(g->gemv.size())) {
       const GroupStage& gs = g->gemv[i].second;
-      if (gs.merged) return from_hip(launch_gemv_merged(gs.fat, gs.total, gs.max_m, gs.max_k, s));
+      if (gs.merged) return from_hip(launch_gemv_merged(gs.fat, gs.total, gs.shmem, s));
       GemvLaunch L{};
       L.units = gs.fat;
       L.total = gs.total;
+      L.fused_shmem = gs.shmem;
       return from_hip(launch_gemv(L, false, g->gemv[i].first, gs.max_m, gs.max_k, gs.fused, s,
                                   gs.glue));
     }

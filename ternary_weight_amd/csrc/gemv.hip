@@ -51,8 +51,13 @@ namespace bl {
 
 constexpr int kGemvLdsBytes = 64 * 1024;   // activation staging limit per workgroup
 constexpr int kMaxNsb = 16;                // specialised superblock counts 1..16
-constexpr int kGemvFusedLdsBytes = 40 * 1024;  // fused-variant staging limit per workgroup
-constexpr int kGemvGlueLdsBytes = 56 * 1024;   // the same with the FFN glue's up rows staged too
+// Fused-variant staging limits per workgroup: single-problem launches (their
+// time grows with the staging, see kGemvSingleFusedMaxM), table launches (up
+// to 52 KB keeps three workgroups per CU, as many as the merged kernel's
+// registers allow), and either with the FFN glue's up rows staged too.
+constexpr int kGemvFusedLdsBytes = 40 * 1024;
+constexpr int kGemvTableLdsBytes = 52 * 1024;
+constexpr int kGemvGlueLdsBytes = 56 * 1024;
 
 // LDS layout of the fused variant (byte offsets): the staged codes (M rows of
 // nsb superblocks) at 0, a table (epilogue scale of up to 16 rows, then the
@@ -535,19 +540,20 @@ hipError_t launch_bucket(const GemvLaunch& L, int bucket, size_t shmem, hipStrea
 
 }  // namespace
 
-bool gemv_fusable(int M, int K, bool glue) {
+bool gemv_fusable(int M, int K, bool glue, bool table) {
   const int b = gemv_bucket(K);
-  return M >= 1 && M <= kGemvMaxM && b > 0 &&
-         fused_lds(M, K, b, glue).bytes <= (glue ? kGemvGlueLdsBytes : kGemvFusedLdsBytes);
+  const int budget = glue ? kGemvGlueLdsBytes : (table ? kGemvTableLdsBytes : kGemvFusedLdsBytes);
+  return M >= 1 && M <= kGemvMaxM && b > 0 && fused_lds(M, K, b, glue).bytes <= budget;
 }
 
-hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int max_k,
-                              hipStream_t stream) {
+size_t gemv_fused_lds_bytes(int M, int K, bool glue) {
+  return static_cast<size_t>(fused_lds(M, K, gemv_bucket(K), glue).bytes);
+}
+
+hipError_t launch_gemv_merged(const FatUnit* units, int total, size_t shmem, hipStream_t stream) {
   if (total <= 0) return hipSuccess;
-  const int b = gemv_bucket(max_k);
-  if (b <= 0 || b > kGemvMergedMaxNsb) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemv_fused_merged_kernel, dim3(total), dim3(256),
-                     fused_lds(max_m, max_k, b, false).bytes, stream, units);
+  if (shmem == 0 || shmem > static_cast<size_t>(kGemvTableLdsBytes)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemv_fused_merged_kernel, dim3(total), dim3(256), shmem, stream, units);
   return hipGetLastError();
 }
 
@@ -559,7 +565,8 @@ hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int
   if ((!single && raw) || (glue && !fused)) return hipErrorInvalidValue;
   if (fused) {
     if (raw || bucket <= 0) return hipErrorInvalidValue;
-    const size_t shmem = fused_lds(max_m, max_k, bucket, glue).bytes;
+    const size_t shmem = L.fused_shmem ? L.fused_shmem : fused_lds(max_m, max_k, bucket, glue).bytes;
+    if (shmem > static_cast<size_t>(kGemvGlueLdsBytes)) return hipErrorInvalidValue;
     if (glue)
       return single ? launch_bucket<false, true, true, true, true>(L, bucket, shmem, stream)
                     : launch_bucket<false, true, true, true, false>(L, bucket, shmem, stream);

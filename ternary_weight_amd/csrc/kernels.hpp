@@ -65,8 +65,12 @@ struct GemvLaunch {
   const FatUnit* units;
   int total;
   int tiles;  // 16-row tiles per wave, 0 = the bucket's full count
+  size_t fused_shmem;  // fused table launches: LDS bytes (0: from max_m, max_k)
 };
-bool gemv_fusable(int M, int K, bool glue = false);
+bool gemv_fusable(int M, int K, bool glue = false, bool table = false);
+// Staging bytes of one fused problem; a table launch takes the largest over
+// its problems (each problem lays its LDS out from its own M and K).
+size_t gemv_fused_lds_bytes(int M, int K, bool glue);
 // A single call fuses only up to this many rows: each workgroup stages and
 // quantizes all M rows, about 1 us more per row, while the separate
 // quantization kernel spreads rows over workgroups (measured per call at
@@ -75,10 +79,10 @@ bool gemv_fusable(int M, int K, bool glue = false);
 constexpr int kGemvSingleFusedMaxM = 3;
 // Fused decode problems of up to kGemvMergedMaxNsb superblocks in one launch
 // over a FatUnit table whose records carry each unit's superblock count
-// (FatUnit::nsb), longest first.  max_m, max_k: the largest M and K.
+// (FatUnit::nsb), longest first.  shmem: the largest gemv_fused_lds_bytes of
+// its problems.
 constexpr int kGemvMergedMaxNsb = 12;
-hipError_t launch_gemv_merged(const FatUnit* units, int total, int max_m, int max_k,
-                              hipStream_t stream);
+hipError_t launch_gemv_merged(const FatUnit* units, int total, size_t shmem, hipStream_t stream);
 hipError_t launch_gemv(const GemvLaunch& L, bool raw, int bucket, int max_m, int max_k,
                        bool fused, hipStream_t stream, bool glue = false);
 // Device-side absmean ternary quantization and I2_S packing of w (device,

@@ -466,6 +466,32 @@ def test_group_forward_in_cuda_graph():
                 assert torch.equal(it["y"], ys), f"replay {rep}"
 
 
+def test_group_merged_decode_mixed_shapes():
+    # Fused decode problems of very different M and K in one merged launch
+    # (M = 16 at K = 256 beside M = 1 and 2 at K = 3072): the launch's LDS is
+    # the largest single problem's staging, each workgroup lays its own out.
+    # K = 4096 (16 superblocks) fuses in its own launch.
+    nan = float("nan")
+    items, singles = [], []
+    for i, (M, K, N) in enumerate([(16, 256, 64), (1, 3072, 1024), (7, 1024, 200), (2, 3072, 96),
+                                   (1, 4096, 80), (5, 2048, 48)]):
+        x, nw, packed, scale = proj_inputs(32, i, 0, M, K, N)
+        it = dict(x=dev(x), norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                  y=torch.full((M, N), nan, device=DEV))
+        items.append(it)
+        singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, N, EPS))
+        if i == 0:
+            assert rel_l2(host(singles[-1]), oracle.bitlinear(x, nw, packed, N, EPS)) <= 1e-3
+    with bl.Group(items) as g:
+        info = g.forward_launches()
+        assert [(d["kind"], d["bucket"], d["count"]) for d in info] == [
+            ("quant", 8, 1), ("decode_fused", 0, 4), ("decode", 8, 1), ("decode_fused", 16, 1)], info
+        g.forward()
+        torch.cuda.synchronize()
+        for i, (it, ys) in enumerate(zip(items, singles)):
+            assert torch.equal(it["y"], ys), i
+
+
 def test_group_with_glue_in_cuda_graph():
     # A group with FFN-glue descriptors (fused glue decode, glue quantization
     # for an unfused decode and a prefill problem) beside a plain fused one,
