@@ -26,9 +26,10 @@
 // wave w takes its 16-row tiles w, w+4, w+8, ... (so at any time the four
 // waves stream one contiguous span), walked in order through a rolling window: the
 // weight loads of D tiles are in flight while one is processed (D = 4, 3, 2
-// for up to 4, 8, 16 superblocks; T = 2D).  Accumulators are combined one
-// tile late, once their MFMAs have drained, and all results are stored
-// after the last tile.
+// for up to 4, 8, 16 superblocks; T = 2D; a single-problem launch gives each
+// wave fewer tiles when N is small, see gemv_body).  Accumulators are
+// combined one tile late, once their MFMAs have drained, and all results are
+// stored after the last tile.
 // The kernel is specialised on the number of superblocks NSB = ceil(K/256):
 // a tile's NSB weight loads are issued together and consumed in order, so
 // the compiler's wait counts are exact and the register footprint small.
@@ -40,8 +41,9 @@
 // not fit, fragments come from global memory through the same
 // out-of-range-reads-zero buffer loads.  Fused variant (the forward when the
 // fp32 rows fit on chip): the workgroup stages the fp32 rows and the norm
-// weight instead and runs the RMSNorm + int8 quantization itself, with the
-// arithmetic of the quantization kernel, while its first weight loads are in
+// weight instead (with the FFN glue, the up rows too) and its four waves run
+// the RMSNorm + int8 quantization themselves, with the arithmetic and order of
+// operations of the quantization kernel, while its first weight loads are in
 // flight; no separate launch and no workspace.  K beyond 16 superblocks runs a
 // generic variant (one tile per wave, superblocks streamed two ahead).
 // Bound: HBM, K/4 bytes per output column.
@@ -149,8 +151,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // superblocks per tile.  NSB == 0: any K, streamed.  GLUE (fused only): the
 // input rows are the FFN glue act(x) * up (P.act, P.up).  tpu: 16-row tiles
 // per wave (1..T); below T a workgroup owns 64*tpu rows, so that a launch of
-// one small problem still spreads over many workgroups (the window then runs
-// on zero-filled loads past tile tpu-1, which store nothing).
+// one small problem still spreads over many workgroups (past tile tpu-1 the
+// window's loads read zeros without a memory access, and those tiles skip
+// their products and store nothing).
 template <bool RAW, bool FROM_LDS, int NSB, bool FUSED, bool GLUE = false>
 __device__ __forceinline__ void gemv_body(const Prob& P, const int unit, const int tpu) {
   static_assert(!FUSED || (FROM_LDS && !RAW && NSB > 0), "fused: forward, staged, specialised K");
