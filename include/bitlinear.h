@@ -141,7 +141,11 @@ bl_status i2s_pack_device(const float* w, int64_t K, int64_t N, uint8_t* packed,
  * Otherwise the codes go through a library-owned workspace (M*K + 8*M bytes)
  * per (device, stream); the workspace is grown with hipMalloc when needed,
  * which is not allowed while the stream is being captured into a graph
- * (BL_ERR_UNSUPPORTED).
+ * (BL_ERR_UNSUPPORTED).  A workspace used during a capture is pinned: the
+ * graph holds its address, so a later growth allocates a new buffer and
+ * keeps the old one, and bl_release_workspace does not free it (it lives
+ * until the process ends).  Replays of such a graph share the buffer with
+ * later calls on the capturing stream: they must not overlap them in time.
  */
 bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* packed_w,
                             float w_scale, int64_t M, int64_t K, int64_t N, float eps, float* y,
@@ -330,8 +334,36 @@ bl_status bl_group_forward_launch(bl_group* g, int32_t i, void* stream);
 /* Frees the group (synchronises the device first). NULL is a no-op. */
 bl_status bl_group_destroy(bl_group* g);
 
-/* Frees the per-(device, stream) workspaces of bitlinear_forward and the
- * hooks (synchronises the device first). */
+/*
+ * bitlinear_forward_batched — count independent projections in one call:
+ * results bit-identical to count separate bitlinear_forward calls
+ * (bitlinear_glu_forward for a descriptor with up set), all enqueued on
+ * stream.  It is the stateless form of a group ("BitNet Embeddings GGUF
+ * Conversion Implementation", s4.5: the seven projections of a layer; K a
+ * multiple of 128, "gguf-gemv", "Requirements").
+ *   descs  host array of count descriptors, validated by the rules of
+ *          bl_group_create (outputs must not alias each other or any input);
+ *          entries with M == 0 are skipped.  Not kept after the call.
+ *   count  >= 1.
+ * Every call validates, plans the launches (the plan a group of the same
+ * descriptors would have: quantization launches per chunk class with one
+ * pass per shared x, one merged fused decode launch, one decode launch per
+ * other superblock count, one prefill launch) and enqueues them in order on
+ * stream; it uses no other stream.  The launch tables (a few bytes per
+ * workgroup) and the unfused problems' codes live in the library workspace
+ * of (device, stream), grown with hipMalloc when needed; the tables reach it
+ * by an asynchronous copy from pinned host staging.  The host waits only for
+ * the previous batched call's table copy on the same stream.
+ * Graph capture: refused with BL_ERR_UNSUPPORTED (the tables are copied on
+ * every call); capture bl_group_forward, whose tables are uploaded once.
+ * Errors: those of bl_group_create, and BL_ERR_NOMEM when the workspace or
+ * the staging cannot grow; nothing is enqueued on an error from validation.
+ */
+bl_status bitlinear_forward_batched(const bl_desc* descs, int32_t count, void* stream);
+
+/* Frees the per-(device, stream) workspaces and table staging of
+ * bitlinear_forward, bitlinear_forward_batched and the hooks (synchronises
+ * the device first).  Workspaces a captured graph uses are kept. */
 bl_status bl_release_workspace(void);
 
 #ifdef __cplusplus

@@ -70,6 +70,7 @@ _SIGS = {
     "bl_group_forward_launches": ([_p], _i32),
     "bl_group_forward_launch_info": ([_p, _i32, _p, _p, _p], _i32),
     "bl_group_forward_launch": ([_p, _i32, _p], _i32),
+    "bitlinear_forward_batched": ([ctypes.POINTER(BlDesc), _i32, _p], _i32),
     "bl_release_workspace": ([], _i32),
     # measurement probes (include/bitlinear_probe.h)
     "bl_probe_read": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
@@ -225,6 +226,32 @@ def bitlinear_matmul_i32(xq, packed_w, N: int, acc=None, stream=None):
     return acc
 
 
+def _descs(items):
+    """bl_desc array of group-style item dicts (see Group)."""
+    torch = _torch()
+    descs = (BlDesc * len(items))()
+    for i, it in enumerate(items):
+        x, y = it["x"], it["y"]
+        M, K = x.shape
+        nw, f16 = _norm(it.get("norm_w"), K)
+        up = it.get("up")
+        descs[i] = BlDesc(_dev(x, torch.float32, "x"), nw,
+                          _dev(it["packed_w"], torch.uint8, "packed_w"),
+                          float(it["w_scale"]), float(it["eps"]), M, K, int(it["N"]),
+                          _dev(y, torch.float32, "y", (M, int(it["N"]))), int(f16),
+                          None if up is None else _dev(up, torch.float32, "up", (M, K)),
+                          int(it.get("act", ACT_SILU)) if up is not None else 0)
+    return descs
+
+
+def bitlinear_forward_batched(items, stream=None) -> None:
+    """Every item's forward (Group-style dicts, outputs in item["y"]) in one
+    stateless call."""
+    descs = _descs(items)
+    _check(_lib.bitlinear_forward_batched(descs, len(items), _stream_handle(stream)),
+           "bitlinear_forward_batched")
+
+
 class Group:
     """Many independent projections run as one launch per stage.
 
@@ -237,21 +264,8 @@ class Group:
     """
 
     def __init__(self, items):
-        torch = _torch()
-        self._keep = []
-        descs = (BlDesc * len(items))()
-        for i, it in enumerate(items):
-            x, y = it["x"], it["y"]
-            M, K = x.shape
-            nw, f16 = _norm(it.get("norm_w"), K)
-            up = it.get("up")
-            descs[i] = BlDesc(_dev(x, torch.float32, "x"), nw,
-                              _dev(it["packed_w"], torch.uint8, "packed_w"),
-                              float(it["w_scale"]), float(it["eps"]), M, K, int(it["N"]),
-                              _dev(y, torch.float32, "y", (M, int(it["N"]))), int(f16),
-                              None if up is None else _dev(up, torch.float32, "up", (M, K)),
-                              int(it.get("act", ACT_SILU)) if up is not None else 0)
-            self._keep.append(it)
+        self._keep = list(items)
+        descs = _descs(items)
         handle = _p()
         _check(_lib.bl_group_create(descs, len(items), ctypes.byref(handle)), "bl_group_create")
         self._h = handle

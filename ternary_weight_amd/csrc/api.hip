@@ -68,27 +68,45 @@ WsLayout ws_layout(int64_t M, int64_t K) {
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  // Used while its stream was being captured into a graph: the graph holds
+  // this address, so the buffer is never freed (growing it retires it).
+  bool captured = false;
+  // Pinned host staging for bitlinear_forward_batched's launch tables, and
+  // an event recorded after the last copy out of it.
+  void* host = nullptr;
+  size_t host_bytes = 0;
+  hipEvent_t host_done = nullptr;
+  bool host_pending = false;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Buffers retired because a captured graph may still use them; kept until
+// the process ends.
+std::vector<void*> g_ws_retired;
 
-// Workspace of at least `bytes` for (current device, stream).  Growing it
-// waits for the stream's earlier work, frees the old buffer and allocates a
-// new one; that is refused while the stream is being captured.
+// Workspace of at least `bytes` for (current device, stream).  During graph
+// capture the existing buffer is used (and marked: it is never freed
+// afterwards) and growing it is refused.  Outside capture, growing it waits
+// for the stream's earlier work and replaces the buffer; the old one is
+// freed unless a captured graph may use it.
 bl_status acquire_ws(hipStream_t stream, size_t bytes, uint8_t** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return BL_ERR_HIP;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return BL_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace& w = g_ws[{dev, stream}];
-  if (w.bytes < bytes) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return BL_ERR_HIP;
-    if (cs != hipStreamCaptureStatusNone) return BL_ERR_UNSUPPORTED;
+  if (cs != hipStreamCaptureStatusNone) {
+    if (w.bytes < bytes) return BL_ERR_UNSUPPORTED;
+    w.captured = true;
+  } else if (w.bytes < bytes) {
     if (w.ptr) {
       if (hipStreamSynchronize(stream) != hipSuccess) return BL_ERR_HIP;
-      if (hipFree(w.ptr) != hipSuccess) return BL_ERR_HIP;
+      if (w.captured) g_ws_retired.push_back(w.ptr);
+      else if (hipFree(w.ptr) != hipSuccess) return BL_ERR_HIP;
       w.ptr = nullptr;
       w.bytes = 0;
+      w.captured = false;
     }
     const size_t nb = round_up(bytes, size_t{1} << 20);
     void* p = nullptr;
@@ -100,6 +118,43 @@ bl_status acquire_ws(hipStream_t stream, size_t bytes, uint8_t** out) {
     w.bytes = nb;
   }
   *out = static_cast<uint8_t*>(w.ptr);
+  return BL_OK;
+}
+
+// Pinned host staging of at least `bytes` for (current device, stream), for
+// tables copied to the device asynchronously: waits until the last copy out
+// of the previous contents has finished.  Not for use during capture.
+bl_status acquire_staging(hipStream_t stream, size_t bytes, uint8_t** out, hipEvent_t* done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BL_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[{dev, stream}];
+  if (w.host_pending) {
+    if (hipEventSynchronize(w.host_done) != hipSuccess) return BL_ERR_HIP;
+    w.host_pending = false;
+  }
+  if (!w.host_done && hipEventCreateWithFlags(&w.host_done, hipEventDisableTiming) != hipSuccess) {
+    w.host_done = nullptr;
+    return BL_ERR_HIP;
+  }
+  if (w.host_bytes < bytes) {
+    if (w.host && hipHostFree(w.host) != hipSuccess) return BL_ERR_HIP;
+    w.host = nullptr;
+    w.host_bytes = 0;
+    const size_t nb = round_up(bytes, size_t{1} << 16);
+    void* p = nullptr;
+    if (hipHostMalloc(&p, nb, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      return BL_ERR_NOMEM;
+    }
+    w.host = p;
+    w.host_bytes = nb;
+  }
+  // The caller records host_done after its copy; mark it pending now (the
+  // lock is released before the copy is enqueued).
+  w.host_pending = true;
+  *out = static_cast<uint8_t*>(w.host);
+  *done = w.host_done;
   return BL_OK;
 }
 
@@ -408,10 +463,16 @@ bl_status bl_release_workspace(void) {
     int cur = 0;
     if (hipGetDevice(&cur) != hipSuccess) return BL_ERR_HIP;
     for (auto& kv : g_ws) {
-      if (!kv.second.ptr) continue;
-      if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-          hipFree(kv.second.ptr) != hipSuccess)
+      Workspace& w = kv.second;
+      if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         st = BL_ERR_HIP;
+        continue;
+      }
+      // A buffer a captured graph uses stays allocated (retired).
+      if (w.ptr && w.captured) g_ws_retired.push_back(w.ptr);
+      else if (w.ptr && hipFree(w.ptr) != hipSuccess) st = BL_ERR_HIP;
+      if (w.host && hipHostFree(w.host) != hipSuccess) st = BL_ERR_HIP;
+      if (w.host_done && hipEventDestroy(w.host_done) != hipSuccess) st = BL_ERR_HIP;
     }
     g_ws.clear();
     if (hipSetDevice(cur) != hipSuccess) st = BL_ERR_HIP;
@@ -657,6 +718,189 @@ void interleave_gemm_units(StageHost& h) {
   h.units.swap(out);
 }
 
+// A launch plan over validated descriptors: the stages' host images (problem
+// records with their workspace pointers, unit tables), serialized into one
+// table image.  Groups upload it once; bitlinear_forward_batched builds one
+// per call.
+struct Plan {
+  std::map<QuantKey, StageHost> hqs;
+  StageHost hm;
+  // Decode problems by (bucket, fused, glue); fused ones of up to
+  // kGemvMergedMaxNsb superblocks without the glue share one merged launch,
+  // keyed (0, true, false).
+  std::map<std::tuple<int, bool, bool>, StageHost> hv;
+  std::vector<uint8_t> image;
+  std::vector<std::array<size_t, 3>> offs;  // per stage: probs, units, fat units
+};
+
+struct PlanSizes {
+  size_t ws_bytes = 0;     // codes, factors and row sums of the unfused problems
+  size_t table_bound = 0;  // upper bound of the table image
+};
+
+bool desc_fused(const bl_desc& d) {
+  return d.M <= kGemvMaxM &&
+         gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), d.up != nullptr, true);
+}
+
+// Validates every descriptor (the rules of bitlinear_forward, plus the glue
+// and norm-weight kind fields) and sizes the plan.
+bl_status plan_sizes(const bl_desc* descs, int32_t count, PlanSizes* out) {
+  if (!descs || count <= 0) return BL_ERR_INVALID_ARGUMENT;
+  int64_t units_q = 0, units_v = 0, units_m = 0;
+  PlanSizes z;
+  for (int32_t i = 0; i < count; ++i) {
+    const bl_desc& d = descs[i];
+    bl_status st = check_forward(d.x, d.norm_w, d.packed_w, d.w_scale, d.M, d.K, d.N, d.eps, d.y);
+    if (st == BL_OK && d.norm_w_f16 != 0 && d.norm_w_f16 != 1) st = BL_ERR_INVALID_ARGUMENT;
+    if (st == BL_OK && d.up && d.act != BL_ACT_SILU && d.act != BL_ACT_GELU_TANH)
+      st = BL_ERR_INVALID_ARGUMENT;
+    if (st == BL_OK && d.M > 0 && d.up && !aligned16(d.up)) st = BL_ERR_MISALIGNED;
+    if (st != BL_OK) return st;
+    if (d.M == 0) continue;
+    const int M = static_cast<int>(d.M), K = static_cast<int>(d.K), N = static_cast<int>(d.N);
+    if (M <= kGemvMaxM) {
+      const int v = gemv_units(N, gemv_bucket(K));
+      units_v += v;
+      z.table_bound += static_cast<size_t>(v) * sizeof(FatUnit);
+    } else {
+      const int u = gemm_units(M, N);
+      units_m += u;
+      z.table_bound += sizeof(Prob) + static_cast<size_t>(u) * sizeof(int2);
+    }
+    if (desc_fused(d)) continue;
+    units_q += quant_units(M);
+    z.table_bound += sizeof(Prob) + static_cast<size_t>(quant_units(M)) * sizeof(int2);
+    z.ws_bytes += ws_layout(d.M, d.K).bytes;
+  }
+  if (units_q > INT32_MAX / 2 || units_v > INT32_MAX / 2 || units_m > INT32_MAX / 2)
+    return BL_ERR_UNSUPPORTED;
+  // every stage holds at least one problem: at most 1 + 2 * count stages,
+  // each with three sections padded to kAlign
+  z.table_bound += (1 + 2 * static_cast<size_t>(count)) * 3 * kAlign;
+  *out = z;
+  return BL_OK;
+}
+
+// Stage host images of the plan (workspace pointers from ws), then the table
+// image.  Descriptors must have passed plan_sizes.
+void plan_build(const bl_desc* descs, int32_t count, uint8_t* ws, Plan& pl) {
+  std::vector<Prob> qprobs;
+  size_t off = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const bl_desc& d = descs[i];
+    if (d.M == 0) continue;
+    const bool glue = d.up != nullptr;
+    const bool fused = desc_fused(d);
+    Prob p{};
+    p.x = d.x;
+    if (glue) {
+      p.up = d.up;
+      p.act = d.act == BL_ACT_SILU ? kActSilu : kActGeluTanh;
+    }
+    p.norm_w = static_cast<const float*>(d.norm_w);
+    p.nw_f16 = d.norm_w_f16;
+    p.w = d.packed_w;
+    if (!fused) {
+      const WsLayout l = ws_layout(d.M, d.K);
+      p.xq = reinterpret_cast<int8_t*>(ws + off + l.xq);
+      p.factor = reinterpret_cast<float*>(ws + off + l.factor);
+      p.rowsum = reinterpret_cast<int32_t*>(ws + off + l.rowsum);
+      off += l.bytes;
+    }
+    p.y = d.y;
+    p.acc = nullptr;
+    p.w_scale = d.w_scale;
+    p.eps = d.eps;
+    p.M = static_cast<int>(d.M);
+    p.K = static_cast<int>(d.K);
+    p.N = static_cast<int>(d.N);
+    if (!fused) qprobs.push_back(p);
+    if (p.M <= kGemvMaxM) {
+      const int b = gemv_bucket(p.K);
+      const bool merge = fused && !glue && b >= 1 && b <= kGemvMergedMaxNsb;
+      // (unfused glue problems read their codes like any other: plain stages)
+      StageHost& sh = pl.hv[{merge ? 0 : b, fused, fused && glue}];
+      sh.fat = true;
+      sh.add(p, gemv_units(p.N, b), merge ? b : 0);
+      if (fused) sh.shmem = std::max(sh.shmem, gemv_fused_lds_bytes(p.M, p.K, glue));
+    } else {
+      pl.hm.add(p, gemm_units(p.M, p.N));
+    }
+  }
+  pl.hqs = build_quant_stages(qprobs);
+  {
+    auto it = pl.hv.find({0, true, false});
+    if (it != pl.hv.end()) order_merged_units(it->second.fat_units);
+  }
+  interleave_gemm_units(pl.hm);
+
+  // Table image, stage order: prefill, quantization stages, decode stages.
+  std::vector<const StageHost*> hosts{&pl.hm};
+  for (const auto& kv : pl.hqs) hosts.push_back(&kv.second);
+  for (const auto& kv : pl.hv) hosts.push_back(&kv.second);
+  const size_t nst = hosts.size();
+  size_t total = 0;
+  pl.offs.assign(nst, {});
+  for (size_t k = 0; k < nst; ++k) {
+    pl.offs[k][0] = total;
+    total += round_up(hosts[k]->probs.size() * sizeof(Prob), kAlign);
+    pl.offs[k][1] = total;
+    total += round_up(hosts[k]->units.size() * sizeof(int2), kAlign);
+    pl.offs[k][2] = total;
+    total += round_up(hosts[k]->fat_units.size() * sizeof(FatUnit), kAlign);
+  }
+  pl.image.assign(std::max<size_t>(total, 1), 0);
+  for (size_t k = 0; k < nst; ++k) {
+    const StageHost& h = *hosts[k];
+    if (!h.probs.empty())
+      std::memcpy(pl.image.data() + pl.offs[k][0], h.probs.data(), h.probs.size() * sizeof(Prob));
+    if (!h.units.empty())
+      std::memcpy(pl.image.data() + pl.offs[k][1], h.units.data(), h.units.size() * sizeof(int2));
+    if (!h.fat_units.empty())
+      std::memcpy(pl.image.data() + pl.offs[k][2], h.fat_units.data(),
+                  h.fat_units.size() * sizeof(FatUnit));
+  }
+}
+
+// The group's stages over a copy of the plan's table image at `tables`
+// (device).
+void plan_bind(const Plan& pl, const uint8_t* tables, bl_group* g) {
+  g->quant.assign(pl.hqs.size(), GroupStage{});
+  g->gemv.assign(pl.hv.size(), std::pair<int, GroupStage>{});
+  std::vector<const StageHost*> hosts{&pl.hm};
+  std::vector<GroupStage*> stages{&g->gemm};
+  size_t qi = 0;
+  for (const auto& kv : pl.hqs) {
+    g->quant[qi].shared = kv.first.shared;
+    g->quant[qi].chunks = kv.first.chunks;
+    g->quant[qi].act = kv.first.act;
+    hosts.push_back(&kv.second);
+    stages.push_back(&g->quant[qi]);
+    ++qi;
+  }
+  size_t bi = 0;
+  for (const auto& kv : pl.hv) {
+    g->gemv[bi].first = std::get<0>(kv.first);
+    g->gemv[bi].second.fused = std::get<1>(kv.first);
+    g->gemv[bi].second.glue = std::get<2>(kv.first);
+    g->gemv[bi].second.merged = std::get<0>(kv.first) == 0 && std::get<1>(kv.first);
+    hosts.push_back(&kv.second);
+    stages.push_back(&g->gemv[bi].second);
+    ++bi;
+  }
+  for (size_t k = 0; k < hosts.size(); ++k) {
+    stages[k]->probs = reinterpret_cast<const Prob*>(tables + pl.offs[k][0]);
+    stages[k]->units = reinterpret_cast<const int2*>(tables + pl.offs[k][1]);
+    stages[k]->fat = hosts[k]->fat ? reinterpret_cast<const FatUnit*>(tables + pl.offs[k][2]) : nullptr;
+    stages[k]->total = static_cast<int>(hosts[k]->nunits());
+    stages[k]->count = hosts[k]->nprobs;
+    stages[k]->max_m = hosts[k]->max_m;
+    stages[k]->max_k = hosts[k]->max_k;
+    stages[k]->shmem = hosts[k]->shmem;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -665,29 +909,9 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
   try {
     if (!out) return BL_ERR_INVALID_ARGUMENT;
     *out = nullptr;
-    if (!descs || count <= 0) return BL_ERR_INVALID_ARGUMENT;
-    int64_t units_q = 0, units_v = 0, units_m = 0;
-    size_t ws_bytes = 0;
-    for (int32_t i = 0; i < count; ++i) {
-      const bl_desc& d = descs[i];
-      bl_status st = check_forward(d.x, d.norm_w, d.packed_w, d.w_scale, d.M, d.K, d.N, d.eps, d.y);
-      if (st == BL_OK && d.norm_w_f16 != 0 && d.norm_w_f16 != 1) st = BL_ERR_INVALID_ARGUMENT;
-      if (st == BL_OK && d.up && d.act != BL_ACT_SILU && d.act != BL_ACT_GELU_TANH)
-        st = BL_ERR_INVALID_ARGUMENT;
-      if (st == BL_OK && d.M > 0 && d.up && !aligned16(d.up)) st = BL_ERR_MISALIGNED;
-      if (st != BL_OK) return st;
-      if (d.M == 0) continue;
-      if (d.M <= kGemvMaxM)
-        units_v += gemv_units(static_cast<int>(d.N), gemv_bucket(static_cast<int>(d.K)));
-      else units_m += gemm_units(static_cast<int>(d.M), static_cast<int>(d.N));
-      if (d.M <= kGemvMaxM &&
-          gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), d.up != nullptr, true))
-        continue;
-      units_q += quant_units(static_cast<int>(d.M));
-      ws_bytes += ws_layout(d.M, d.K).bytes;
-    }
-    if (units_q > INT32_MAX / 2 || units_v > INT32_MAX / 2 || units_m > INT32_MAX / 2)
-      return BL_ERR_UNSUPPORTED;
+    PlanSizes sz;
+    bl_status st = plan_sizes(descs, count, &sz);
+    if (st != BL_OK) return st;
 
     bl_group* g = new (std::nothrow) bl_group;
     if (!g) return BL_ERR_NOMEM;
@@ -695,135 +919,25 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
       delete g;
       return BL_ERR_HIP;
     }
-    if (ws_bytes > 0 && hipMalloc(&g->workspace, ws_bytes) != hipSuccess) {
+    if (sz.ws_bytes > 0 && hipMalloc(&g->workspace, sz.ws_bytes) != hipSuccess) {
       (void)hipGetLastError();
       free_group(g);
       return BL_ERR_NOMEM;
     }
-
-    std::vector<Prob> qprobs;
-    StageHost hm;
-    // Decode problems by (bucket, fused, glue); fused ones of up to
-    // kGemvMergedMaxNsb superblocks without the glue share one merged launch,
-    // keyed (0, true, false).
-    std::map<std::tuple<int, bool, bool>, StageHost> hv;
-    uint8_t* ws = static_cast<uint8_t*>(g->workspace);
-    size_t off = 0;
-    for (int32_t i = 0; i < count; ++i) {
-      const bl_desc& d = descs[i];
-      if (d.M == 0) continue;
-      const bool glue = d.up != nullptr;
-      const bool fused =
-          d.M <= kGemvMaxM && gemv_fusable(static_cast<int>(d.M), static_cast<int>(d.K), glue, true);
-      Prob p{};
-      p.x = d.x;
-      if (glue) {
-        p.up = d.up;
-        p.act = d.act == BL_ACT_SILU ? kActSilu : kActGeluTanh;
-      }
-      p.norm_w = static_cast<const float*>(d.norm_w);
-      p.nw_f16 = d.norm_w_f16;
-      p.w = d.packed_w;
-      if (!fused) {
-        const WsLayout l = ws_layout(d.M, d.K);
-        p.xq = reinterpret_cast<int8_t*>(ws + off + l.xq);
-        p.factor = reinterpret_cast<float*>(ws + off + l.factor);
-        p.rowsum = reinterpret_cast<int32_t*>(ws + off + l.rowsum);
-        off += l.bytes;
-      }
-      p.y = d.y;
-      p.acc = nullptr;
-      p.w_scale = d.w_scale;
-      p.eps = d.eps;
-      p.M = static_cast<int>(d.M);
-      p.K = static_cast<int>(d.K);
-      p.N = static_cast<int>(d.N);
-      if (!fused) qprobs.push_back(p);
-      if (p.M <= kGemvMaxM) {
-        const int b = gemv_bucket(p.K);
-        const bool merge = fused && !glue && b >= 1 && b <= kGemvMergedMaxNsb;
-        // (unfused glue problems read their codes like any other: plain stages)
-        StageHost& sh = hv[{merge ? 0 : b, fused, fused && glue}];
-        sh.fat = true;
-        sh.add(p, gemv_units(p.N, b), merge ? b : 0);
-        if (fused) sh.shmem = std::max(sh.shmem, gemv_fused_lds_bytes(p.M, p.K, glue));
-      }
-      else hm.add(p, gemm_units(p.M, p.N));
-    }
-    std::map<QuantKey, StageHost> hqs = build_quant_stages(qprobs);
-    {
-      auto it = hv.find({0, true, false});
-      if (it != hv.end()) order_merged_units(it->second.fat_units);
-    }
-    interleave_gemm_units(hm);
-
-    // One device buffer for every table.
-    g->gemv.resize(hv.size());
-    g->quant.resize(hqs.size());
-    std::vector<StageHost*> hosts{&hm};
-    std::vector<GroupStage*> stages{&g->gemm};
-    size_t qi = 0;
-    for (auto& kv : hqs) {
-      g->quant[qi].shared = kv.first.shared;
-      g->quant[qi].chunks = kv.first.chunks;
-      g->quant[qi].act = kv.first.act;
-      hosts.push_back(&kv.second);
-      stages.push_back(&g->quant[qi]);
-      ++qi;
-    }
-    size_t bi = 0;
-    for (auto& kv : hv) {
-      g->gemv[bi].first = std::get<0>(kv.first);
-      g->gemv[bi].second.fused = std::get<1>(kv.first);
-      g->gemv[bi].second.glue = std::get<2>(kv.first);
-      g->gemv[bi].second.merged = std::get<0>(kv.first) == 0 && std::get<1>(kv.first);
-      hosts.push_back(&kv.second);
-      stages.push_back(&g->gemv[bi].second);
-      ++bi;
-    }
-    const size_t nst = hosts.size();
-    size_t total = 0;
-    std::vector<std::array<size_t, 3>> offs(nst);
-    for (size_t k = 0; k < nst; ++k) {
-      offs[k][0] = total;
-      total += round_up(hosts[k]->probs.size() * sizeof(Prob), kAlign);
-      offs[k][1] = total;
-      total += round_up(hosts[k]->units.size() * sizeof(int2), kAlign);
-      offs[k][2] = total;
-      total += round_up(hosts[k]->fat_units.size() * sizeof(FatUnit), kAlign);
-    }
-    std::vector<uint8_t> image(std::max<size_t>(total, 1), 0);
-    for (size_t k = 0; k < nst; ++k) {
-      const StageHost& h = *hosts[k];
-      if (!h.probs.empty())
-        std::memcpy(image.data() + offs[k][0], h.probs.data(), h.probs.size() * sizeof(Prob));
-      if (!h.units.empty())
-        std::memcpy(image.data() + offs[k][1], h.units.data(), h.units.size() * sizeof(int2));
-      if (!h.fat_units.empty())
-        std::memcpy(image.data() + offs[k][2], h.fat_units.data(), h.fat_units.size() * sizeof(FatUnit));
-    }
-    if (hipMalloc(&g->tables, image.size()) != hipSuccess) {
+    Plan pl;
+    plan_build(descs, count, static_cast<uint8_t*>(g->workspace), pl);
+    if (hipMalloc(&g->tables, pl.image.size()) != hipSuccess) {
       (void)hipGetLastError();
       free_group(g);
       return BL_ERR_NOMEM;
     }
-    if (hipMemcpy(g->tables, image.data(), image.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    if (hipMemcpy(g->tables, pl.image.data(), pl.image.size(), hipMemcpyHostToDevice) != hipSuccess) {
       free_group(g);
       return BL_ERR_HIP;
     }
-    uint8_t* t = static_cast<uint8_t*>(g->tables);
-    for (size_t k = 0; k < nst; ++k) {
-      stages[k]->probs = reinterpret_cast<const Prob*>(t + offs[k][0]);
-      stages[k]->units = reinterpret_cast<const int2*>(t + offs[k][1]);
-      stages[k]->fat = hosts[k]->fat ? reinterpret_cast<const FatUnit*>(t + offs[k][2]) : nullptr;
-      stages[k]->total = static_cast<int>(hosts[k]->nunits());
-      stages[k]->count = hosts[k]->nprobs;
-      stages[k]->max_m = hosts[k]->max_m;
-      stages[k]->max_k = hosts[k]->max_k;
-      stages[k]->shmem = hosts[k]->shmem;
-    }
+    plan_bind(pl, static_cast<const uint8_t*>(g->tables), g);
     int nfused = 0;
-    for (const auto& st : g->gemv) nfused += st.second.fused ? 1 : 0;
+    for (const auto& st2 : g->gemv) nfused += st2.second.fused ? 1 : 0;
     g->naux = std::min(std::max(nfused - 1, 0), kAuxStreams);
     bool ok = g->naux == 0 || hipEventCreateWithFlags(&g->fork, hipEventDisableTiming) == hipSuccess;
     for (int j = 0; ok && j < g->naux; ++j)
@@ -1006,6 +1120,48 @@ bl_status bl_group_destroy(bl_group* g) {
     free_group(g);
     if (hipSetDevice(cur) != hipSuccess) st = BL_ERR_HIP;
     return st;
+  } catch (...) {
+    return BL_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- stateless batched call ---
+
+extern "C" {
+
+bl_status bitlinear_forward_batched(const bl_desc* descs, int32_t count, void* stream) {
+  try {
+    PlanSizes sz;
+    bl_status st = plan_sizes(descs, count, &sz);
+    if (st != BL_OK) return st;
+    bool any = false;
+    for (int32_t i = 0; i < count; ++i) any = any || descs[i].M > 0;
+    if (!any) return BL_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // The tables travel through pinned host staging on every call, which a
+    // captured graph could not replay: capture takes a group instead.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return BL_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return BL_ERR_UNSUPPORTED;
+    const size_t ws_part = round_up(sz.ws_bytes, kAlign);
+    uint8_t* ws = nullptr;
+    if ((st = acquire_ws(s, ws_part + sz.table_bound, &ws)) != BL_OK) return st;
+    Plan pl;
+    plan_build(descs, count, ws, pl);
+    if (pl.image.size() > sz.table_bound) return BL_ERR_INTERNAL;
+    uint8_t* host = nullptr;
+    hipEvent_t done = nullptr;
+    if ((st = acquire_staging(s, pl.image.size(), &host, &done)) != BL_OK) return st;
+    std::memcpy(host, pl.image.data(), pl.image.size());
+    if (hipMemcpyAsync(ws + ws_part, host, pl.image.size(), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipEventRecord(done, s) != hipSuccess)
+      return BL_ERR_HIP;
+    bl_group g;
+    if (hipGetDevice(&g.device) != hipSuccess) return BL_ERR_HIP;
+    plan_bind(pl, ws + ws_part, &g);
+    return group_run(&g, s, true);  // no auxiliary streams: every launch on s
   } catch (...) {
     return BL_ERR_INTERNAL;
   }

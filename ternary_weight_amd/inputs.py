@@ -122,3 +122,13 @@ def sample_rows(M: int, count: int, seed: int = 0) -> np.ndarray:
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0x5A, M, count, seed])))
     mid = g.choice(np.arange(1, M - 1), size=count - 2, replace=False)
     return np.sort(np.concatenate([[0, M - 1], mid]))
+
+
+def tile_rows(M: int, tile: int, seed: int = 0) -> np.ndarray:
+    """Sorted distinct row indices: one seeded row inside every block of
+    `tile` consecutive rows (so every row tile of a tiled kernel is hit),
+    plus the first and the last row."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0x7A, M, tile, seed])))
+    starts = np.arange(0, M, tile)
+    picks = starts + (g.random(len(starts)) * np.minimum(tile, M - starts)).astype(np.int64)
+    return np.unique(np.concatenate([[0, M - 1], picks]))

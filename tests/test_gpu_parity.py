@@ -117,6 +117,11 @@ MATMUL_CASES = [
     # tiled MFMA kernel
     (17, 128, 1), (17, 1024, 1024), (64, 640, 256), (200, 1280, 333), (255, 2048, 640),
     (257, 640, 2048), (512, 3072, 1024), (130, 8192, 129),
+    # the Gemma3-270M layer at M = 512 (q, k/v, o, gate/up, down)
+    (512, 640, 1024), (512, 640, 256), (512, 1024, 640), (512, 640, 2048), (512, 2048, 640),
+    # decode rows too long to stage in LDS: activation fragments from global
+    # memory (M*K > 64 KB), with even and odd superblock counts
+    (16, 8192, 96), (9, 8064, 130), (12, 65536, 8), (9, 4224, 130),
 ]
 
 
@@ -162,6 +167,38 @@ def test_decode_single_call_wide_n(M, K, N):
         g.forward()
         torch.cuda.synchronize()
         assert torch.equal(it["y"], y)
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 8192, 200), (11, 8064, 77)])
+def test_decode_long_rows_from_global(M, K, N):
+    # Decode rows longer than the 64 KB activation staging: the fragments are
+    # read from global memory.  Single call and a group table (the other
+    # kernel instance) against the oracle and the hooks, bit for bit.
+    x, nw, packed, scale = proj_inputs(23, M, K, M, K, N)
+    x[M // 2] = 0.0
+    dx, dn, dp = dev(x), dev(nw), dev(packed)
+    y = bl.bitlinear_forward(dx, dn, dp, scale, N, EPS)
+    xq, f = bl.bitlinear_quant(dx, dn, EPS)
+    acc = bl.bitlinear_matmul_i32(xq, dp, N)
+    assert np.array_equal(host(acc), oracle.matmul_i32(host(xq), packed, K, N))
+    assert torch.equal(y, _hooks_epilogue(acc, f, scale))
+    assert rel_l2(host(y), oracle.bitlinear(x, nw, packed, N, EPS)) <= 1e-3
+    it = dict(x=dx, norm_w=dn, packed_w=dp, w_scale=scale, eps=EPS, N=N,
+              y=torch.full((M, N), float("nan"), device=DEV))
+    other = dict(x=dev(x[:1].copy()), norm_w=dn, packed_w=dp, w_scale=scale, eps=EPS, N=N,
+                 y=torch.full((1, N), float("nan"), device=DEV))
+    with bl.Group([it, other]) as g:
+        assert [d["kind"] for d in g.forward_launches()] == ["quant", "decode"]
+        g.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(it["y"], y)
+        assert torch.equal(other["y"], bl.bitlinear_forward(other["x"], dn, dp, scale, N, EPS))
+
+
+def _hooks_epilogue(acc, f, scale):
+    """The forward's fp32 epilogue applied to the hooks' results: float(acc)
+    times (factor / w_scale), each step one fp32 rounding."""
+    return acc.to(torch.float32) * (f / torch.tensor(scale, dtype=torch.float32, device=DEV))[:, None]
 
 
 # ------------------------------------------------------------ whole path ---
@@ -811,23 +848,79 @@ def test_glu_forward_qwen_down_full_size_sampled_rows():
 
 
 # ------------------------------------------ full-size workloads, sampled ---
+# Workloads 4 and 5 run at full size in the grouped launch the bench times,
+# into NaN-filled outputs (every element must be written: a skipped or
+# mis-indexed tile would leave a NaN).  Each BitLinear is then checked on one
+# seeded row in every 128-row tile of the prefill kernel (rows drawn per
+# BitLinear), plus the first and the last row:
+#   * the group's output equals the fp32 epilogue of the hooks
+#     (matmul_i32 o quant) bit for bit;
+#   * the int8 codes and factors meet the quantization criteria against the
+#     oracle;
+#   * for the BitLinears in `exact`, matmul_i32 fed the oracle's own codes of
+#     the whole matrix equals the oracle's int32 product exactly;
+#   * on a smaller per-BitLinear sample, rel L2 <= 1e-3 against the oracle.
+# The oracle runs in host threads (its C functions release the GIL).
 
-def _sampled_check(wid, rows_per, group_items, refs):
-    """Run the group once, then compare sampled rows with the oracle."""
-    with bl.Group(group_items) as g:
+ORACLE_THREADS = 16
+TILE_M = 128  # activation rows per prefill workgroup tile
+
+
+def _pool_map(fn, jobs):
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        return list(ex.map(fn, jobs))
+
+
+def _full_size_checks(items, refs, exact, l2_rows):
+    """items: group dicts (y NaN-filled); refs: (x host, norm_w, packed, scale,
+    N, tag, seed) per item; exact: indices of items whose int32 product is
+    compared with the oracle on every tile row."""
+    with bl.Group(items) as g:
         g.forward()
         torch.cuda.synchronize()
-        worst = 0.0
-        for it, (x, nw, packed, N, tag) in zip(group_items, refs):
-            M = x.shape[0]
-            rows = inputs.sample_rows(M, rows_per, seed=wid)
-            y = host(it["y"][torch.as_tensor(rows, device=DEV)])
-            y_ref = oracle.bitlinear(x[rows], nw, packed, N, EPS)
-            err = rel_l2(y, y_ref)
-            worst = max(worst, err)
-            assert err <= 1e-3, f"{tag}: rel L2 {err}"
-            assert np.all(np.isfinite(host(it["y"][-1]))) and np.all(np.isfinite(host(it["y"][0])))
-    return worst
+    flips = codes = 0
+    l2_jobs, exact_jobs = [], []
+    for i, (it, (x, nw, packed, scale, N, tag, seed)) in enumerate(zip(items, refs)):
+        M, K = x.shape
+        y = it["y"]
+        assert bool(torch.isfinite(y).all()), f"{tag}: output elements left unwritten"
+        rows = inputs.tile_rows(M, TILE_M, seed)
+        assert len(np.unique(rows // TILE_M)) == (M + TILE_M - 1) // TILE_M
+        idx = torch.as_tensor(rows, device=DEV)
+        xq, f = bl.bitlinear_quant(it["x"], it["norm_w"], EPS)
+        acc = bl.bitlinear_matmul_i32(xq, it["packed_w"], N)
+        assert torch.equal(y[idx], _hooks_epilogue(acc[idx], f[idx], scale)), \
+            f"{tag}: group output differs from the hooks' composition"
+        q_ref, f_ref = oracle.quant(x[rows], nw, EPS)
+        flips += check_codes(host(xq[idx]), q_ref, x[rows], nw)
+        codes += q_ref.size
+        check_factor(host(f[idx]), f_ref)
+        del xq, acc
+        lrows = inputs.sample_rows(M, l2_rows, seed=seed)
+        l2_jobs.append((host(y[torch.as_tensor(lrows, device=DEV)]), x[lrows], nw, packed, N, tag))
+        if i in exact:
+            q_all, _ = oracle.quant(x, nw, EPS)
+            acc_o = bl.bitlinear_matmul_i32(dev(q_all), it["packed_w"], N)
+            exact_jobs.append((host(acc_o[idx]), q_all[rows], packed, K, N, tag))
+            del acc_o
+
+    def l2(job):
+        y_gpu, xr, nw, packed, N, tag = job
+        return rel_l2(y_gpu, oracle.bitlinear(xr, nw, packed, N, EPS)), tag
+
+    def exact_eq(job):
+        acc_gpu, qr, packed, K, N, tag = job
+        return np.array_equal(acc_gpu, oracle.matmul_i32(qr, packed, K, N)), tag
+
+    worst = 0.0
+    for err, tag in _pool_map(l2, l2_jobs):
+        assert err <= 1e-3, f"{tag}: rel L2 {err}"
+        worst = max(worst, err)
+    for ok, tag in _pool_map(exact_eq, exact_jobs):
+        assert ok, f"{tag}: int32 product differs from the oracle's"
+    assert flips <= 1e-4 * codes, f"{flips} code flips in {codes}"
+    return worst, flips, codes
 
 
 def test_workload4_full_size_sampled_rows():
@@ -844,11 +937,13 @@ def test_workload4_full_size_sampled_rows():
             packed, scale = oracle.i2s_pack(W)
             nw = inputs.norm_weight(4, layer, pi, K)
             items.append(dict(x=xs[K][1], norm_w=dev(nw), packed_w=dev(packed), w_scale=scale,
-                              eps=EPS, N=N, y=torch.empty((w.M, N), device=DEV)))
-            refs.append((xs[K][0], nw, packed, N, f"layer {layer} {name}"))
-        log(f"workload 4: layer {layer} prepared")
-    worst = _sampled_check(4, 4, items, refs)
-    log(f"workload 4: worst rel L2 {worst:.2e}")
+                              eps=EPS, N=N, y=torch.full((w.M, N), float("nan"), device=DEV)))
+            refs.append((xs[K][0], nw, packed, scale, N, f"layer {layer} {name}", 100 * layer + pi))
+        if layer % 7 == 6:
+            log(f"workload 4: layers 0..{layer} prepared")
+    exact = set(range(len(w.projs))) | set(range(len(items) - len(w.projs), len(items)))
+    worst, flips, codes = _full_size_checks(items, refs, exact, 8)
+    log(f"workload 4: worst rel L2 {worst:.2e}, {flips} code flips in {codes}")
 
 
 def test_workload5_full_size_sampled_rows():
@@ -857,17 +952,10 @@ def test_workload5_full_size_sampled_rows():
     for pi, (name, K, N) in enumerate(w.projs):
         x, nw, packed, scale = proj_inputs(5, 0, pi, w.M, K, N, heavy=True)
         items.append(dict(x=dev(x), norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS,
-                          N=N, y=torch.empty((w.M, N), device=DEV)))
-        refs.append((x, nw, packed, N, name))
-        # Quantization statistics over the whole heavy-tailed activation matrix.
-        xq, f = bl.bitlinear_quant(items[-1]["x"], items[-1]["norm_w"], EPS)
-        rows = inputs.sample_rows(w.M, 256, seed=pi)
-        q_ref, f_ref = oracle.quant(x[rows], nw, EPS)
-        flips = check_codes(host(xq)[rows], q_ref, x[rows], nw)
-        check_factor(host(f)[rows], f_ref)
-        log(f"workload 5 {name}: {flips} flips in {q_ref.size} sampled codes")
-    worst = _sampled_check(5, 16, items, refs)
-    log(f"workload 5: worst rel L2 {worst:.2e}")
+                          N=N, y=torch.full((w.M, N), float("nan"), device=DEV)))
+        refs.append((x, nw, packed, scale, N, name, 500 + pi))
+    worst, flips, codes = _full_size_checks(items, refs, set(range(len(items))), 16)
+    log(f"workload 5: worst rel L2 {worst:.2e}, {flips} code flips in {codes}")
 
 
 # ------------------------------------------------------- device-side packing ---
@@ -943,3 +1031,100 @@ def test_forward_with_device_packed_weights():
     y_h = host(bl.bitlinear_forward(dev(x), dev(nw), dev(ph), sh, N, EPS))
     assert np.array_equal(y_d, y_h)
     assert rel_l2(y_d, oracle.bitlinear(x, nw, ph, N, EPS)) <= 1e-3
+
+
+# ------------------------------------------------- stateless batched call ---
+
+def _mixed_items(seed, specs):
+    """Group-style items over (M, K, N, kind) specs; kind: "plain", "nonorm",
+    "f16", "glu" (SiLU glue) or "shared" (reads the previous item's x)."""
+    items = []
+    for i, (M, K, N, kind) in enumerate(specs):
+        x, nw, packed, scale = proj_inputs(seed, i, 0, M, K, N)
+        it = dict(x=dev(x), norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                  y=torch.full((M, N), float("nan"), device=DEV))
+        if kind == "nonorm":
+            it["norm_w"] = None
+        elif kind == "f16":
+            it["norm_w"] = it["norm_w"].half()
+        elif kind == "glu":
+            it["up"] = dev(inputs.activations(seed, i, 1, M, K))
+            it["act"] = bl.ACT_SILU
+        elif kind == "shared":
+            it["x"] = items[-1]["x"]
+        items.append(it)
+    return items
+
+
+def _single(it):
+    if "up" in it:
+        return bl.bitlinear_glu_forward(it["x"], it["up"], it["act"], it["norm_w"], it["packed_w"],
+                                        it["w_scale"], it["N"], EPS)
+    return bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], it["w_scale"], it["N"], EPS)
+
+
+def test_batched_matches_separate_calls():
+    # Decode (fused, unfused, long rows), prefill, shared inputs, glue, no
+    # norm and float16 norms in one stateless call; then a smaller and a
+    # larger call on the same stream (the second grows the workspace).
+    specs = [(1, 1024, 2048, "plain"), (1, 1024, 1024, "shared"), (1, 3072, 1024, "glu"),
+             (8, 1024, 96, "plain"), (16, 8192, 40, "nonorm"), (300, 2048, 640, "plain"),
+             (300, 2048, 640, "shared"), (40, 640, 256, "f16"), (17, 3072, 100, "glu"),
+             (3, 640, 33, "nonorm"), (0, 1024, 64, "plain")]
+    for seed, sp in ((25, specs), (26, specs[:4]), (27, specs + [(2048, 3072, 1024, "plain")])):
+        items = _mixed_items(seed, sp)
+        bl.bitlinear_forward_batched(items)
+        torch.cuda.synchronize()
+        for it in items:
+            if it["x"].shape[0]:
+                assert torch.equal(it["y"], _single(it)), (seed, it["x"].shape, it["N"])
+        log(f"batched seed {seed}: {len(items)} descriptors bit-identical to single calls")
+    # checked once against the oracle as well
+    x, nw, packed, scale = proj_inputs(27, 5, 0, 300, 2048, 640)
+    assert rel_l2(host(items[5]["y"]), oracle.bitlinear(x, nw, packed, 640, EPS)) <= 1e-3
+
+
+def test_batched_refused_during_capture():
+    items = _mixed_items(28, [(40, 1024, 64, "plain")])
+    bl.bitlinear_forward_batched(items)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        with pytest.raises(bl.BitLinearError) as e:
+            bl.bitlinear_forward_batched(items)
+    assert e.value.status == bl.BL_ERR_UNSUPPORTED
+
+
+def test_captured_forward_survives_workspace_growth_and_release():
+    # A graph captured around an unfused forward holds the workspace's
+    # address.  A later, larger call on the same stream grows the workspace
+    # and bl_release_workspace frees what it can: the captured buffer must
+    # stay allocated, so replays keep reproducing the eager result.
+    M, K, N = 40, 1024, 256
+    x, nw, packed, scale = proj_inputs(29, 0, 0, M, K, N)
+    dx, dn, dp = dev(x), dev(nw), dev(packed)
+    s = torch.cuda.Stream()
+    y = torch.full((M, N), float("nan"), device=DEV)
+    with torch.cuda.stream(s):
+        ref = bl.bitlinear_forward(dx, dn, dp, scale, N, EPS)  # workspace of s exists
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        bl.bitlinear_forward(dx, dn, dp, scale, N, EPS, y=y)
+    M2, K2, N2 = 4096, 3072, 512
+    x2, nw2, packed2, scale2 = proj_inputs(29, 1, 0, M2, K2, N2)
+    with torch.cuda.stream(s):
+        y2 = bl.bitlinear_forward(dev(x2), dev(nw2), dev(packed2), scale2, N2, EPS)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(M2, 8, seed=29)
+    assert rel_l2(host(y2)[rows], oracle.bitlinear(x2[rows], nw2, packed2, N2, EPS)) <= 1e-3
+    bl.bl_release_workspace()
+    junk = torch.full((16 << 20,), 7.0, device=DEV)  # reuse of freed memory would show
+    for rep in range(3):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {rep}"
+    del junk

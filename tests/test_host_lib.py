@@ -246,3 +246,28 @@ def test_f16_norm_weight_validation():
     d[1] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, A, 2)   # unknown norm dtype
     assert bl.lib.bl_group_create(d, 2, ctypes.byref(h)) == bl.BL_ERR_INVALID_ARGUMENT
     assert not h.value
+
+
+def test_batched_validation():
+    # bitlinear_forward_batched validates every descriptor as bl_group_create
+    # does, before any HIP call; descriptors with M = 0 only are a no-op.
+    fb = bl.lib.bitlinear_forward_batched
+    d = (bl.BlDesc * 3)()
+    d[0] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, A)
+    d[1] = bl.BlDesc(A, A, A, 1.0, 1e-6, 700, 1024, 64, A)
+    d[2] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 200, 8, A)  # K % 128
+    assert fb(d, 3, None) == bl.BL_ERR_UNSUPPORTED
+    d[2] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, MIS)
+    assert fb(d, 3, None) == bl.BL_ERR_MISALIGNED
+    d[2] = bl.BlDesc(A, A, A, 0.0, 1e-6, 4, 128, 8, A)  # scale 0
+    assert fb(d, 3, None) == bl.BL_ERR_INVALID_ARGUMENT
+    d[2] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, A, 0, A, 9)  # unknown activation
+    assert fb(d, 3, None) == bl.BL_ERR_INVALID_ARGUMENT
+    d[2] = bl.BlDesc(A, A, A, 1.0, 1e-6, 4, 128, 8, A, 3)  # unknown norm dtype
+    assert fb(d, 3, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert fb(d, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert fb(None, 3, None) == bl.BL_ERR_INVALID_ARGUMENT
+    z = (bl.BlDesc * 2)()
+    z[0] = bl.BlDesc(0, 0, A, 1.0, 1e-6, 0, 128, 8, 0)
+    z[1] = bl.BlDesc(A, A, A, 1.0, 1e-6, 0, 1024, 64, A)
+    assert fb(z, 2, None) == bl.BL_OK
