@@ -361,6 +361,29 @@ bl_status bl_group_destroy(bl_group* g);
  */
 bl_status bitlinear_forward_batched(const bl_desc* descs, int32_t count, void* stream);
 
+/*
+ * bitlinear_forward_noalloc — bitlinear_forward for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): same arguments, same kernels, the same
+ * bits as bitlinear_forward; norm_w float32 or NULL.  It calls no hipMalloc,
+ * hipFree or allocating library routine.
+ * Scratch: an unfused call (every call except the fused decode one of
+ * bitlinear_forward, M <= 3 with rows that fit on chip) keeps its codes,
+ * factors and row sums in a static device array of 64 MiB (67108864 bytes)
+ * inside the library, one per GPU, held until the process ends.  Sizes whose
+ * layout exceeds it, M*K + 2*ceil(4*M/256)*256 bytes with M*K rounded up to
+ * 256, are refused with BL_ERR_UNSUPPORTED (e.g. M = 16384 fits up to K =
+ * 4096, M = 32768 up to K = 2048).
+ * Every call on one GPU shares that GPU's array, from any stream or host
+ * thread, and finds the last call's contents in it: calls that overlap in
+ * time on one GPU race and must be ordered by the caller.  The first call
+ * on a device resolves the array's address (make it outside any capture).
+ * Errors: those of bitlinear_forward, BL_ERR_UNSUPPORTED for the size limit.
+ */
+bl_status bitlinear_forward_noalloc(const float* x, const float* norm_w, const uint8_t* packed_w,
+                                    float w_scale, int64_t M, int64_t K, int64_t N, float eps,
+                                    float* y, void* stream);
+
 /* Frees the per-(device, stream) workspaces and table staging of
  * bitlinear_forward, bitlinear_forward_batched and the hooks (synchronises
  * the device first).  Workspaces a captured graph uses are kept. */

@@ -71,6 +71,7 @@ _SIGS = {
     "bl_group_forward_launch_info": ([_p, _i32, _p, _p, _p], _i32),
     "bl_group_forward_launch": ([_p, _i32, _p], _i32),
     "bitlinear_forward_batched": ([ctypes.POINTER(BlDesc), _i32, _p], _i32),
+    "bitlinear_forward_noalloc": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
     "bl_release_workspace": ([], _i32),
     # measurement probes (include/bitlinear_probe.h)
     "bl_probe_read": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
@@ -194,6 +195,19 @@ def bitlinear_forward(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y
         _dev(x, torch.float32, "x"), nw,
         _dev(packed_w, torch.uint8, "packed_w"), w_scale, M, K, N, eps,
         _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)), "bitlinear_forward")
+    return y
+
+
+def bitlinear_forward_noalloc(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y,
+                              stream=None):
+    """bitlinear_forward with the library's static device scratch instead of
+    its allocated workspace (y must be given: nothing is allocated)."""
+    torch = _torch()
+    M, K = x.shape
+    nw = None if norm_w is None else _dev(norm_w, torch.float32, "norm_w", (K,))
+    _check(_lib.bitlinear_forward_noalloc(
+        _dev(x, torch.float32, "x"), nw, _dev(packed_w, torch.uint8, "packed_w"), w_scale, M, K, N,
+        eps, _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)), "bitlinear_forward_noalloc")
     return y
 
 

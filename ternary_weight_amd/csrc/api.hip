@@ -1168,3 +1168,80 @@ bl_status bitlinear_forward_batched(const bl_desc* descs, int32_t count, void* s
 }
 
 }  // extern "C"
+
+// ------------------------------------------------ allocation-free forward ---
+// bitlinear_forward_noalloc keeps the codes, factors and row sums of an
+// unfused call in `scratch`, a static device array: every GPU that loads the
+// library holds its own copy until the process ends.  On the host the
+// array's name is only a stand-in, not a device address; the address comes
+// from hipGetSymbolAddress, resolved once per device (with that device
+// current) and kept, and only that address is handed to the kernels.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t{64} << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::map<int, uint8_t*> g_scratch;  // device -> address of its scratch
+
+bl_status scratch_address(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BL_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return BL_ERR_HIP;
+    }
+    it = g_scratch.emplace(dev, static_cast<uint8_t*>(p)).first;
+  }
+  *out = it->second;
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bl_status bitlinear_forward_noalloc(const float* x, const float* norm_w, const uint8_t* packed_w,
+                                    float w_scale, int64_t M, int64_t K, int64_t N, float eps,
+                                    float* y, void* stream) {
+  try {
+    bl_status st = check_forward(x, norm_w, packed_w, w_scale, M, K, N, eps, y);
+    if (st != BL_OK || M == 0) return st;
+    const WsLayout l = ws_layout(M, K);
+    const bool fused = M <= kGemvSingleFusedMaxM && gemv_fusable(static_cast<int>(M), static_cast<int>(K));
+    if (!fused && l.bytes > kScratchBytes) return BL_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Prob p{};
+    p.x = x;
+    p.norm_w = norm_w;
+    p.w = packed_w;
+    p.y = y;
+    p.acc = nullptr;
+    p.w_scale = w_scale;
+    p.eps = eps;
+    p.M = static_cast<int>(M);
+    p.K = static_cast<int>(K);
+    p.N = static_cast<int>(N);
+    if (fused) return from_hip(launch_matmul_single(p, false, true, s));
+    uint8_t* ws = nullptr;
+    if ((st = scratch_address(&ws)) != BL_OK) return st;
+    p.xq = reinterpret_cast<int8_t*>(ws + l.xq);
+    p.factor = reinterpret_cast<float*>(ws + l.factor);
+    p.rowsum = reinterpret_cast<int32_t*>(ws + l.rowsum);
+    // The quantization kernel writes every code, factor and row sum of the
+    // M rows before the product reads them: nothing needs clearing.
+    if ((st = from_hip(launch_quant(single_set(p, quant_units(p.M)), p.K, false, kActNone, s))) !=
+        BL_OK)
+      return st;
+    return from_hip(launch_matmul_single(p, false, false, s));
+  } catch (...) {
+    return BL_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

@@ -271,3 +271,15 @@ def test_batched_validation():
     z[0] = bl.BlDesc(0, 0, A, 1.0, 1e-6, 0, 128, 8, 0)
     z[1] = bl.BlDesc(A, A, A, 1.0, 1e-6, 0, 1024, 64, A)
     assert fb(z, 2, None) == bl.BL_OK
+
+
+def test_noalloc_validation():
+    # bitlinear_forward_noalloc validates as bitlinear_forward does, and
+    # refuses a layout past its static scratch, all before any HIP call.
+    f = bl.lib.bitlinear_forward_noalloc
+    assert f(0, A, A, 1.0, 4, 128, 8, 1e-6, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert f(A, A, A, 1.0, 4, 192, 8, 1e-6, A, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, A, MIS, 1.0, 4, 128, 8, 1e-6, A, None) == bl.BL_ERR_MISALIGNED
+    assert f(A, 0, A, 1.0, 0, 128, 8, 1e-6, A, None) == bl.BL_OK           # M = 0
+    assert f(A, A, A, 1.0, 32768, 3072, 8, 1e-6, A, None) == bl.BL_ERR_UNSUPPORTED  # 96 MiB of codes
+    assert f(A, A, A, 1.0, 16384, 4096 + 128, 8, 1e-6, A, None) == bl.BL_ERR_UNSUPPORTED
