@@ -677,14 +677,26 @@ std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs)
 // window the problems' tile lists are merged in proportion to their progress,
 // so output-heavy tiles (small K) run beside compute-heavy ones (large K)
 // instead of after them.  Each problem keeps its own tile order.
+//
+// Then the tiles are dealt to the XCDs.  Consecutive workgroup ids go to the
+// 8 XCDs in turn, and every XCD receives the same number of workgroups, but
+// tiles of different K take different times: a plain split of the list into
+// 8 contiguous ranges gave a launch of three problems (two at K = 1024, one
+// at K = 3072) XCDs with only the long tiles, which finished last.  So each
+// window's merged sequence is cut into 8 contiguous slices and XCD x takes
+// slice x of every window, in window order: every XCD gets the same mix of
+// tiles, and a slice still holds consecutive tiles of each problem (shared
+// activation rows stay in that XCD's L2).  The kernel reads the table entry
+// xcd_remap(b, total) for workgroup b (XCD b % 8, its (b / 8)-th workgroup),
+// so XCD x's k-th tile is stored at entry x*q + min(x, r) + k.
 constexpr size_t kGemmWindowBytes = size_t{2} << 20;
+constexpr int kXcds = 8;
 
 void interleave_gemm_units(StageHost& h) {
-  if (h.probs.size() < 2) return;
+  if (h.units.empty()) return;
   std::vector<int> tiles(h.probs.size(), 0);
   for (const int2& u : h.units) ++tiles[u.x];
-  std::vector<int2> out;
-  out.reserve(h.units.size());
+  std::vector<std::vector<int2>> windows;
   size_t p0 = 0;
   while (p0 < h.probs.size()) {
     size_t p1 = p0, bytes = 0;
@@ -697,6 +709,7 @@ void interleave_gemm_units(StageHost& h) {
     }
     // Merge: repeatedly take the problem whose next tile is least advanced
     // relative to its tile count (ties to the lower index).
+    std::vector<int2> seq;
     std::vector<int> next(p1 - p0, 0);
     for (;;) {
       int best = -1;
@@ -711,9 +724,38 @@ void interleave_gemm_units(StageHost& h) {
         }
       }
       if (best < 0) break;
-      out.push_back(int2{static_cast<int>(p0) + best, next[best]++});
+      seq.push_back(int2{static_cast<int>(p0) + best, next[best]++});
     }
+    windows.push_back(std::move(seq));
     p0 = p1;
+  }
+  // Deal: slice x of every window to XCD x.
+  std::vector<std::vector<int2>> xcd(kXcds);
+  for (const auto& seq : windows) {
+    const size_t L = seq.size();
+    for (int x = 0; x < kXcds; ++x)
+      xcd[x].insert(xcd[x].end(), seq.begin() + L * x / kXcds, seq.begin() + L * (x + 1) / kXcds);
+  }
+  // Exact counts per XCD (q + 1 for the first r): move tiles from the ends
+  // of longer lists to the ends of shorter ones.
+  const size_t total = h.units.size();
+  const size_t q = total / kXcds, r = total % kXcds;
+  auto want = [&](int x) { return q + (static_cast<size_t>(x) < r ? 1 : 0); };
+  std::vector<int2> spill;
+  for (int x = 0; x < kXcds; ++x)
+    while (xcd[x].size() > want(x)) {
+      spill.push_back(xcd[x].back());
+      xcd[x].pop_back();
+    }
+  for (int x = 0; x < kXcds; ++x)
+    while (xcd[x].size() < want(x)) {
+      xcd[x].push_back(spill.back());
+      spill.pop_back();
+    }
+  std::vector<int2> out(total);
+  for (int x = 0; x < kXcds; ++x) {
+    const size_t base = static_cast<size_t>(x) * q + std::min(static_cast<size_t>(x), r);
+    std::copy(xcd[x].begin(), xcd[x].end(), out.begin() + static_cast<std::ptrdiff_t>(base));
   }
   h.units.swap(out);
 }
