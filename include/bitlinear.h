@@ -59,6 +59,7 @@ typedef int32_t bl_status;
 #define BL_ERR_HIP (-5)              /* the HIP runtime reported an error */
 #define BL_ERR_NOMEM (-6)            /* device or host allocation failed */
 #define BL_ERR_INTERNAL (-7)         /* unexpected internal failure */
+#define BL_ERR_NOT_FOUND (-8)        /* bl_gguf_find_tensor: no tensor of that name */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* bl_status_string(bl_status s);
@@ -113,6 +114,45 @@ bl_status i2s_pack(const float* w, int64_t K, int64_t N, uint8_t* packed, size_t
  */
 bl_status i2s_pack_device(const float* w, int64_t K, int64_t N, uint8_t* packed,
                           size_t packed_bytes, float* w_scale_out, void* stream);
+
+/*
+ * bl_gguf_find_tensor — locates a tensor in a GGUF model file held in host
+ * memory, on the host (no GPU call), so that I2_S projection weights and
+ * float16 norm weights can be taken straight from a model file ("BitNet
+ * Embeddings GGUF Conversion Implementation", s2 tensor names such as
+ * "blk.0.attn_q.weight" and "blk.0.attn_q_norm_in.weight", s5, and s6.2: I2_S
+ * is type 36 with quant size (4, 1); s3: the float32 scale is appended to
+ * the packed data).
+ *   file, file_bytes  the whole file image (caller-owned, read only).
+ *   name              NUL-terminated tensor name.
+ *   out               filled on BL_OK:
+ *     type    ggml type id (0 float32, 1 float16, 36 I2_S; others as stored);
+ *     n_dims, dims  dimensions, innermost first (a [N][K] weight has
+ *             dims[0] = K, dims[1] = N);
+ *     offset  byte offset of the tensor's data in the file (the data
+ *             section starts at the next multiple of the uint32
+ *             "general.alignment" value, 32 when absent);
+ *     nbytes  bytes of data: 4 per float32 element, 2 per float16 element,
+ *             elements/4 + 4 for I2_S (the codes, then the float32 scale:
+ *             exactly i2s_packed_bytes(K, N), the buffer bitlinear_forward
+ *             takes, with w_scale its last four bytes); 0 for other types.
+ * Reads GGUF versions 2 and 3, little-endian.  Every read is bounds-checked.
+ * Errors: BL_ERR_INVALID_ARGUMENT (null argument, bad magic, a truncated or
+ * malformed image, data past the end of the file), BL_ERR_UNSUPPORTED
+ * (another version; an I2_S tensor that is not 2-D with K % 128 == 0),
+ * BL_ERR_NOT_FOUND (no tensor of that name).  The in-block order of the codes
+ * is the one this library reads (see above); whether real bitnet.cpp files
+ * store the same order is not pinned here (no such file was available).
+ */
+typedef struct bl_gguf_tensor {
+    int32_t type;
+    int32_t n_dims;
+    int64_t dims[4];
+    uint64_t offset;
+    uint64_t nbytes;
+} bl_gguf_tensor;
+bl_status bl_gguf_find_tensor(const uint8_t* file, size_t file_bytes, const char* name,
+                              bl_gguf_tensor* out);
 
 /*
  * bitlinear_forward — the whole path for one projection on the GPU

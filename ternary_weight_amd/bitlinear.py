@@ -19,6 +19,15 @@ LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m ternary_weight_amd.build`")
 
+# Load torch first when it is installed: it carries its own HIP runtime, and
+# the library must bind to that same runtime (loaded first, the library would
+# pull in the system one, and torch's tensors would then belong to another
+# runtime than the library's kernel launches).
+try:
+    import torch as _torch_first  # noqa: F401
+except ImportError:
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 BL_OK = 0
@@ -29,6 +38,7 @@ BL_ERR_NONFINITE = -4
 BL_ERR_HIP = -5
 BL_ERR_NOMEM = -6
 BL_ERR_INTERNAL = -7
+BL_ERR_NOT_FOUND = -8
 
 _p, _i64, _f32, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32
 
@@ -44,11 +54,18 @@ class BlDesc(ctypes.Structure):
                 ("up", _p), ("act", _i32)]
 
 
+class GgufTensor(ctypes.Structure):
+    """Mirror of ``bl_gguf_tensor``."""
+    _fields_ = [("type", _i32), ("n_dims", _i32), ("dims", _i64 * 4), ("offset", ctypes.c_uint64),
+                ("nbytes", ctypes.c_uint64)]
+
+
 _SIGS = {
     "bl_status_string": ([_i32], ctypes.c_char_p),
     "bl_k_max": ([], _i64),
     "i2s_packed_bytes": ([_i64, _i64], ctypes.c_size_t),
     "i2s_pack": ([_p, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
+    "bl_gguf_find_tensor": ([_p, ctypes.c_size_t, ctypes.c_char_p, ctypes.POINTER(GgufTensor)], _i32),
     "i2s_pack_device": ([_p, _i64, _i64, _p, ctypes.c_size_t, _p, _p], _i32),
     "bitlinear_forward": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
     "bitlinear_quant": ([_p, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
@@ -123,6 +140,32 @@ def i2s_pack(w: np.ndarray) -> tuple[np.ndarray, float]:
     _check(_lib.i2s_pack(w.ctypes.data, K, N, out.ctypes.data, nbytes, ctypes.byref(scale)),
            "i2s_pack")
     return out, float(scale.value)
+
+
+GGUF_F32, GGUF_F16, GGUF_I2S = 0, 1, 36  # ggml type ids
+
+
+def gguf_find_tensor(file: np.ndarray, name: str) -> dict:
+    """A tensor's type, dims (innermost first), data offset and size in a GGUF
+    file image (uint8 numpy array); raises BitLinearError if absent or the
+    image is malformed."""
+    file = np.ascontiguousarray(file, dtype=np.uint8)
+    t = GgufTensor()
+    _check(_lib.bl_gguf_find_tensor(file.ctypes.data, file.size, name.encode(), ctypes.byref(t)),
+           f"bl_gguf_find_tensor({name})")
+    return dict(type=int(t.type), dims=[int(t.dims[i]) for i in range(t.n_dims)],
+                offset=int(t.offset), nbytes=int(t.nbytes))
+
+
+def gguf_i2s_weight(file: np.ndarray, name: str) -> tuple[np.ndarray, float, int, int]:
+    """(I2_S buffer (codes + scale, a view of the file), scale, K, N) of a
+    projection weight stored in a GGUF file image."""
+    t = gguf_find_tensor(file, name)
+    if t["type"] != GGUF_I2S:
+        raise ValueError(f"{name} has ggml type {t['type']}, not I2_S (36)")
+    K, N = t["dims"]
+    buf = np.asarray(file, dtype=np.uint8)[t["offset"]:t["offset"] + t["nbytes"]]
+    return buf, float(buf[-4:].view(np.float32)[0]), K, N
 
 
 # ---------------------------------------------------------------- device ---

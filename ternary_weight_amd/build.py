@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libbitlinear.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "pack_device.hip", "api.hip", "probe.hip"]
-CXX_SOURCES = ["pack.cpp"]
+CXX_SOURCES = ["pack.cpp", "gguf.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -199,6 +199,7 @@ const char* bl_status_string(bl_status s) {
     case BL_ERR_HIP: return "BL_ERR_HIP";
     case BL_ERR_NOMEM: return "BL_ERR_NOMEM";
     case BL_ERR_INTERNAL: return "BL_ERR_INTERNAL";
+    case BL_ERR_NOT_FOUND: return "BL_ERR_NOT_FOUND";
     default: return "BL_ERR_UNKNOWN";
   }
 }

@@ -237,11 +237,14 @@ __device__ __forceinline__ void gemv_body(const Prob& P, const int unit, const i
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(P.w), 0, N * rowbytes, kBufferDword3);
   const int tile0 = (unit * 4 * tpu + wave) * 16;
-  const int wbase = (tile0 + r16) * rowbytes + 16 * g;
+  // Offsets in unsigned arithmetic: rows past N (up to 511 of them) would
+  // overflow a signed product near the 2^31 offset limit; their loads are
+  // replaced by kOob anyway, and an in-range offset is below 2^31.
+  const uint32_t wbase = static_cast<uint32_t>(tile0 + r16) * static_cast<uint32_t>(rowbytes) + 16u * g;
   auto wload = [&](int t, int sb) -> v4i {
     const bool ok = (t < tpu) & (tile0 + 64 * t + r16 < N) & (sb < nsb) & (64 * sb + 16 * g < rowbytes);
-    return __builtin_amdgcn_raw_buffer_load_b128(
-        wrs, ok ? wbase + 64 * t * rowbytes + 64 * sb : kOob, 0, 0);
+    const uint32_t off = wbase + static_cast<uint32_t>(64 * t) * static_cast<uint32_t>(rowbytes) + 64u * sb;
+    return __builtin_amdgcn_raw_buffer_load_b128(wrs, ok ? static_cast<int>(off) : kOob, 0, 0);
   };
   v4i buf[D][kHeld];
 #pragma unroll

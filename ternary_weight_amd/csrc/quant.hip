@@ -101,16 +101,18 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
   }
 }
 
-// Share sets whose norm weights fit in registers alongside the row
-// (share <= quant_set_max(NC)): each wave owns kSetRowsPerWave rows of the
-// set, reads each row once (the next row's loads in flight while the current
-// one is processed), computes its Sum(x^2) once, and emits every problem's
-// codes from the same registers; the set's norm weights are loaded once per
-// wave and widened to f32 (1 where a problem has none: u = x * 1 = x).  Each
-// row's Sum(x^2), max|u| and codes follow the plain variant's order and
+// Share sets (share <= quant_set_max(NC)): each wave owns kSetRowsPerWave
+// rows of the set, reads each row once (the next row's loads in flight while
+// the current one is processed), computes its Sum(x^2) once, and emits every
+// problem's codes from the same registers.  The set's norm weights are
+// staged once per workgroup in LDS, widened to f32 (1 where a problem has
+// none: u = x * 1 = x), and read from there per row: held in registers they
+// cost the K = 1024 kernel half its waves (124 against 76 VGPRs).  Each row's
+// Sum(x^2), max|u| and codes follow the plain variant's order and
 // arithmetic, so results are bit-identical to unshared quantization.
 template <int NC, int SMAX>
 __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
+  __shared__ f4 nws[SMAX][kWave * NC];  // chunk c of member p's norm weight
   const int lane = threadIdx.x & (kWave - 1);
   int local;
   const int pi = find_prob(set, blockIdx.x, &local);
@@ -121,7 +123,6 @@ __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
   float* fac[SMAX];
   int32_t* rsum[SMAX];
   bool norm[SMAX];
-  f4 w[SMAX][NC];
 #pragma unroll
   for (int p = 0; p < SMAX; ++p) {
     if (p >= share) break;
@@ -131,16 +132,15 @@ __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
     rsum[p] = Q.rowsum;
     norm[p] = Q.norm_w != nullptr;
     const int kind = nw_kind(Q);
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = lane + kWave * i;
+    for (int c = threadIdx.x; c < kWave * NC; c += 256) {
       f4 v = f4{1.f, 1.f, 1.f, 1.f};
       if (c >= nch) v = f4{0.f, 0.f, 0.f, 0.f};
       else if (kind == kNwF32) v = nw_chunk<kNwF32>(Q, c);
       else if (kind == kNwF16) v = nw_chunk<kNwF16>(Q, c);
-      w[p][i] = v;
+      nws[p][c] = v;
     }
   }
+  __syncthreads();
   const int m0 = local * kSetRows + wave_id() * kSetRowsPerWave;
   auto load_row = [&](int m, f4 (&xv)[NC]) {
     const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m < P.M ? m : 0) * P.K);
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
       f4 u[NC];
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
-        u[i] = xv[i] * w[p][i];
+        u[i] = xv[i] * nws[p][lane + kWave * i];
         amax = fmaxf(amax, absmax4(u[i]));
       }
       amax = wave_max(amax);
@@ -193,10 +193,9 @@ __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
   }
 }
 
-// Problems per set of the register-resident kernel: their norm weights take
-// at most 16 float4 per lane, and at most 3 problems (a layer's q, k and v;
-// a fourth norm weight would cost the K = 1024 kernel its fourth wave per
-// SIMD).
+// Problems per set of the register-resident kernel: their staged norm
+// weights take at most 16 float4 per lane of LDS (16 KB per workgroup), and
+// at most 3 problems (a layer's q, k and v).
 constexpr int set_max(int nc) { return nc <= 0 ? 0 : (16 / nc < 3 ? (16 / nc < 1 ? 1 : 16 / nc) : 3); }
 int quant_set_max(int nc) { return set_max(nc); }
 

@@ -1128,3 +1128,29 @@ def test_captured_forward_survives_workspace_growth_and_release():
         torch.cuda.synchronize()
         assert torch.equal(y, ref), f"replay {rep}"
     del junk
+
+
+# --------------------------------------------------- weights from a GGUF file ---
+
+def test_forward_from_gguf_image():
+    # A Qwen3-shaped q projection and its float16 per-projection norm stored in
+    # a GGUF image (tests/gguf_file.py), located with bl_gguf_find_tensor and
+    # uploaded as they stand: the forward equals the oracle on the same bytes,
+    # and the float32 forward on the widened norm bit for bit.
+    import gguf_file as gg
+    K, N, M = 1024, 2048, 5
+    packed, scale = oracle.i2s_pack(inputs.weight(32, 0, 0, N, K))
+    nw = inputs.norm_weight(32, 0, 0, K).astype(np.float16)
+    img = gg.write([("general.architecture", gg.STRING, "qwen3")],
+                   [("blk.0.attn_q_norm_in.weight", gg.T_F16, [K], nw.tobytes()),
+                    ("blk.0.attn_q.weight", gg.T_I2S, [K, N], packed.tobytes())])
+    buf, w_scale, K2, N2 = bl.gguf_i2s_weight(img, "blk.0.attn_q.weight")
+    assert (K2, N2) == (K, N) and w_scale == scale
+    t = bl.gguf_find_tensor(img, "blk.0.attn_q_norm_in.weight")
+    nw_dev = dev(img[t["offset"]:t["offset"] + t["nbytes"]].copy()).view(torch.float16)
+    x = inputs.activations(32, 0, 1, M, K)
+    y = bl.bitlinear_forward(dev(x), nw_dev, dev(buf.copy()), w_scale, N, EPS)
+    nw32 = oracle.half_to_float(nw.view(np.uint16))
+    assert rel_l2(host(y), oracle.bitlinear(x, nw32, packed, N, EPS)) <= 1e-3
+    y32 = bl.bitlinear_forward(dev(x), dev(nw32), dev(packed), scale, N, EPS)
+    assert torch.equal(y, y32)
