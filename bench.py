@@ -458,20 +458,19 @@ def bench_prefill(torch, bl, args):
     # each for quantization and product (q/k/v and gate/up then do not share
     # their input's pass).
     per_shape = []
-    if not args.skip_variants:
-        for pi, (name, K, N) in enumerate(w.projs):
-            sel = [i for i, p in enumerate(projs) if p["proj"] == pi]
-            rs = run_prefill_group(torch, bl, [items[i] for i in sel],
-                                   [dict(projs[i], xkey=(i,)) for i in sel], w.M, args,
-                                   max(3, steps // 2))
-            per_shape.append({"proj": name, "K": K, "N": N, "bitlinears": len(sel),
-                              "gemm_us": round(rs["mm_ms"] * 1e3, 1), "gemm_us_stats": rs["mm_us_stats"],
-                              "gemm_TOPS": round(rs["mm_tops"], 1),
-                              "frac_of_peak": round(rs["mm_tops"] / INT8_PEAK_TOPS, 4),
-                              "gemm_bytes_GBps": round(rs["gemm_bytes"] / (rs["mm_ms"] * 1e-3) / 1e9, 1),
-                              "quant_GBps": rs["quant_launches"][0]["GBps"]})
-            log(f"prefill shape {name} {K}->{N} x28: GEMM {rs['mm_ms'] * 1e3:.1f} us "
-                f"({rs['mm_tops']:.0f} TOPS)")
+    for pi, (name, K, N) in enumerate(w.projs):
+        sel = [i for i, p in enumerate(projs) if p["proj"] == pi]
+        rs = run_prefill_group(torch, bl, [items[i] for i in sel],
+                               [dict(projs[i], xkey=(i,)) for i in sel], w.M, args,
+                               max(3, steps // 2))
+        per_shape.append({"proj": name, "K": K, "N": N, "bitlinears": len(sel),
+                          "gemm_us": round(rs["mm_ms"] * 1e3, 1), "gemm_us_stats": rs["mm_us_stats"],
+                          "gemm_TOPS": round(rs["mm_tops"], 1),
+                          "frac_of_peak": round(rs["mm_tops"] / INT8_PEAK_TOPS, 4),
+                          "gemm_bytes_GBps": round(rs["gemm_bytes"] / (rs["mm_ms"] * 1e-3) / 1e9, 1),
+                          "quant_GBps": rs["quant_launches"][0]["GBps"]})
+        log(f"prefill shape {name} {K}->{N} x28: GEMM {rs['mm_ms'] * 1e3:.1f} us "
+            f"({rs['mm_tops']:.0f} TOPS)")
     r.update(projs=projs, xs=xs, M=w.M, no_norm_quant_ms=nn_quant_ms, f16_quant_ms=f16_quant_ms,
              per_shape=per_shape, steps=steps)
     return r
@@ -982,7 +981,12 @@ def main():
             "value": round(lc["tops"], 2), "unit": "TOPS (int8-equivalent)",
             "ms_per_step": round(lc["ms"], 4), "ms_per_step_events": round(lc["ms_events"], 4),
             "step_us_stats": lc["step_us_stats"],
-            "roofline": mfma_roofline(lc, peaks, "gemm_kernel (3 problems, one launch)"),
+            "roofline": mfma_roofline(lc, peaks, "gemm_kernel (3 problems, one launch)", {
+                "traffic": traffic_from_profiles("gemm_long_context_m32768", "gemm.hip"),
+                "mfma_busy_from_counters": profile_value("gemm_long_context_m32768",
+                                                         "mfma_busy_fraction", "gemm.hip"),
+                "clock_GHz_from_counters": profile_value("gemm_long_context_m32768",
+                                                         "effective_clock_GHz", "gemm.hip")}),
             "stages_us": {"quant": round(lc["quant_ms"] * 1e3, 1), "matmul": round(lc["mm_ms"] * 1e3, 1)},
             "quant_launches": lc["quant_launches"],
         }
