@@ -500,6 +500,7 @@ struct GroupStage {
   bool merged = false; // fused decode stage of several superblock counts (one launch)
   bool shared = false; // quantization stages: every unit heads a share set
   int chunks = 0;      // quantization stages: float4 chunks per lane (0: streaming)
+  int set_rows = kSetRowsPerWave;  // shared quantization stages: rows per wave
   int act = kActNone;  // quantization stages: the FFN glue of every problem (kActNone: none)
   bool glue = false;   // decode stages: fused with the FFN glue (Prob::act per problem)
   size_t shmem = 0;    // fused decode stages: LDS bytes, the largest of the problems' own
@@ -589,6 +590,7 @@ struct StageHost {
   std::vector<int2> units;
   std::vector<FatUnit> fat_units;
   int max_m = 0, max_k = 0;
+  int set_rows = kSetRowsPerWave;  // shared quantization stages: rows per wave
   void add(const Prob& p, int nunits, int nsb = 0) {
     ++nprobs;
     const int idx = static_cast<int>(probs.size());
@@ -652,11 +654,23 @@ std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs)
     for (size_t b = 0; b < set.size(); b += cap)
       parts.emplace_back(set.begin() + b, set.begin() + std::min(set.size(), b + cap));
   }
+  // Rows per wave of each shared launch: kSetRowsPerWave, unless that leaves
+  // the launch fewer than kSetFewUnits workgroups.
+  std::map<QuantKey, long> units_at_default;
+  for (const auto& set : parts) {
+    const Prob& lead = probs[set[0]];
+    const int nc = quant_chunks(lead.K);
+    if (set.size() > 1 && nc > 0)
+      units_at_default[QuantKey{nc, true, lead.act}] += quant_set_units(lead.M, kSetRowsPerWave);
+  }
   std::map<QuantKey, StageHost> out;
   for (const auto& set : parts) {
     const Prob& lead = probs[set[0]];
     const int nc = quant_chunks(lead.K);
-    StageHost& h = out[QuantKey{nc, set.size() > 1, lead.act}];
+    const QuantKey key{nc, set.size() > 1, lead.act};
+    StageHost& h = out[key];
+    if (set.size() > 1 && nc > 0)
+      h.set_rows = units_at_default[key] < kSetFewUnits ? 1 : kSetRowsPerWave;
     const int first = static_cast<int>(h.probs.size());
     for (size_t k = 0; k < set.size(); ++k) {
       Prob p = probs[set[k]];
@@ -664,7 +678,8 @@ std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs)
       h.probs.push_back(p);
       ++h.nprobs;
     }
-    const int units = set.size() > 1 && nc > 0 ? quant_set_units(lead.M) : quant_units(lead.M);
+    const int units =
+        set.size() > 1 && nc > 0 ? quant_set_units(lead.M, h.set_rows) : quant_units(lead.M);
     for (int u = 0; u < units; ++u) h.units.push_back(int2{first, u});
     h.max_m = std::max(h.max_m, lead.M);
     h.max_k = std::max(h.max_k, lead.K);
@@ -941,6 +956,7 @@ void plan_bind(const Plan& pl, const uint8_t* tables, bl_group* g) {
     stages[k]->max_m = hosts[k]->max_m;
     stages[k]->max_k = hosts[k]->max_k;
     stages[k]->shmem = hosts[k]->shmem;
+    stages[k]->set_rows = hosts[k]->set_rows;
   }
 }
 
@@ -1004,7 +1020,7 @@ namespace {
 
 bl_status quant_launch(bl_group* g, size_t i, hipStream_t s) {
   const GroupStage& q = g->quant[i];
-  return from_hip(launch_quant(stage_set(q), q.max_k, q.shared, q.act, s));
+  return from_hip(launch_quant(stage_set(q), q.max_k, q.shared, q.act, s, q.set_rows));
 }
 
 }  // namespace

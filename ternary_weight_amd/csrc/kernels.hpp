@@ -22,12 +22,17 @@ constexpr int kGemvMaxM = 16;
 constexpr int kQuantRowsPerWave = 1;
 constexpr int kQuantRows = 4 * kQuantRowsPerWave;
 inline int quant_units(int M) { return (M + kQuantRows - 1) / kQuantRows; }
-// Share-set launches (shared && quant_chunks(K) > 0): kSetRows rows per
-// workgroup, kSetRowsPerWave per wave, and at most quant_set_max(chunks)
-// problems per set (larger sets are split by the caller).
+// Share-set launches (shared && quant_chunks(K) > 0): rows_per_wave rows per
+// wave (kSetRowsPerWave, or 1 for launches that would otherwise have fewer
+// than kSetFewUnits workgroups: there each wave's rows, one after another on
+// a fraction of the CUs, are the launch's critical path), four waves per
+// workgroup, and at most quant_set_max(chunks) problems per set (larger sets
+// are split by the caller).
 constexpr int kSetRowsPerWave = 4;
-constexpr int kSetRows = 4 * kSetRowsPerWave;
-inline int quant_set_units(int M) { return (M + kSetRows - 1) / kSetRows; }
+constexpr int kSetFewUnits = 512;
+inline int quant_set_units(int M, int rows_per_wave) {
+  return (M + 4 * rows_per_wave - 1) / (4 * rows_per_wave);
+}
 int quant_set_max(int nc);
 // Decode kernel: a workgroup owns 64 weight rows of one problem.  Problems
 // are launched in buckets of equal superblock count ceil(K/256) (1..16; 0 =
@@ -48,7 +53,10 @@ int gemm_units(int M, int N);
 // its x).  act: every record's input is act(x) * up (kActSilu, kActGeluTanh;
 // records carry the same value in Prob::act) or x (kActNone); not with shared.
 int quant_chunks(int max_k);
-hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hipStream_t stream);
+// set_rows: rows per wave of a shared launch (kSetRowsPerWave or 1), as its
+// units were counted with.
+hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hipStream_t stream,
+                        int set_rows = kSetRowsPerWave);
 // Row sums of caller-supplied int8 activations (for the raw-integer hook).
 hipError_t launch_rowsum(const Prob& p, hipStream_t stream);
 // Stage 2, M <= kGemvMaxM: weight-streaming MFMA decode kernel for one

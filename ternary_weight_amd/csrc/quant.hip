@@ -101,16 +101,18 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
   }
 }
 
-// Share sets (share <= quant_set_max(NC)): each wave owns kSetRowsPerWave
-// rows of the set, reads each row once (the next row's loads in flight while
-// the current one is processed), computes its Sum(x^2) once, and emits every
-// problem's codes from the same registers.  The set's norm weights are
+// Share sets (share <= quant_set_max(NC)): each wave owns ROWS consecutive
+// rows of the set (kSetRowsPerWave, or 1 for short launches), reads each row
+// once (the next row's loads in flight while the current one is processed,
+// the first row's issued before the norm weights are staged), computes its
+// Sum(x^2) once, and emits every problem's codes from the same registers.
+// The set's norm weights are
 // staged once per workgroup in LDS, widened to f32 (1 where a problem has
 // none: u = x * 1 = x), and read from there per row: held in registers they
 // cost the K = 1024 kernel half its waves (124 against 76 VGPRs).  Each row's
 // Sum(x^2), max|u| and codes follow the plain variant's order and
 // arithmetic, so results are bit-identical to unshared quantization.
-template <int NC, int SMAX>
+template <int NC, int SMAX, int ROWS>
 __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
   __shared__ f4 nws[SMAX][kWave * NC];  // chunk c of member p's norm weight
   const int lane = threadIdx.x & (kWave - 1);
@@ -119,6 +121,17 @@ __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
   const Prob P = prob_at(set, pi);
   const int share = P.share > 1 ? (P.share < SMAX ? P.share : SMAX) : 1;
   const int nch = P.K >> 2;
+  const int m0 = local * 4 * ROWS + wave_id() * ROWS;
+  auto load_row = [&](int m, f4 (&xv)[NC]) {
+    const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m < P.M ? m : 0) * P.K);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      xv[i] = (m < P.M && c < nch) ? f4(__builtin_nontemporal_load(xr + c)) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  f4 xa[NC], xb[NC];
+  load_row(m0, xa);
   int8_t* xq[SMAX];
   float* fac[SMAX];
   int32_t* rsum[SMAX];
@@ -141,23 +154,12 @@ __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
     }
   }
   __syncthreads();
-  const int m0 = local * kSetRows + wave_id() * kSetRowsPerWave;
-  auto load_row = [&](int m, f4 (&xv)[NC]) {
-    const BL_GLOBAL f4* xr = gptr<f4>(P.x + static_cast<int64_t>(m < P.M ? m : 0) * P.K);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = lane + kWave * i;
-      xv[i] = (m < P.M && c < nch) ? f4(__builtin_nontemporal_load(xr + c)) : f4{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  f4 xa[NC], xb[NC];
-  load_row(m0, xa);
-#pragma unroll
-  for (int r = 0; r < kSetRowsPerWave; ++r) {
+  for (int r = 0; r < ROWS; ++r) {
     const int m = m0 + r;
     f4(&xv)[NC] = (r & 1) ? xb : xa;
     f4(&xn)[NC] = (r & 1) ? xa : xb;
-    if (r + 1 < kSetRowsPerWave) load_row(m + 1, xn);
+    if (r + 1 < ROWS) load_row(m + 1, xn);
     if (m >= P.M) break;
     float ss = 0.f;
 #pragma unroll
@@ -289,16 +291,22 @@ int quant_chunks(int max_k) {
     default: hipLaunchKernelGGL(quant_stream_kernel, grid, block, 0, stream, set);            \
   }
 
-hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hipStream_t stream) {
+hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hipStream_t stream,
+                        int set_rows) {
   if (set.total <= 0) return hipSuccess;
   if (shared && act != kActNone) return hipErrorInvalidValue;
+  if (shared && set_rows != 1 && set_rows != kSetRowsPerWave) return hipErrorInvalidValue;
   const int nc = quant_chunks(max_k);
   const dim3 grid(set.total), block(256);
   if (shared && nc > 0) {
     switch (nc) {
 #define BL_QUANT_SET(n)                                                                          \
   case n:                                                                                        \
-    hipLaunchKernelGGL((quant_set_kernel<n, set_max(n)>), grid, block, 0, stream, set);          \
+    if (set_rows == 1)                                                                           \
+      hipLaunchKernelGGL((quant_set_kernel<n, set_max(n), 1>), grid, block, 0, stream, set);    \
+    else                                                                                         \
+      hipLaunchKernelGGL((quant_set_kernel<n, set_max(n), kSetRowsPerWave>), grid, block, 0,     \
+                         stream, set);                                                           \
     break;
       BL_QUANT_SET(1) BL_QUANT_SET(2) BL_QUANT_SET(3) BL_QUANT_SET(4) BL_QUANT_SET(6)
       BL_QUANT_SET(8)
