@@ -274,6 +274,11 @@ bl_status bitlinear_glu_forward_nwf16(const float* gate, const float* up, int32_
  * the input is read once, and each gets its own codes from its own norm_w.
  * Descriptors with up set (the FFN glue) are never shared; they are
  * quantized by glue launches, or fused into decode launches of their own.
+ * A prefill launch whose output tiles all fit on the device at once (one
+ * workgroup per compute unit) runs as long as its largest K: there the K
+ * blocks of the longest problems are split over several workgroups per
+ * output tile (bl_prefill_splits reports the factors), whose int32 partial
+ * sums are added exactly before the epilogue.
  * Results are bit-identical to separate bitlinear_forward (with up:
  * bitlinear_glu_forward) calls on the same inputs.
  */
@@ -311,12 +316,30 @@ typedef struct bl_group bl_group;
 /*
  * bl_group_create — validates every descriptor (same rules as
  * bitlinear_forward), copies the table to the current device, and allocates
- * the group's own workspace and launch tables.  Blocking; may call hipMalloc.
- * The group keeps the descriptors' device pointers: the caller keeps those
- * buffers alive until bl_group_destroy.  Outputs must not alias each other or
- * any input.  count >= 1.
+ * the group's own workspace and launch tables (the workspace also holds the
+ * partial tiles and tile counts of split prefill problems, the counts
+ * cleared here and left cleared by every launch).  Blocking; may call
+ * hipMalloc and hipMemset.  The group keeps the descriptors' device
+ * pointers: the caller keeps those buffers alive until bl_group_destroy.
+ * Outputs must not alias each other or any input.  count >= 1.
  */
 bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out);
+
+/*
+ * bl_prefill_splits — the K split factor each descriptor gets in a group
+ * created on a device with cus compute units (host only, no HIP call):
+ * splits[i] = 1 for decode descriptors (M <= 16), empty ones and unsplit
+ * prefill ones.  When the prefill descriptors' output tiles (128 rows x 256
+ * columns each) number at most cus, the descriptor with the most K blocks
+ * (128 positions) per workgroup has its factor doubled, repeatedly, while the
+ * tiles times factors stay within cus and each split keeps at least 3
+ * blocks (ties go to the earlier descriptor).  cus = 0: no splits.
+ *   descs   host array of count descriptors, validated as by bl_group_create
+ *   splits  host array of count int32 (written on success only)
+ * Errors: BL_ERR_INVALID_ARGUMENT (null splits, cus < 0, or a descriptor
+ * error as in bl_group_create).
+ */
+bl_status bl_prefill_splits(const bl_desc* descs, int32_t count, int32_t cus, int32_t* splits);
 
 /* Both stages for every descriptor, enqueued on stream (quant, then matmul).
  * Fused decode problems (they need no quantization launch) of up to 12

@@ -88,6 +88,7 @@ _SIGS = {
     "bl_group_forward_launch_info": ([_p, _i32, _p, _p, _p], _i32),
     "bl_group_forward_launch": ([_p, _i32, _p], _i32),
     "bitlinear_forward_batched": ([ctypes.POINTER(BlDesc), _i32, _p], _i32),
+    "bl_prefill_splits": ([ctypes.POINTER(BlDesc), _i32, _i32, ctypes.POINTER(_i32)], _i32),
     "bitlinear_forward_noalloc": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
     "bl_release_workspace": ([], _i32),
     # measurement probes (include/bitlinear_probe.h)
@@ -299,6 +300,15 @@ def _descs(items):
                           None if up is None else _dev(up, torch.float32, "up", (M, K)),
                           int(it.get("act", ACT_SILU)) if up is not None else 0)
     return descs
+
+
+def prefill_splits(items, cus: int) -> list[int]:
+    """The K split factor each item would get in a Group on a device with
+    `cus` compute units (1: not split); see bl_prefill_splits."""
+    descs = _descs(items)
+    out = (_i32 * len(items))()
+    _check(_lib.bl_prefill_splits(descs, len(items), int(cus), out), "bl_prefill_splits")
+    return [int(v) for v in out]
 
 
 def bitlinear_forward_batched(items, stream=None) -> None:

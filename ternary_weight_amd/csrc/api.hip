@@ -501,6 +501,7 @@ struct GroupStage {
   bool shared = false; // quantization stages: every unit heads a share set
   int chunks = 0;      // quantization stages: float4 chunks per lane (0: streaming)
   int set_rows = kSetRowsPerWave;  // shared quantization stages: rows per wave
+  bool split = false;  // prefill stages: some problem has K splits
   int act = kActNone;  // quantization stages: the FFN glue of every problem (kActNone: none)
   bool glue = false;   // decode stages: fused with the FFN glue (Prob::act per problem)
   size_t shmem = 0;    // fused decode stages: LDS bytes, the largest of the problems' own
@@ -539,6 +540,7 @@ ProbSet stage_set(const GroupStage& st) {
   s.probs = st.probs;
   s.units = st.units;
   s.total = st.total;
+  s.split = st.split ? 1 : 0;
   return s;
 }
 
@@ -591,6 +593,7 @@ struct StageHost {
   std::vector<FatUnit> fat_units;
   int max_m = 0, max_k = 0;
   int set_rows = kSetRowsPerWave;  // shared quantization stages: rows per wave
+  bool split = false;              // prefill stage: some problem has K splits
   void add(const Prob& p, int nunits, int nsb = 0) {
     ++nprobs;
     const int idx = static_cast<int>(probs.size());
@@ -792,9 +795,61 @@ struct Plan {
 };
 
 struct PlanSizes {
-  size_t ws_bytes = 0;     // codes, factors and row sums of the unfused problems
+  size_t ws_bytes = 0;     // codes, factors and row sums of the unfused problems,
+                           // then the split partial tiles and tile counts
+  size_t cnt_off = 0;      // the tile counts: [cnt_off, cnt_off + cnt_bytes) of it
+  size_t cnt_bytes = 0;
   size_t table_bound = 0;  // upper bound of the table image
 };
+
+// K splits of the prefill problems (one factor per descriptor, 1 = none).
+// A prefill launch whose tiles all fit on the device at once (cus compute
+// units, one workgroup each) runs as long as its longest workgroup, i.e. its
+// largest K: so while the launch still fits, the problem with the most K
+// blocks per workgroup gets its split doubled, as long as each split keeps
+// kGemmMinSplitBlocks blocks.  cus = 0: no splits.
+std::vector<int> gemm_splits(const bl_desc* descs, int32_t count, int cus) {
+  std::vector<int> sp(static_cast<size_t>(count), 1);
+  if (cus <= 0) return sp;
+  auto prefill = [&](int32_t i) { return descs[i].M > kGemvMaxM; };
+  auto tiles = [&](int32_t i) {
+    return static_cast<int64_t>(gemm_units(static_cast<int>(descs[i].M), static_cast<int>(descs[i].N)));
+  };
+  int64_t total = 0;
+  for (int32_t i = 0; i < count; ++i)
+    if (prefill(i)) total += tiles(i);
+  if (total == 0 || total > cus) return sp;
+  for (;;) {
+    int32_t best = -1;
+    int64_t best_nb = 0, best_s = 1;
+    for (int32_t i = 0; i < count; ++i) {
+      if (!prefill(i)) continue;
+      const int64_t nb = descs[i].K / 128;
+      // blocks per workgroup nb / sp[i], compared without division
+      if (best < 0 || nb * best_s > best_nb * sp[i]) {
+        best = i;
+        best_nb = nb;
+        best_s = sp[i];
+      }
+    }
+    if (best < 0) break;
+    const int64_t ns = 2 * best_s;
+    if (best_nb / ns < kGemmMinSplitBlocks) break;
+    const int64_t add = tiles(best) * (ns - best_s);
+    if (total + add > cus) break;
+    total += add;
+    sp[best] = static_cast<int>(ns);
+  }
+  return sp;
+}
+
+// Workspace bytes of the partial tiles of a split prefill problem.
+size_t split_part_bytes(const bl_desc& d, int split) {
+  if (split <= 1) return 0;
+  return round_up(static_cast<size_t>(gemm_units(static_cast<int>(d.M), static_cast<int>(d.N))) *
+                      static_cast<size_t>(split) * kGemmPartInts * 4,
+                  kAlign);
+}
 
 bool desc_fused(const bl_desc& d) {
   return d.M <= kGemvMaxM &&
@@ -803,7 +858,7 @@ bool desc_fused(const bl_desc& d) {
 
 // Validates every descriptor (the rules of bitlinear_forward, plus the glue
 // and norm-weight kind fields) and sizes the plan.
-bl_status plan_sizes(const bl_desc* descs, int32_t count, PlanSizes* out) {
+bl_status plan_sizes(const bl_desc* descs, int32_t count, int cus, PlanSizes* out) {
   if (!descs || count <= 0) return BL_ERR_INVALID_ARGUMENT;
   int64_t units_q = 0, units_v = 0, units_m = 0;
   PlanSizes z;
@@ -833,6 +888,23 @@ bl_status plan_sizes(const bl_desc* descs, int32_t count, PlanSizes* out) {
   }
   if (units_q > INT32_MAX / 2 || units_v > INT32_MAX / 2 || units_m > INT32_MAX / 2)
     return BL_ERR_UNSUPPORTED;
+  // Split prefill problems: partial tiles after the per-problem regions, all
+  // tile counts at the end; their units replace the unsplit ones.
+  const std::vector<int> sp = gemm_splits(descs, count, cus);
+  size_t cnt = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (sp[i] <= 1) continue;
+    const bl_desc& d = descs[i];
+    const size_t t = static_cast<size_t>(gemm_units(static_cast<int>(d.M), static_cast<int>(d.N)));
+    z.ws_bytes += split_part_bytes(d, sp[i]);
+    z.table_bound += t * static_cast<size_t>(sp[i] - 1) * sizeof(int2);
+    cnt += t * sizeof(unsigned);
+  }
+  if (cnt > 0) {
+    z.cnt_off = z.ws_bytes;
+    z.cnt_bytes = round_up(cnt, kAlign);
+    z.ws_bytes += z.cnt_bytes;
+  }
   // every stage holds at least one problem: at most 1 + 2 * count stages,
   // each with three sections padded to kAlign
   z.table_bound += (1 + 2 * static_cast<size_t>(count)) * 3 * kAlign;
@@ -842,9 +914,17 @@ bl_status plan_sizes(const bl_desc* descs, int32_t count, PlanSizes* out) {
 
 // Stage host images of the plan (workspace pointers from ws), then the table
 // image.  Descriptors must have passed plan_sizes.
-void plan_build(const bl_desc* descs, int32_t count, uint8_t* ws, Plan& pl) {
+void plan_build(const bl_desc* descs, int32_t count, int cus, uint8_t* ws, Plan& pl) {
   std::vector<Prob> qprobs;
   size_t off = 0;
+  const std::vector<int> sp = gemm_splits(descs, count, cus);
+  size_t part_off = 0, cnt_total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (descs[i].M == 0) continue;
+    if (!desc_fused(descs[i])) part_off += ws_layout(descs[i].M, descs[i].K).bytes;
+  }
+  size_t cnt_off = part_off;
+  for (int32_t i = 0; i < count; ++i) cnt_off += split_part_bytes(descs[i], sp[i]);
   for (int32_t i = 0; i < count; ++i) {
     const bl_desc& d = descs[i];
     if (d.M == 0) continue;
@@ -883,7 +963,16 @@ void plan_build(const bl_desc* descs, int32_t count, uint8_t* ws, Plan& pl) {
       sh.add(p, gemv_units(p.N, b), merge ? b : 0);
       if (fused) sh.shmem = std::max(sh.shmem, gemv_fused_lds_bytes(p.M, p.K, glue));
     } else {
-      pl.hm.add(p, gemm_units(p.M, p.N));
+      const int t = gemm_units(p.M, p.N);
+      if (sp[i] > 1) {
+        p.ksplit = sp[i];
+        p.part = reinterpret_cast<int32_t*>(ws + part_off);
+        p.tile_cnt = reinterpret_cast<unsigned*>(ws + cnt_off + cnt_total);
+        part_off += split_part_bytes(d, sp[i]);
+        cnt_total += static_cast<size_t>(t) * sizeof(unsigned);
+        pl.hm.split = true;
+      }
+      pl.hm.add(p, t * (sp[i] > 1 ? sp[i] : 1));
     }
   }
   pl.hqs = build_quant_stages(qprobs);
@@ -957,6 +1046,7 @@ void plan_bind(const Plan& pl, const uint8_t* tables, bl_group* g) {
     stages[k]->max_k = hosts[k]->max_k;
     stages[k]->shmem = hosts[k]->shmem;
     stages[k]->set_rows = hosts[k]->set_rows;
+    stages[k]->split = hosts[k]->split;
   }
 }
 
@@ -969,22 +1059,30 @@ bl_status bl_group_create(const bl_desc* descs, int32_t count, bl_group** out) {
     if (!out) return BL_ERR_INVALID_ARGUMENT;
     *out = nullptr;
     PlanSizes sz;
-    bl_status st = plan_sizes(descs, count, &sz);
+    bl_status st = plan_sizes(descs, count, 0, &sz);  // validation first
     if (st != BL_OK) return st;
+    int device = 0, cus = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+      return BL_ERR_HIP;
+    if ((st = plan_sizes(descs, count, cus, &sz)) != BL_OK) return st;
 
     bl_group* g = new (std::nothrow) bl_group;
     if (!g) return BL_ERR_NOMEM;
-    if (hipGetDevice(&g->device) != hipSuccess) {
-      delete g;
-      return BL_ERR_HIP;
-    }
+    g->device = device;
     if (sz.ws_bytes > 0 && hipMalloc(&g->workspace, sz.ws_bytes) != hipSuccess) {
       (void)hipGetLastError();
       free_group(g);
       return BL_ERR_NOMEM;
     }
+    // split prefill tiles: the counts start at zero (each launch leaves them so)
+    if (sz.cnt_bytes > 0 &&
+        hipMemset(static_cast<uint8_t*>(g->workspace) + sz.cnt_off, 0, sz.cnt_bytes) != hipSuccess) {
+      free_group(g);
+      return BL_ERR_HIP;
+    }
     Plan pl;
-    plan_build(descs, count, static_cast<uint8_t*>(g->workspace), pl);
+    plan_build(descs, count, cus, static_cast<uint8_t*>(g->workspace), pl);
     if (hipMalloc(&g->tables, pl.image.size()) != hipSuccess) {
       (void)hipGetLastError();
       free_group(g);
@@ -1186,14 +1284,34 @@ bl_status bl_group_destroy(bl_group* g) {
 
 }  // extern "C"
 
+extern "C" {
+
+bl_status bl_prefill_splits(const bl_desc* descs, int32_t count, int32_t cus, int32_t* splits) {
+  try {
+    if (!splits || cus < 0) return BL_ERR_INVALID_ARGUMENT;
+    PlanSizes sz;
+    const bl_status st = plan_sizes(descs, count, 0, &sz);
+    if (st != BL_OK) return st;
+    const std::vector<int> sp = gemm_splits(descs, count, cus);
+    for (int32_t i = 0; i < count; ++i) splits[i] = sp[static_cast<size_t>(i)];
+    return BL_OK;
+  } catch (...) {
+    return BL_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"
+
 // ------------------------------------------------- stateless batched call ---
 
 extern "C" {
 
 bl_status bitlinear_forward_batched(const bl_desc* descs, int32_t count, void* stream) {
   try {
+    // No K splits here: the workspace is shared between calls of different
+    // plans, so tile counts could not be kept at zero between them.
     PlanSizes sz;
-    bl_status st = plan_sizes(descs, count, &sz);
+    bl_status st = plan_sizes(descs, count, 0, &sz);
     if (st != BL_OK) return st;
     bool any = false;
     for (int32_t i = 0; i < count; ++i) any = any || descs[i].M > 0;
@@ -1208,7 +1326,7 @@ bl_status bitlinear_forward_batched(const bl_desc* descs, int32_t count, void* s
     uint8_t* ws = nullptr;
     if ((st = acquire_ws(s, ws_part + sz.table_bound, &ws)) != BL_OK) return st;
     Plan pl;
-    plan_build(descs, count, ws, pl);
+    plan_build(descs, count, 0, ws, pl);
     if (pl.image.size() > sz.table_bound) return BL_ERR_INTERNAL;
     uint8_t* host = nullptr;
     hipEvent_t done = nullptr;

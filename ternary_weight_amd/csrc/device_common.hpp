@@ -49,6 +49,15 @@ struct Prob {
   // Implementation", s3 tensor types and s6.1: norms are stored as float16),
   // widened exactly to f32 when loaded.
   int nw_f16;
+  // Prefill launches: the K blocks of each output tile are split over ksplit
+  // workgroups (0 or 1: no split).  Each split stores its int32 partial tile
+  // in `part` (ksplit partial tiles per output tile, kGemmPartInts int32
+  // each) and counts itself in tile_cnt[tile]; the last to arrive adds the
+  // other partials and runs the epilogue, then sets the count back to 0
+  // (the counts are zero between launches).
+  int ksplit;
+  int32_t* part;
+  unsigned* tile_cnt;
 };
 
 constexpr int kActNone = 0, kActSilu = 1, kActGeluTanh = 2;
@@ -62,6 +71,7 @@ struct ProbSet {
   const Prob* probs;
   const int2* units;
   int total;  // total work units
+  int split;  // prefill launches: some problem has ksplit > 1
 };
 
 // A work unit that carries its problem record inline: one scalar load finds

@@ -42,6 +42,14 @@
 // loads of the stages still allowed in flight); scheduling barriers keep the
 // LDS reads, waits and MFMAs in the order above.
 //
+// K split (grouped launches whose tiles all fit on the CUs at once, for
+// example one layer at a few hundred tokens): such a launch lasts as long as
+// its longest-K tile, while most CUs idle, so the host planner gives the
+// longest problems several workgroups per output tile, each over a
+// contiguous share of the K blocks.  Each split leaves its int32 partial tile
+// in the workspace, and the last to arrive (a per-tile count) adds the others
+// and runs the epilogue: no workgroup ever waits for another.
+//
 // Bound: int8 MFMA for K >= 2048; for K <= 1024 the fp32 output (4*M*N bytes)
 // weighs as much as the MFMA time.
 #include <type_traits>
@@ -90,7 +98,10 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* ldst) {
                                    (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
 }
 
-template <bool RAW>
+// SPLIT: the launch holds problems with K splits (the split bookkeeping is
+// compiled only into this instance; launches without splits keep the plain
+// kernel's registers).
+template <bool RAW, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
 
@@ -103,9 +114,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   const int M = P.M, K = P.K, N = P.N;
   const int rowbytes = K >> 2;
   const int tiles_n = (N + kTileN - 1) / kTileN;
-  const int m0 = (local / tiles_n) * kTileM;
-  const int n0 = (local % tiles_n) * kTileN;
-  const int nblk = K / kBlockK;
+  // K split: unit `local` is split `split` of output tile `tile` and takes
+  // the tile's K blocks [kb0, kb0 + nblk).
+  const int ks = SPLIT && P.ksplit > 1 ? P.ksplit : 1;
+  const int tile = local / ks, split = local - tile * ks;
+  const int m0 = (tile / tiles_n) * kTileM;
+  const int n0 = (tile % tiles_n) * kTileN;
+  const int kb0 = (K / kBlockK) * split / ks;
+  const int nblk = (K / kBlockK) * (split + 1) / ks - kb0;
 
   // This lane's direct-load sources (32-bit offsets from the problem's
   // bases): for activation instruction i the lane fills LDS row
@@ -116,14 +132,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   for (int i = 0; i < kXLoads; ++i) {
     const int row = 32 * wave + 8 * i + (lane >> 3);
     const int slot = xs_slot(row, lane & 7);
-    xoff[i] = min(m0 + row, M - 1) * K + slot * 16;
+    xoff[i] = min(m0 + row, M - 1) * K + kb0 * kBlockK + slot * 16;
   }
   int woff[kWLoads];
 #pragma unroll
   for (int i = 0; i < kWLoads; ++i) {
     const int row = 64 * wave + 32 * i + (lane >> 1);
     const int slot = ws_slot(row, lane & 1);
-    woff[i] = min(n0 + row, N - 1) * rowbytes + slot * 16;
+    woff[i] = min(n0 + row, N - 1) * rowbytes + kb0 * (kBlockK / 4) + slot * 16;
   }
   auto issue = [&](int kb, int slot_off) {
     uint8_t* st = smem + slot_off;
@@ -261,6 +277,62 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   for (; kb + 1 < nblk; ++kb) stage(Yes{}, kb);
   stage(No{}, kb);
 
+  if (SPLIT && ks > 1) {
+    // Split tiles.  Each split stores its accumulators, counts itself in,
+    // and the last split to arrive adds the others' partials in its
+    // registers, resets the count and runs the epilogue; int32 sums are
+    // exact in any order, so the result equals the unsplit product bit for
+    // bit.  The splits may run on different XCDs, each with its own L2, so
+    // the partials are written and read with the sc1 cache policy (the one
+    // the compiler gives agent-scope atomic accesses: coherent across the
+    // XCDs), and every wave's stores have completed (vmcnt 0, then the
+    // barrier) before the count is raised.  A device-scope fence instead
+    // would write back and invalidate the whole L2 of the XCD, the other
+    // workgroups' cached operands included (measured: the launch took 50%
+    // longer than unsplit).  Layout: 16-byte piece p of lane l of wave w of
+    // split s at ((s*4 + w)*32 + p)*64 + l within the tile's partials, so
+    // each store instruction writes 1 KB contiguously.
+    constexpr int kSc1 = 16;  // cache policy bits: sc1
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        P.part + static_cast<int64_t>(tile) * ks * kGemmPartInts, 0, ks * kGemmPartInts * 4, kBufferDword3);
+    auto poff = [&](int s, int p) { return (s * (kGemmPartInts / 4) + (wave * 32 + p) * 64 + lane) * 16; };
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v4i{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2], acc[fn][fm][4 * q + 3]},
+              prs, poff(split, (fn * 2 + fm) * 4 + q), 0, kSc1);
+    asm volatile("" ::: "memory");
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave's partial is stored; every wave is past the ring
+    volatile int* flag = reinterpret_cast<volatile int*>(smem);
+    if (threadIdx.x == 0) {
+      const unsigned before = __hip_atomic_fetch_add(gptr_out<unsigned>(P.tile_cnt) + tile, 1u,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = before == static_cast<unsigned>(ks - 1);
+    }
+    __syncthreads();
+    if (*flag == 0) return;  // (uniform) another split finishes this tile
+    for (int s = 0; s < ks; ++s) {
+      if (s == split) continue;
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v4i v = __builtin_amdgcn_raw_buffer_load_b128(prs, poff(s, (fn * 2 + fm) * 4 + q), 0, kSc1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[fn][fm][4 * q + i] += v[i];
+          }
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(gptr_out<unsigned>(P.tile_cnt) + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
   // Epilogue.  Fragment (fn, fm) lane holds weight rows 8q + 4g + r (q, r in
   // 0..3) of activation row r32: a store straight from there would write
   // 32 B into each of 32 rows per instruction.  Instead each 32-row half of
@@ -328,10 +400,13 @@ int gemm_units(int M, int N) {
 hipError_t launch_gemm(const ProbSet& set, bool raw, hipStream_t stream) {
   if (set.total <= 0) return hipSuccess;
   const dim3 grid(set.total), block(256);
-  if (raw)
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, block, 0, stream, set);
-  else
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, block, 0, stream, set);
+  if (set.split) {
+    if (raw) hipLaunchKernelGGL((gemm_kernel<true, true>), grid, block, 0, stream, set);
+    else hipLaunchKernelGGL((gemm_kernel<false, true>), grid, block, 0, stream, set);
+  } else {
+    if (raw) hipLaunchKernelGGL((gemm_kernel<true, false>), grid, block, 0, stream, set);
+    else hipLaunchKernelGGL((gemm_kernel<false, false>), grid, block, 0, stream, set);
+  }
   return hipGetLastError();
 }
 

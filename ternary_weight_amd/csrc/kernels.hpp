@@ -44,7 +44,11 @@ constexpr int kGemvSingleUnits = 512;
 int gemv_units(int N, int bucket, int tiles = 0);
 int gemv_single_tiles(int N, int bucket);
 int gemv_bucket(int K);
-int gemm_units(int M, int N);
+int gemm_units(int M, int N);  // output tiles of one prefill problem
+// One prefill output tile of int32 partial sums (Prob::part), and the
+// fewest K blocks (128 positions each) a split of a tile may take.
+constexpr int kGemmPartInts = 128 * 256;
+constexpr int kGemmMinSplitBlocks = 3;
 
 // Stage 1: fused RMSNorm + absmax int8 quantization of every row in the set.
 // max_k: the largest K in the set (it selects the register-resident variant:

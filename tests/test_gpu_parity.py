@@ -1084,6 +1084,58 @@ def test_batched_matches_separate_calls():
     assert rel_l2(host(items[5]["y"]), oracle.bitlinear(x, nw, packed, 640, EPS)) <= 1e-3
 
 
+SPLIT_GROUPS = [
+    # The Gemma3-270M layer at M = 512 (q, k, v and gate, up sharing x): o is
+    # split 2 ways and down 4 ways on a 256-CU device.
+    [(512, 640, 1024, "plain"), (512, 640, 256, "shared"), (512, 640, 256, "shared"),
+     (512, 1024, 640, "plain"), (512, 640, 2048, "plain"), (512, 640, 2048, "shared"),
+     (512, 2048, 640, "plain")],
+    # Ragged rows and columns, uneven block splits (K = 3200: 25 blocks),
+    # float16 and no norm weights, a decode problem beside them.
+    [(300, 4096, 256, "plain"), (17, 3200, 520, "f16"), (129, 1536, 100, "nonorm"),
+     (1, 1024, 64, "plain"), (40, 6272, 32, "plain")],
+]
+
+
+@pytest.mark.parametrize("gi", range(len(SPLIT_GROUPS)))
+def test_group_split_prefill(gi):
+    # Split prefill tiles (partial int32 tiles added by the last split to
+    # arrive) against single calls, which never split: bit for bit, over
+    # repeated forwards (the tile counts must come back to zero) and over
+    # replays of a captured forward.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    items = _mixed_items(40 + gi, SPLIT_GROUPS[gi])
+    splits = bl.prefill_splits(items, cus)
+    log(f"split group {gi}: splits {splits} on {cus} CUs")
+    assert max(splits) > 1
+    singles = [_single(it) for it in items]
+    with bl.Group(items) as g:
+        for rep in range(4):
+            for it in items:
+                it["y"].fill_(float("nan"))
+            g.forward()
+            torch.cuda.synchronize()
+            for i, (it, ys) in enumerate(zip(items, singles)):
+                assert torch.equal(it["y"], ys), (gi, rep, i)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            g.forward()
+        for rep in range(3):
+            for it in items:
+                it["y"].fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for i, (it, ys) in enumerate(zip(items, singles)):
+                assert torch.equal(it["y"], ys), (gi, "replay", rep, i)
+    # the most-split problem against the oracle as well
+    i = int(np.argmax(splits))
+    M, K, N, kind = SPLIT_GROUPS[gi][i]
+    assert kind == "plain"
+    x, nw, packed, scale = proj_inputs(40 + gi, i, 0, M, K, N)
+    assert rel_l2(host(items[i]["y"]), oracle.bitlinear(x, nw, packed, N, EPS)) <= 1e-3
+
+
 def test_batched_refused_during_capture():
     items = _mixed_items(28, [(40, 1024, 64, "plain")])
     bl.bitlinear_forward_batched(items)

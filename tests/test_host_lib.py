@@ -225,6 +225,44 @@ def test_group_validation():
     assert lib.bl_group_forward_launch_info(None, 0, None, None, None) == bl.BL_ERR_INVALID_ARGUMENT
 
 
+def _splits(shapes, cus):
+    d = (bl.BlDesc * len(shapes))()
+    for i, (M, K, N) in enumerate(shapes):
+        d[i] = bl.BlDesc(A, A, A, 1.0, 1e-6, M, K, N, A)
+    out = (ctypes.c_int32 * len(shapes))()
+    st = bl.lib.bl_prefill_splits(d, len(shapes), cus, out)
+    return st, list(out)
+
+
+GEMMA3_M512 = [(512, K, N) for _, K, N in inputs.GEMMA3_270M]
+
+
+def test_prefill_splits():
+    # Gemma3-270M layer at M = 512: 112 output tiles (q 16, k 4, v 4, o 12,
+    # gate 32, up 32, down 12) with 5, 5, 5, 8, 5, 5, 16 K blocks.  Doubling
+    # the most blocks per workgroup: down -> 2 (8 blocks; 124 tiles), o -> 2
+    # (o comes first at 8 = 16/2; 136), down -> 4 (160); then q at 5 blocks
+    # would keep 2 < 3: stop.
+    assert _splits(GEMMA3_M512, 256) == (bl.BL_OK, [1, 1, 1, 2, 1, 1, 4])
+    assert _splits(GEMMA3_M512, 124) == (bl.BL_OK, [1, 1, 1, 1, 1, 1, 2])
+    assert _splits(GEMMA3_M512, 135) == (bl.BL_OK, [1, 1, 1, 1, 1, 1, 2])
+    assert _splits(GEMMA3_M512, 112) == (bl.BL_OK, [1] * 7)   # no room for any split
+    assert _splits(GEMMA3_M512, 111) == (bl.BL_OK, [1] * 7)   # does not fit at once
+    assert _splits(GEMMA3_M512, 0) == (bl.BL_OK, [1] * 7)
+    # one long-K problem: 3 tiles, 32 blocks -> 8 (4 blocks each; 16 would leave 2 < 3)
+    assert _splits([(300, 4096, 256)], 256) == (bl.BL_OK, [8])
+    assert _splits([(300, 4096, 256)], 12) == (bl.BL_OK, [4])
+    # decode and empty descriptors are never split; M = 17 is prefill
+    assert _splits([(16, 4096, 256), (0, 4096, 256), (17, 4096, 256)], 256) == (bl.BL_OK, [1, 1, 8])
+    # the 28-layer Qwen3-0.6B stack at M = 16384 has far more tiles than CUs
+    stack = [(16384, K, N) for _, K, N in inputs.QWEN3_06B] * 28
+    assert _splits(stack, 256) == (bl.BL_OK, [1] * len(stack))
+    assert _splits([(512, 1024, 64)], -1)[0] == bl.BL_ERR_INVALID_ARGUMENT
+    assert _splits([(512, 1000, 64)], 256)[0] == bl.BL_ERR_UNSUPPORTED  # K % 128
+    d = (bl.BlDesc * 1)(bl.BlDesc(A, A, A, 1.0, 1e-6, 512, 1024, 64, A))
+    assert bl.lib.bl_prefill_splits(d, 1, 256, None) == bl.BL_ERR_INVALID_ARGUMENT
+
+
 def test_f16_norm_weight_validation():
     # the float16 norm weight calls validate exactly as their float32 twins
     f, q = bl.lib.bitlinear_forward_nwf16, bl.lib.bitlinear_quant_nwf16
