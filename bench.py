@@ -385,7 +385,8 @@ def run_prefill_group(torch, bl, items, projs, M, args, steps):
     qbytes = quant_bytes_by_launch(M, projs)
     quant_launches = []
     for d, t in zip(info[:-1], launch_ms[:-1]):
-        nb = qbytes.get((d["kind"], d["bucket"]))
+        # a merged launch (small groups) does every set's work
+        nb = sum(qbytes.values()) if d["kind"] == "quant_merged" else qbytes.get((d["kind"], d["bucket"]))
         mean = float(np.mean(t))
         quant_launches.append(dict(kind=d["kind"], chunks=d["bucket"], bitlinears=d["count"],
                                    us=round(mean * 1e3, 1), us_stats=us_stats(t), bytes=nb,

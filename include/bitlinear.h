@@ -294,6 +294,8 @@ bl_status bitlinear_glu_forward_nwf16(const float* gate, const float* up, int32_
 #define BL_LAUNCH_QUANT_GLUE 5   /* FFN glue + RMSNorm + int8 quantization of unfused
                                     descriptors with up set (one activation per launch) */
 #define BL_LAUNCH_DECODE_FUSED_GLUE 6 /* BL_LAUNCH_DECODE_FUSED for descriptors with up set */
+#define BL_LAUNCH_QUANT_MERGED 7 /* BL_LAUNCH_QUANT and BL_LAUNCH_QUANT_SHARED work of a
+                                    small group in one launch (see bl_group_quant) */
 typedef struct bl_desc {
     const float* x;          /* device [M][K] */
     const void* norm_w;      /* device [K] float32 (float16 if norm_w_f16), or NULL: no norm */
@@ -357,7 +359,11 @@ bl_status bl_group_forward(bl_group* g, void* stream);
  * launch per register-resident chunk count ceil(K/256) class (1, 2, 3, 4, 6,
  * 8, 12, 16 chunks of 256; 0 = rows longer than 4096) and kind (single
  * descriptors, glue descriptors with SiLU, with GELU-tanh, then share sets),
- * in increasing chunk count. */
+ * in increasing chunk count.  A small group whose quantization would take
+ * several such launches, none of them glue or longer rows, and at most 8192
+ * rows in all (one row per wave of 2048 workgroups) runs it as one launch of
+ * kind BL_LAUNCH_QUANT_MERGED instead (bucket 0): small launches cost their
+ * fixed launch time, not their work.  Same codes, factors and row sums. */
 bl_status bl_group_quant(bl_group* g, void* stream);
 /* Stage 2 only: integer product + epilogue for every descriptor, reading the
  * workspace written by the last bl_group_quant on the same stream (fused
@@ -385,8 +391,9 @@ bl_status bl_group_matmul_launch_info(const bl_group* g, int32_t i, int32_t* kin
 bl_status bl_group_matmul_launch(bl_group* g, int32_t i, void* stream);
 /* The whole forward as individual launches: first the quantization launches
  * of bl_group_quant (kind BL_LAUNCH_QUANT, BL_LAUNCH_QUANT_GLUE or
- * BL_LAUNCH_QUANT_SHARED, bucket = the chunk count, count = descriptors
- * quantized), then the matmul launches.
+ * BL_LAUNCH_QUANT_SHARED, bucket = the chunk count; or the one
+ * BL_LAUNCH_QUANT_MERGED launch, bucket 0; count = descriptors quantized),
+ * then the matmul launches.
  * bl_group_forward == every forward launch in order.
  *   bl_group_forward_launches: number of launches (-1 for a NULL group). */
 int32_t bl_group_forward_launches(const bl_group* g);

@@ -44,7 +44,7 @@ _p, _i64, _f32, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c
 
 # BL_LAUNCH_* of include/bitlinear.h
 LAUNCH_KINDS = {0: "decode", 1: "prefill", 2: "quant", 3: "decode_fused", 4: "quant_shared",
-                5: "quant_glue", 6: "decode_fused_glue"}
+                5: "quant_glue", 6: "decode_fused_glue", 7: "quant_merged"}
 
 
 class BlDesc(ctypes.Structure):

@@ -9,8 +9,9 @@
 #include <cstring>
 #include <map>
 #include <mutex>
-#include <tuple>
 #include <new>
+#include <set>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -618,6 +619,8 @@ struct StageHost {
 // one, each by the register-resident chunk count of their K.  Sets keep the
 // order of their first problem.  Glue problems (act(x) * up) never share;
 // they go to launches of their own per activation.
+constexpr int kQuantMergedChunks = -1;  // QuantKey::chunks of the merged launch
+
 struct QuantKey {
   int chunks;
   bool shared;
@@ -656,6 +659,40 @@ std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs)
     }
     for (size_t b = 0; b < set.size(); b += cap)
       parts.emplace_back(set.begin() + b, set.begin() + std::min(set.size(), b + cap));
+  }
+  // Small groups: every set in one merged launch (one row per wave) when the
+  // separate launches would be several, all register-resident and without
+  // the glue, and at most kQuantMergeMaxUnits workgroups in all.
+  {
+    std::set<std::pair<int, bool>> kinds;
+    int64_t units = 0;
+    bool ok = true;
+    for (const auto& set : parts) {
+      const Prob& lead = probs[set[0]];
+      const int nc = quant_chunks(lead.K);
+      if (nc == 0 || lead.act != kActNone) ok = false;
+      kinds.insert({nc, set.size() > 1});
+      units += quant_units(lead.M);
+    }
+    if (ok && kinds.size() > 1 && units <= kQuantMergeMaxUnits) {
+      std::map<QuantKey, StageHost> out;
+      StageHost& h = out[QuantKey{kQuantMergedChunks, false, kActNone}];
+      h.set_rows = 1;
+      for (const auto& set : parts) {
+        const Prob& lead = probs[set[0]];
+        const int first = static_cast<int>(h.probs.size());
+        for (size_t k = 0; k < set.size(); ++k) {
+          Prob p = probs[set[k]];
+          p.share = k == 0 ? static_cast<int>(set.size()) : 0;
+          h.probs.push_back(p);
+          ++h.nprobs;
+        }
+        for (int u = 0; u < quant_units(lead.M); ++u) h.units.push_back(int2{first, u});
+        h.max_m = std::max(h.max_m, lead.M);
+        h.max_k = std::max(h.max_k, lead.K);
+      }
+      return out;
+    }
   }
   // Rows per wave of each shared launch: kSetRowsPerWave, unless that leaves
   // the launch fewer than kSetFewUnits workgroups.
@@ -1118,6 +1155,7 @@ namespace {
 
 bl_status quant_launch(bl_group* g, size_t i, hipStream_t s) {
   const GroupStage& q = g->quant[i];
+  if (q.chunks == kQuantMergedChunks) return from_hip(launch_quant_merged(stage_set(q), s));
   return from_hip(launch_quant(stage_set(q), q.max_k, q.shared, q.act, s, q.set_rows));
 }
 
@@ -1247,10 +1285,13 @@ bl_status bl_group_forward_launch_info(const bl_group* g, int32_t i, int32_t* ki
   if (!g || i < 0 || i >= bl_group_forward_launches(g)) return BL_ERR_INVALID_ARGUMENT;
   const int32_t q = static_cast<int32_t>(g->quant.size());
   if (i >= q) return bl_group_matmul_launch_info(g, i - q, kind, bucket, count);
+  const bool merged = g->quant[i].chunks == kQuantMergedChunks;
   if (kind)
-    *kind = g->quant[i].shared ? BL_LAUNCH_QUANT_SHARED
-                               : (g->quant[i].act != kActNone ? BL_LAUNCH_QUANT_GLUE : BL_LAUNCH_QUANT);
-  if (bucket) *bucket = g->quant[i].chunks;
+    *kind = merged ? BL_LAUNCH_QUANT_MERGED
+                   : (g->quant[i].shared ? BL_LAUNCH_QUANT_SHARED
+                                         : (g->quant[i].act != kActNone ? BL_LAUNCH_QUANT_GLUE
+                                                                        : BL_LAUNCH_QUANT));
+  if (bucket) *bucket = merged ? 0 : g->quant[i].chunks;
   if (count) *count = g->quant[i].count;
   return BL_OK;
 }

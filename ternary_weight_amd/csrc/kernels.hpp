@@ -61,6 +61,15 @@ int quant_chunks(int max_k);
 // units were counted with.
 hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hipStream_t stream,
                         int set_rows = kSetRowsPerWave);
+// Every quantization of a small group in one launch: units of share sets
+// (Prob::share > 1, chunk count quant_chunks(K) <= 8) and of single
+// problems (quant_chunks(K) > 0), no FFN glue, all at one row per wave
+// (quant_units(M) units per set or problem).  Used for groups whose
+// quantization would otherwise take several launches and at most
+// kQuantMergeMaxUnits workgroups: launches that small cost their fixed
+// launch time, not their work.
+constexpr int kQuantMergeMaxUnits = 2048;
+hipError_t launch_quant_merged(const ProbSet& set, hipStream_t stream);
 // Row sums of caller-supplied int8 activations (for the raw-integer hook).
 hipError_t launch_rowsum(const Prob& p, hipStream_t stream);
 // Stage 2, M <= kGemvMaxM: weight-streaming MFMA decode kernel for one

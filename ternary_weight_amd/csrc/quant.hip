@@ -26,6 +26,8 @@
 // GGUF Conversion Implementation" s4.5) form a share set in a grouped launch:
 // one pass reads the row and its Sum(x^2) once and emits every projection's
 // codes, so the input is read once instead of once per projection.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace bl {
@@ -112,12 +114,17 @@ __global__ __launch_bounds__(256) void quant_reg_kernel(ProbSet set) {
 // cost the K = 1024 kernel half its waves (124 against 76 VGPRs).  Each row's
 // Sum(x^2), max|u| and codes follow the plain variant's order and
 // arithmetic, so results are bit-identical to unshared quantization.
+// nws: LDS for SMAX * kWave * NC float4 (chunk c of member p's norm weight
+// at p * kWave * NC + c).
+// Problems per set of the register-resident kernel: their staged norm
+// weights take at most 16 float4 per lane of LDS (16 KB per workgroup), and
+// at most 3 problems (a layer's q, k and v).
+constexpr int set_max(int nc) { return nc <= 0 ? 0 : (16 / nc < 3 ? (16 / nc < 1 ? 1 : 16 / nc) : 3); }
+int quant_set_max(int nc) { return set_max(nc); }
+
 template <int NC, int SMAX, int ROWS>
-__global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
-  __shared__ f4 nws[SMAX][kWave * NC];  // chunk c of member p's norm weight
+__device__ __forceinline__ void quant_set_rows(const ProbSet& set, int pi, int local, f4* nws) {
   const int lane = threadIdx.x & (kWave - 1);
-  int local;
-  const int pi = find_prob(set, blockIdx.x, &local);
   const Prob P = prob_at(set, pi);
   const int share = P.share > 1 ? (P.share < SMAX ? P.share : SMAX) : 1;
   const int nch = P.K >> 2;
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
       if (c >= nch) v = f4{0.f, 0.f, 0.f, 0.f};
       else if (kind == kNwF32) v = nw_chunk<kNwF32>(Q, c);
       else if (kind == kNwF16) v = nw_chunk<kNwF16>(Q, c);
-      nws[p][c] = v;
+      nws[p * kWave * NC + c] = v;
     }
   }
   __syncthreads();
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
       f4 u[NC];
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
-        u[i] = xv[i] * nws[p][lane + kWave * i];
+        u[i] = xv[i] * nws[p * kWave * NC + lane + kWave * i];
         amax = fmaxf(amax, absmax4(u[i]));
       }
       amax = wave_max(amax);
@@ -195,11 +202,67 @@ __global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
   }
 }
 
-// Problems per set of the register-resident kernel: their staged norm
-// weights take at most 16 float4 per lane of LDS (16 KB per workgroup), and
-// at most 3 problems (a layer's q, k and v).
-constexpr int set_max(int nc) { return nc <= 0 ? 0 : (16 / nc < 3 ? (16 / nc < 1 ? 1 : 16 / nc) : 3); }
-int quant_set_max(int nc) { return set_max(nc); }
+
+template <int NC, int SMAX, int ROWS>
+__global__ __launch_bounds__(256) void quant_set_kernel(ProbSet set) {
+  __shared__ f4 nws[SMAX * kWave * NC];
+  int local;
+  const int pi = find_prob(set, blockIdx.x, &local);
+  quant_set_rows<NC, SMAX, ROWS>(set, pi, local, nws);
+}
+
+// Largest LDS staging of a share set (float4), over the chunk counts that
+// share (1..8).
+constexpr int set_lds_f4(int nc) { return set_max(nc) * kWave * nc; }
+constexpr int kMergedNwsF4 = 1024;
+static_assert(set_lds_f4(1) <= kMergedNwsF4 && set_lds_f4(2) <= kMergedNwsF4 &&
+                  set_lds_f4(3) <= kMergedNwsF4 && set_lds_f4(4) <= kMergedNwsF4 &&
+                  set_lds_f4(6) <= kMergedNwsF4 && set_lds_f4(8) <= kMergedNwsF4,
+              "merged staging");
+
+// Every quantization of a small group in one launch: each workgroup runs
+// the body of its unit's kind (share set or single problem) and chunk count
+// quant_chunks(K), one row per wave, four per workgroup.  The bodies are the
+// separate launches' own, so the codes, factors and row sums are the same.
+__global__ __launch_bounds__(256) void quant_merged_kernel(ProbSet set) {
+  __shared__ f4 nws[kMergedNwsF4];
+  const int lane = threadIdx.x & (kWave - 1);
+  int local;
+  const int pi = find_prob(set, blockIdx.x, &local);
+  const Prob P = prob_at(set, pi);
+  const int m_begin = local * kQuantRows + wave_id() * kQuantRowsPerWave;
+  static_assert(kQuantRowsPerWave == 1, "one row per wave, as quant_set_rows<..., 1>");
+  const int nc = (P.K + 255) >> 8;
+  if (P.share > 1) {
+    switch (nc) {
+      case 1: quant_set_rows<1, set_max(1), 1>(set, pi, local, nws); break;
+      case 2: quant_set_rows<2, set_max(2), 1>(set, pi, local, nws); break;
+      case 3: quant_set_rows<3, set_max(3), 1>(set, pi, local, nws); break;
+      case 4: quant_set_rows<4, set_max(4), 1>(set, pi, local, nws); break;
+      case 5: case 6: quant_set_rows<6, set_max(6), 1>(set, pi, local, nws); break;
+      case 7: case 8: quant_set_rows<8, set_max(8), 1>(set, pi, local, nws); break;
+      default: break;  // not planned
+    }
+    return;
+  }
+  auto rows = [&](auto ncc) {
+    constexpr int C = decltype(ncc)::value;
+    switch (nw_kind(P)) {
+      case kNwF32: quant_reg_rows<C, kActNone, kNwF32>(P, m_begin, lane); break;
+      case kNwF16: quant_reg_rows<C, kActNone, kNwF16>(P, m_begin, lane); break;
+      default: quant_reg_rows<C, kActNone, kNwNone>(P, m_begin, lane);
+    }
+  };
+  using std::integral_constant;
+  if (nc <= 1) rows(integral_constant<int, 1>{});
+  else if (nc <= 2) rows(integral_constant<int, 2>{});
+  else if (nc <= 3) rows(integral_constant<int, 3>{});
+  else if (nc <= 4) rows(integral_constant<int, 4>{});
+  else if (nc <= 6) rows(integral_constant<int, 6>{});
+  else if (nc <= 8) rows(integral_constant<int, 8>{});
+  else if (nc <= 12) rows(integral_constant<int, 12>{});
+  else rows(integral_constant<int, 16>{});
+}
 
 // Rows longer than the register budget: two streaming passes over the row.
 __device__ void quant_stream_row(const Prob& P, int m, int lane);
@@ -323,6 +386,12 @@ hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hip
     BL_QUANT_SWITCH(quant_reg_kernel, , kActNone)
   }
 #undef BL_QUANT_SWITCH
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_merged(const ProbSet& set, hipStream_t stream) {
+  if (set.total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_merged_kernel, dim3(set.total), dim3(256), 0, stream, set);
   return hipGetLastError();
 }
 

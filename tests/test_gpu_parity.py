@@ -291,11 +291,12 @@ def test_forward_matches_hooks_bitwise(M, K):
 
 
 def test_group_forward_launch_kinds_and_order():
-    # The forward as launches: quantization of the problems not fused (by
-    # chunk count: K 1024 -> 4, 4096 -> 16), the merged fused decode launch
-    # (3 and 4 superblocks: their fp32 rows fit the on-chip staging; bucket
-    # reported as 0), the unfused decode launch (16 superblocks), then the
-    # prefill launch.
+    # The forward as launches: quantization of the problems not fused (K 1024
+    # -> 4 chunks, 4096 -> 16: two classes, so one merged launch for this
+    # small group, bucket 0), the merged fused decode launch (3 and 4
+    # superblocks: their fp32 rows fit the on-chip staging; bucket reported
+    # as 0), the unfused decode launch (16 superblocks), then the prefill
+    # launch.
     specs = [(1, 1024, 64), (8, 640, 40), (16, 4096, 32), (3, 1024, 48), (40, 1024, 72),
              (2, 4096, 24)]
     items, singles = [], []
@@ -307,9 +308,9 @@ def test_group_forward_launch_kinds_and_order():
         singles.append(bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], scale, N, EPS))
     with bl.Group(items) as g:
         info = g.forward_launches()
-        assert [d["kind"] for d in info] == ["quant", "quant", "decode_fused", "decode", "prefill"]
-        assert [d["bucket"] for d in info] == [4, 16, 0, 16, 0]
-        assert [d["count"] for d in info] == [1, 2, 3, 2, 1]
+        assert [d["kind"] for d in info] == ["quant_merged", "decode_fused", "decode", "prefill"]
+        assert [d["bucket"] for d in info] == [0, 0, 16, 0]
+        assert [d["count"] for d in info] == [3, 3, 2, 1]
         for i in range(len(info)):
             g.forward_launch(i)
         torch.cuda.synchronize()
@@ -405,11 +406,13 @@ def test_group_matches_separate_calls():
             assert torch.equal(it["y"], ys)
 
 
-def test_group_shared_input_quantization():
+@pytest.mark.parametrize("M", [300, 2304])
+def test_group_shared_input_quantization(M):
     # Projections reading one x (q/k/v-like, gate/up-like) share a pass of
     # the quantization launch; a projection on the same x with another eps,
-    # or on a prefix view of x with another M, must not join the set.
-    M = 300
+    # or on a prefix view of x with another M, must not join the set.  At
+    # M = 300 the group's quantization is one merged launch; at M = 2304 it
+    # needs more than 2048 workgroups, so the classes launch separately.
     x = dev(inputs.activations(21, 0, 0, M, 1024))
     x2 = dev(inputs.activations(21, 0, 1, M, 2048))
     specs = [(x, 1024, 512, EPS), (x, 1024, 256, EPS), (x2, 2048, 384, EPS), (x, 1024, 128, EPS),
@@ -425,8 +428,12 @@ def test_group_shared_input_quantization():
         singles.append(bl.bitlinear_forward(xx, nw, it["packed_w"], scale, N, eps))
     with bl.Group(items) as g:
         info = g.forward_launches()
-        assert [(d["kind"], d["bucket"], d["count"]) for d in info[:3]] == [
-            ("quant", 4, 2), ("quant_shared", 4, 3), ("quant_shared", 8, 2)]
+        if M == 300:
+            assert (info[0]["kind"], info[0]["bucket"], info[0]["count"]) == ("quant_merged", 0, 7)
+            assert not any(d["kind"].startswith("quant") for d in info[1:])
+        else:
+            assert [(d["kind"], d["bucket"], d["count"]) for d in info[:3]] == [
+                ("quant", 4, 2), ("quant_shared", 4, 3), ("quant_shared", 8, 2)]
         g.forward()
         torch.cuda.synchronize()
         for i, (it, ys) in enumerate(zip(items, singles)):
@@ -440,12 +447,14 @@ def test_group_shared_input_quantization():
         assert rel_l2(host(items[i]["y"]), ref) <= 1e-3
 
 
-def test_group_large_share_sets_split():
+@pytest.mark.parametrize("M", [260, 2304])
+def test_group_large_share_sets_split(M):
     # Share sets larger than the register-resident share kernel holds (3
     # problems at K <= 1024, 2 at K = 2048) are split; every part still reads
     # x once and gives bit-identical results to separate calls, with norm
-    # weights of every kind (float32, float16, none) inside one set.
-    M = 260
+    # weights of every kind (float32, float16, none) inside one set.  At
+    # M = 260 the parts run in one merged launch, at M = 2304 in launches per
+    # class.
     x = dev(inputs.activations(27, 0, 0, M, 1024))
     x2 = dev(inputs.activations(27, 0, 1, M, 2048))
     specs = [(x, 1024, 64 * (i + 1), ("f32", "f16", "none")[i % 3]) for i in range(6)] + \
@@ -463,7 +472,10 @@ def test_group_large_share_sets_split():
         q = sorted((d["kind"], d["bucket"], d["count"]) for d in g.forward_launches()
                    if d["kind"].startswith("quant"))
         # K = 1024: two parts of 3, one launch; K = 2048: a part of 2 and a single
-        assert q == [("quant", 8, 1), ("quant_shared", 4, 6), ("quant_shared", 8, 2)], q
+        if M == 260:
+            assert q == [("quant_merged", 0, 9)], q
+        else:
+            assert q == [("quant", 8, 1), ("quant_shared", 4, 6), ("quant_shared", 8, 2)], q
         g.forward()
         torch.cuda.synchronize()
         for i, (it, ys) in enumerate(zip(items, singles)):
@@ -631,7 +643,9 @@ def test_no_norm_group_mixed_with_normed_share_set():
                 singles.append(bl.bitlinear_forward(x, nw, it["packed_w"], scale, N, EPS))
     with bl.Group(items) as g:
         kinds = [d["kind"] for d in g.forward_launches()]
-        assert "quant_shared" in kinds and "decode_fused" in kinds
+        # share sets at K = 1024, single problems at K = 3072 (12 chunks): one
+        # merged quantization launch for this small group
+        assert "quant_merged" in kinds and "decode_fused" in kinds
         g.forward()
         torch.cuda.synchronize()
         for i, (it, ys) in enumerate(zip(items, singles)):
@@ -704,7 +718,8 @@ def test_f16_norm_weight_group_mixed_kinds():
             singles.append(bl.bitlinear_forward(x, nw, it["packed_w"], scale, N, EPS))
     with bl.Group(items) as g:
         kinds = [d["kind"] for d in g.forward_launches()]
-        assert "quant_shared" in kinds and "decode_fused" in kinds and "prefill" in kinds
+        # a set of 3 and a single at M = 300: one merged quantization launch
+        assert "quant_merged" in kinds and "decode_fused" in kinds and "prefill" in kinds
         g.forward()
         torch.cuda.synchronize()
         for i, (it, ys) in enumerate(zip(items, singles)):
