@@ -492,8 +492,11 @@ def bench_gemma_layer(torch, bl, args):
             xs[key] = torch.from_numpy(xs_host[key]).to(dev)
         p["xkey"] = key
     items = prefill_items(torch, projs, xs, w.M, dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    splits = bl.prefill_splits(items, cus)
     r = run_prefill_group(torch, bl, items, projs, w.M, args, args.steps)
-    r.update(projs=projs, xs_host=xs_host, M=w.M)
+    r.update(projs=projs, xs_host=xs_host, M=w.M, cus=cus,
+             splits={names[p["proj"]]: s for p, s in zip(projs, splits)})
     return r
 
 
@@ -925,6 +928,8 @@ def main():
                                        "note": "launch/latency-bound: 5.7 G ops is 1.1 us at the MFMA peak"}),
             "stages_us": {"quant": round(g3["quant_ms"] * 1e3, 2), "matmul": round(g3["mm_ms"] * 1e3, 2)},
             "quant_launches": g3["quant_launches"],
+            # K split of each projection in the prefill launch (bl_prefill_splits)
+            "k_splits": g3["splits"], "cus": g3["cus"],
         }
         log(f"gemma3 layer M=512: {g3['ms'] * 1e3:.1f} us/step, GEMM {g3['mm_ms'] * 1e3:.1f} us "
             f"({g3['mm_tops']:.0f} TOPS), quant {g3['quant_ms'] * 1e3:.1f} us")
@@ -983,7 +988,7 @@ def main():
             "ms_per_step": round(lc["ms"], 4), "ms_per_step_events": round(lc["ms_events"], 4),
             "step_us_stats": lc["step_us_stats"],
             "roofline": mfma_roofline(lc, peaks, "gemm_kernel (3 problems, one launch)", {
-                "traffic": traffic_from_profiles("gemm_long_context_m32768", "gemm.hip"),
+                "traffic": profile_value("gemm_long_context_m32768", "traffic_bytes_per_launch", "gemm.hip"),
                 "mfma_busy_from_counters": profile_value("gemm_long_context_m32768",
                                                          "mfma_busy_fraction", "gemm.hip"),
                 "clock_GHz_from_counters": profile_value("gemm_long_context_m32768",
