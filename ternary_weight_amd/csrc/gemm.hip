@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
       for (int i = 0; i < 4; ++i) a[i] = field_codes(static_cast<uint32_t>(w[fn][i]), j);
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm)
-        acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bx[fm], acc[fn][fm], 0, 0, 0);
+        acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bx[fm], a, acc[fn][fm], 0, 0, 0);
     }
   };
   // All waves' direct loads visible, and every wave past its reads so far.
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
       for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
         for (int fm = 0; fm < 2; ++fm)
-          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a3[fn], bx[3][fm], acc[fn][fm], 0, 0, 0);
+          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bx[3][fm], a3[fn], acc[fn][fm], 0, 0, 0);
     } else {
       mma_step(wp, bx[3], 3, 0, 4);
     }
@@ -333,64 +333,52 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
       __hip_atomic_store(gptr_out<unsigned>(P.tile_cnt) + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // Epilogue.  Fragment (fn, fm) lane holds weight rows 8q + 4g + r (q, r in
-  // 0..3) of activation row r32: a store straight from there would write
-  // 32 B into each of 32 rows per instruction.  Instead each 32-row half of
-  // the wave tile (fm) is scaled, transposed through the now idle stage ring
-  // (16 KB per wave, 16-byte slots XOR-swizzled by row) and written back so
-  // that each store instruction covers two full 512-byte row segments.
+  // Epilogue.  The activation fragment is the MFMA's A operand and the
+  // weight fragment its B operand, so fragment (fn, fm) lane l holds output
+  // column (weight row) l % 32 of the fragment, for the activation rows
+  // i = 8q + 4g + r of its registers 4q + r (q, r in 0..3, g = l / 32).  A
+  // register stored as one dword per lane then writes two full 128-byte row
+  // segments (32 consecutive columns of rows i and i + 4): no transposition
+  // through LDS.  With the operands the other way round (each lane 16
+  // columns of one row) the stores had to go through an LDS transposition
+  // to avoid 32-byte row pieces; the prefill launches were 1-8% slower.
+  // The tile's row scales and row sums go through LDS once.
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();  // every wave is done with the last stage
+  __builtin_amdgcn_s_barrier();  // every wave is done with the ring
   asm volatile("" ::: "memory");
-  uint8_t* tbuf = smem + wave * (32 * 512);
-  const int nw0 = n0 + wn * 128;  // first output column of this wave
+  float* lsc = reinterpret_cast<float*>(smem);
+  int* lrs = reinterpret_cast<int*>(smem + 4 * kTileM);
+  if (threadIdx.x < kTileM) {
+    const int m = min(m0 + static_cast<int>(threadIdx.x), M - 1);
+    lsc[threadIdx.x] = RAW ? 0.f : gptr<float>(P.factor)[m] / P.w_scale;
+    lrs[threadIdx.x] = gptr<int32_t>(P.rowsum)[m];
+  }
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  const int ncol = n0 + wn * 128 + r32;  // this lane's column in fragment fn = 0
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm) {
-    const int mbase = m0 + wm * 64 + fm * 32;
-    {
-      const int m = mbase + r32;
-      const bool mok = m < M;
-      const int rs = mok ? gptr<int32_t>(P.rowsum)[m] : 0;
-      float scale = 0.f;
-      if (!RAW && mok) scale = gptr<float>(P.factor)[m] / P.w_scale;
+  for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
+    for (int q = 0; q < 4; ++q) {
+      const int il = wm * 64 + fm * 32 + 8 * q + 4 * g;  // the first of this lane's 4 rows
+      const f4 sc = *reinterpret_cast<const f4*>(lsc + il);
+      const v4i rs = *reinterpret_cast<const v4i*>(lrs + il);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int slot = fn * 8 + 2 * q + g;  // 16-byte column slot (4 outputs)
-          v4i v = v4i{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
-                      acc[fn][fm][4 * q + 3]} - rs;
-          if (!RAW) {
-            const f4 out = f4{static_cast<float>(v[0]) * scale, static_cast<float>(v[1]) * scale,
-                              static_cast<float>(v[2]) * scale, static_cast<float>(v[3]) * scale};
-            v = __builtin_bit_cast(v4i, out);
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + il + r;
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+          const int n = ncol + fn * 32;
+          if (m < M && n < N) {
+            // Non-temporal: the output is written once and not read back here.
+            const int v = acc[fn][fm][4 * q + r] - rs[r];
+            const int64_t o = static_cast<int64_t>(m) * N + n;
+            if (RAW) __builtin_nontemporal_store(v, gptr_out<int32_t>(P.acc) + o);
+            else __builtin_nontemporal_store(static_cast<float>(v) * sc[r], gptr_out<float>(P.y) + o);
           }
-          *reinterpret_cast<v4i*>(tbuf + r32 * 512 + ((slot ^ r32) & 31) * 16) = v;
-        }
-    }
-    // Read back row-contiguous: lane covers slot (lane % 32) of row 2i + lane/32.
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 2 * i + g;
-      const int slot = lane & 31;
-      const v4i v = *reinterpret_cast<const v4i*>(tbuf + row * 512 + ((slot ^ row) & 31) * 16);
-      const int m = mbase + row;
-      const int n = nw0 + 4 * slot;
-      if (m >= M || n >= N) continue;
-      const int64_t o = static_cast<int64_t>(m) * N + n;
-      if ((N & 3) == 0) {
-        // Non-temporal: the output is written once and not read back here.
-        if (RAW) __builtin_nontemporal_store(v, gptr_out<v4i>(P.acc + o));
-        else __builtin_nontemporal_store(__builtin_bit_cast(f4, v), gptr_out<f4>(P.y + o));
-      } else {
-        const f4 fv = __builtin_bit_cast(f4, v);
-        for (int e = 0; e < 4 && n + e < N; ++e) {
-          if (RAW) gptr_out<int32_t>(P.acc)[o + e] = v[e];
-          else gptr_out<float>(P.y)[o + e] = fv[e];
         }
       }
     }
-  }
 }
 
 int gemm_units(int M, int N) {
