@@ -903,7 +903,9 @@ def main():
             "weight_GBps": round(w1["weight_GBps"], 1),
             "roofline": {"bound": "hbm", "kernel": "quant_reg_kernel + gemv_kernel (one call, two launches)",
                          "achieved": round(w1["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(w1["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(w1["GBps"] / HBM_PEAK_GBS, 4),
+                         # HBM bytes of the call's decode launch (the dominant one)
+                         "traffic": profile_value("gemv_single_m8", "traffic_bytes_per_launch", "gemv.hip"),
                          "algorithmic_bytes_per_call": w1["bytes"],
                          "launch_floor_us": round(w1["floor_us"], 2),
                          "call_over_two_launch_floors": round(st["median"] / (2 * w1["floor_us"]), 2),
@@ -925,6 +927,9 @@ def main():
             "step_us_stats": g3["step_us_stats"],
             "roofline": mfma_roofline(g3, peaks, "gemm_kernel (7 problems, one launch)",
                                       {"launch_floor_us": peaks["launch_floor_us"],
+                                       # HBM bytes of the GEMM launch, K-split partials included
+                                       "traffic": profile_value("gemm_gemma3_layer_m512",
+                                                                "traffic_bytes_per_launch", "gemm.hip"),
                                        "note": "launch/latency-bound: 5.7 G ops is 1.1 us at the MFMA peak"}),
             "stages_us": {"quant": round(g3["quant_ms"] * 1e3, 2), "matmul": round(g3["mm_ms"] * 1e3, 2)},
             "quant_launches": g3["quant_launches"],
