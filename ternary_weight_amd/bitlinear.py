@@ -171,19 +171,45 @@ def gguf_i2s_weight(file: np.ndarray, name: str) -> tuple[np.ndarray, float, int
 
 # ---------------------------------------------------------------- device ---
 
+# torch and the few of its entry points the hot path uses, bound once: a
+# small projection's call is a few microseconds of GPU time, and per-call
+# module lookups and Stream objects cost the host as much.
+_TORCH = None
+_TENSOR = None
+_RAW_STREAM = None  # current stream's raw handle by device index, where torch offers it
+_GET_DEVICE = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH, _TENSOR, _RAW_STREAM, _GET_DEVICE
+    if _TORCH is None:
+        import torch
+        _TENSOR = torch.Tensor
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _GET_DEVICE = getattr(torch._C, "_cuda_getDevice", None)
+        _TORCH = torch
+    return _TORCH
 
 
 def _stream_handle(stream) -> int | None:
-    torch = _torch()
+    """The HIP stream handle: the given stream's, or the current stream's."""
     if stream is None:
+        torch = _torch()
+        if _RAW_STREAM is not None and _GET_DEVICE is not None:
+            return _RAW_STREAM(_GET_DEVICE())
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def _dev(t, dtype, name: str, shape=None) -> int:
+    """t's device pointer after checking that t is a contiguous GPU tensor of
+    dtype (and shape); one combined test on the common path, the specific
+    error otherwise."""
+    if _TENSOR is None:
+        _torch()
+    if (isinstance(t, _TENSOR) and t.is_cuda and t.dtype is dtype and t.is_contiguous()
+            and (shape is None or t.shape == shape)):
+        return t.data_ptr()
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
