@@ -26,6 +26,7 @@ durations come from HIP events on the stream the kernels run on and are
 reported as mean, median, p10 and p90.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-prefill] [--skip-cpu]
+                    [--library-reference]
 """
 from __future__ import annotations
 
@@ -76,6 +77,9 @@ def parse():
     # The GPU clock needs tens of milliseconds of load to settle: with 5
     # warmup steps (1 ms) the decode launch measured 203 us against 196 us.
     ap.add_argument("--min-warmup-ms", type=float, default=300.0)
+    ap.add_argument("--library-reference", action="store_true",
+                    help="also time the platform's int8 GEMM (torch._int_mm, hipBLASLt) on the stack's "
+                         "shapes, as context for the prefill GEMM's rate (not part of the path)")
     return ap.parse_args()
 
 
@@ -638,6 +642,32 @@ def bench_device_pack(torch, bl, args):
                          "algorithmic_bytes_per_call": nbytes}}
 
 
+def library_reference(torch) -> dict:
+    """The platform library's int8 GEMM on the Qwen3-0.6B stack shapes at
+    M = 16384, as context for the prefill GEMM: torch._int_mm (int8 x int8 ->
+    int32, hipBLASLt) with plain int8 weights (four times the packed bytes, no
+    unpacking, no scale epilogue), one product per call, B column-major (the
+    faster of its two layouts here).  Not part of the path."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    M = 16384
+    res = {}
+    for name, K, N in (("q", 1024, 2048), ("k", 1024, 1024), ("o", 2048, 1024),
+                       ("gate", 1024, 3072), ("down", 3072, 1024)):
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+        b = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev, generator=g).t()
+        call = lambda: torch._int_mm(a, b)
+        mean_ms, _ = time_calls(torch, call, 30, 5, 200.0)
+        us = mean_ms * 1e3
+        ops = 2 * M * N * K
+        res[name] = {"K": K, "N": N, "us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),
+                     "frac": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)}
+        del a, b
+    return {"what": "torch._int_mm (hipBLASLt) int8 x int8 -> int32 on plain int8 weights, M=16384, "
+                    "one GEMM per call; context only", "per_shape": res}
+
+
 def measure_peaks(torch, bl):
     """Sustained HBM read / copy bandwidth and int8 MFMA rate of this GPU (probes)."""
     dev = torch.device("cuda")
@@ -1015,6 +1045,11 @@ def main():
             f"glue-fed down forward {glue['forward_ms']:.3f} ms ({glue['forward_TOPS']:.0f} TOPS); "
             f"M=1 one-launch glue forward {glue['decode_M1_forward_us']:.1f} us")
         out["ffn_glue"] = glue
+    if args.library_reference:
+        ref = library_reference(torch)
+        log("library int8 GEMM reference: " + ", ".join(
+            f"{k} {v['TOPS']:.0f} TOPS" for k, v in ref["per_shape"].items()))
+        out["library_reference"] = ref
     dp = bench_device_pack(torch, bl, args)
     log(f"device pack: {dp['us']:.1f} us ({dp['roofline']['achieved']:.0f} GB/s)")
     out["device_pack"] = dp
