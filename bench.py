@@ -696,7 +696,14 @@ def measure_peaks(torch, bl):
     write = {}
     for nt in (False, True):
         write[nt] = max(nbytes / timed(lambda: bl.probe_write(buf, b, nt)) / 1e9 for b in (4096, 16384))
-    del buf, src, dst
+    # reads with one 16-byte write per 64 (or 16) 16-byte reads: HBM under a
+    # decode launch's kind of traffic (its outputs are about 1.2% of its bytes)
+    mixed = {}
+    msrc, mdst = buf[: nbytes // 2], buf[nbytes // 2: nbytes // 2 + (128 << 20)]
+    for rd in (64, 16):
+        moved = msrc.numel() * (1 + 1 / rd)
+        mixed[rd] = max(moved / timed(lambda: bl.probe_mixed(msrc, mdst, rd, sink, b)) / 1e9 for b in (1024, 2048))
+    del buf, src, dst, msrc, mdst
     # Launch floor: back-to-back launches of a one-workgroup kernel that
     # writes 16 bytes (what any launch costs on this stream).
     tiny = torch.empty(256, dtype=torch.uint8, device=dev)
@@ -720,6 +727,8 @@ def measure_peaks(torch, bl):
             "copy_GBps_read_plus_write": round(copy, 1),
             "hbm_write_GBps": round(max(write.values()), 1),
             "hbm_write_by_kind": {"plain": round(write[False], 1), "nontemporal": round(write[True], 1)},
+            "hbm_mixed_GBps": {"1_write_per_64_reads": round(mixed[64], 1),
+                               "1_write_per_16_reads": round(mixed[16], 1)},
             "launch_floor_us": round(floor_us, 2),
             "mfma_i8_TOPS": round(max(mfma.values()), 1),
             "mfma_i8_TOPS_by_shape": {f"{k}x{k}": round(v, 1) for k, v in mfma.items()}}
@@ -908,6 +917,10 @@ def main():
         "measured_peaks": peaks,
     }
     out["roofline"]["frac_of_measured"] = round(dom["GBps"] / peaks["hbm_read_GBps"], 4)
+    # against this box's reads with 1.5% of the bytes written (the decode
+    # launch writes 1.2%): writes mixed into a read stream cost more than their bytes
+    out["roofline"]["frac_of_measured_mixed"] = round(
+        dom["GBps"] / peaks["hbm_mixed_GBps"]["1_write_per_64_reads"], 4)
     if not args.skip_variants:
         for key, what in (("no_norm", "the decode step with norm_w NULL on every projection "
                                       "(no per-projection norm)"),

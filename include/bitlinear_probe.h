@@ -34,6 +34,17 @@ bl_status bl_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks
  * nontemporal != 0 uses non-temporal stores. */
 bl_status bl_probe_write(void* dst, size_t bytes, int32_t blocks, int32_t nontemporal, void* stream);
 
+/* Mixed read/write stream: `blocks` workgroups of 256 threads read every
+ * 16-byte word of src once (non-temporal) and, per 256 * reads_per_write
+ * words read, write 256 words of dst (non-temporal, values independent of
+ * the reads): src_bytes / reads_per_write bytes written in all.
+ * reads_per_write is 16 or 64 (a write share of 6% or 1.5% of the bytes,
+ * near a decode launch's output share); src_bytes is a nonzero multiple of
+ * 4096 * reads_per_write, dst holds at least src_bytes / reads_per_write
+ * bytes, both 16-byte aligned.  sink: as for bl_probe_read. */
+bl_status bl_probe_mixed(const void* src, size_t src_bytes, void* dst, size_t dst_bytes,
+                         int32_t reads_per_write, uint32_t* sink, int32_t blocks, void* stream);
+
 /* int8 matrix-core throughput: each of `blocks` workgroups of 4 waves runs,
  * per wave on register operands, either (shape 16) 4*iters
  * v_mfma_i32_16x16x64_i8 in four independent chains or (shape 32) 2*iters

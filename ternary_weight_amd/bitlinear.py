@@ -95,6 +95,7 @@ _SIGS = {
     "bl_probe_read": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
     "bl_probe_copy": ([_p, _p, ctypes.c_size_t, _i32, _p], _i32),
     "bl_probe_write": ([_p, ctypes.c_size_t, _i32, _i32, _p], _i32),
+    "bl_probe_mixed": ([_p, ctypes.c_size_t, _p, ctypes.c_size_t, _i32, _p, _i32, _p], _i32),
     "bl_probe_mfma_i8": ([_i32, _i32, _i32, _p, _p], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -444,6 +445,14 @@ def probe_write(dst, blocks: int, nontemporal: bool = False, stream=None) -> Non
     torch = _torch()
     _check(_lib.bl_probe_write(_dev(dst, torch.uint8, "dst"), dst.numel(), blocks, int(nontemporal),
                                _stream_handle(stream)), "bl_probe_write")
+
+
+def probe_mixed(src, dst, reads_per_write: int, sink, blocks: int, stream=None) -> None:
+    """Mixed read/write probe over uint8 device tensors (see bitlinear_probe.h)."""
+    torch = _torch()
+    _check(_lib.bl_probe_mixed(_dev(src, torch.uint8, "src"), src.numel(), _dev(dst, torch.uint8, "dst"),
+                               dst.numel(), reads_per_write, _dev(sink, torch.int32, "sink"), blocks,
+                               _stream_handle(stream)), "bl_probe_mixed")
 
 
 def probe_mfma_i8(iters: int, blocks: int, sink, shape: int = 16, stream=None) -> None:

@@ -8,6 +8,8 @@
 //     counters: its traffic is known exactly);
 //   * streaming write: every byte of a buffer written once (the prefill
 //     kernel's output stream without any compute);
+//   * mixed stream: reads with one write per 16 or 64 of them (the decode
+//     kernel's mix of weight reads and output writes without any compute);
 //   * int8 MFMA: back-to-back v_mfma_i32_16x16x64_i8 on register operands.
 #include "../../include/bitlinear_probe.h"
 #include "kernels.hpp"
@@ -52,6 +54,25 @@ __global__ __launch_bounds__(256) void probe_write_kernel(v4i* __restrict__ dst,
     if (NT) __builtin_nontemporal_store(v, dst + i);
     else dst[i] = v;
   }
+}
+
+// Mixed stream: block unit b reads the 256*RD 16-byte words at 256*RD*b of
+// src (each wave instruction 1 KB contiguous) and writes the 256 words at
+// 256*b of dst, all non-temporal; the writes do not depend on the reads.
+template <int RD>
+__global__ __launch_bounds__(256) void probe_mixed_kernel(const v4i* __restrict__ src, v4i* __restrict__ dst,
+                                                          int64_t units, uint32_t* sink) {
+  const int t = threadIdx.x;
+  v4i acc = v4i{0, 0, 0, 0};
+  const v4i val = v4i{t, 1, 2, 3};
+  for (int64_t b = blockIdx.x; b < units; b += gridDim.x) {
+    const v4i* s = src + b * 256 * RD;
+#pragma unroll
+    for (int u = 0; u < RD; ++u) acc ^= __builtin_nontemporal_load(s + u * 256 + t);
+    __builtin_nontemporal_store(val, dst + b * 256 + t);
+  }
+  const uint32_t x = static_cast<uint32_t>(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+  if (x == 0x9e3779b9u) sink[0] = x;  // keeps the loads alive; practically never stores
 }
 
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -125,6 +146,25 @@ bl_status bl_probe_write(void* dst, size_t bytes, int32_t blocks, int32_t nontem
     hipLaunchKernelGGL(bl::probe_write_kernel<false>, dim3(blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<bl::v4i*>(dst),
                        static_cast<int64_t>(bytes / 16));
+  return bl::hip_status(hipGetLastError());
+}
+
+bl_status bl_probe_mixed(const void* src, size_t src_bytes, void* dst, size_t dst_bytes,
+                         int32_t reads_per_write, uint32_t* sink, int32_t blocks, void* stream) {
+  if (!src || !dst || !sink || blocks <= 0 || (reads_per_write != 16 && reads_per_write != 64))
+    return BL_ERR_INVALID_ARGUMENT;
+  const size_t unit = static_cast<size_t>(16) * 256 * static_cast<size_t>(reads_per_write);
+  if (src_bytes == 0 || src_bytes % unit != 0 || dst_bytes < src_bytes / static_cast<size_t>(reads_per_write))
+    return BL_ERR_INVALID_ARGUMENT;
+  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0)
+    return BL_ERR_MISALIGNED;
+  const int64_t units = static_cast<int64_t>(src_bytes / unit);
+  if (reads_per_write == 16)
+    hipLaunchKernelGGL(bl::probe_mixed_kernel<16>, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const bl::v4i*>(src), static_cast<bl::v4i*>(dst), units, sink);
+  else
+    hipLaunchKernelGGL(bl::probe_mixed_kernel<64>, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const bl::v4i*>(src), static_cast<bl::v4i*>(dst), units, sink);
   return bl::hip_status(hipGetLastError());
 }
 

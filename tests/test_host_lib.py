@@ -193,6 +193,14 @@ def test_probe_validation():
     assert lib.bl_probe_write(None, 64, 1, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_probe_write(A, 63, 1, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_probe_write(MIS, 64, 1, 1, None) == bl.BL_ERR_MISALIGNED
+    U = 4096 * 16
+    assert lib.bl_probe_mixed(None, U, A, U, 16, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_probe_mixed(A, U, A, U, 8, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT   # ratio
+    assert lib.bl_probe_mixed(A, U + 16, A, U, 16, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT  # not whole units
+    assert lib.bl_probe_mixed(A, U, A, U // 16 - 16, 16, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT  # dst short
+    assert lib.bl_probe_mixed(A, 0, A, U, 16, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_probe_mixed(A, U, A, U, 16, A, 0, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert lib.bl_probe_mixed(MIS, U, A, U, 16, A, 1, None) == bl.BL_ERR_MISALIGNED
     assert lib.bl_probe_mfma_i8(0, 1, 16, A, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_probe_mfma_i8(1, 1, 8, A, None) == bl.BL_ERR_INVALID_ARGUMENT
 
