@@ -560,6 +560,43 @@ def prefill_steps(args) -> int:
     return max(3, min(50, args.steps // 2))
 
 
+def bench_prefill_fused(torch, bl, args):
+    """One BitLinear per call at M = 16384 for each Qwen3-0.6B shape: the
+    forward as quantization launch + tiled product (bitlinear_forward) against
+    the forward whose product quantizes in its producer (statistics launch +
+    tiled product reading fp32 rows; bitlinear_forward_prefill_fused).  Same
+    outputs bit for bit (checked here on every shape)."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(23)
+    M = 16384
+    res = {}
+    for name, K, N in (("q", 1024, 2048), ("k", 1024, 1024), ("o", 2048, 1024),
+                       ("gate", 1024, 3072), ("down", 3072, 1024)):
+        w = torch.randn((N, K), generator=g, device=dev) * 0.02
+        pw, scale = bl.i2s_pack_device(w)
+        del w
+        x = torch.randn((M, K), generator=g, device=dev)
+        nw = 1.0 + 0.1 * torch.randn((K,), generator=g, device=dev)
+        y1 = torch.empty((M, N), device=dev)
+        y2 = torch.empty((M, N), device=dev)
+        t1, _ = time_calls(torch, lambda: bl.bitlinear_forward(x, nw, pw, scale, N, inputs.EPS, y=y1),
+                           20, 5, 100.0)
+        t2, _ = time_calls(torch, lambda: bl.bitlinear_forward_prefill_fused(x, nw, pw, scale, N, inputs.EPS, y=y2),
+                           20, 5, 100.0)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(y1, y2))
+        ops = 2 * M * N * K
+        res[name] = {"K": K, "N": N, "forward_us": round(t1 * 1e3, 1), "fused_producer_us": round(t2 * 1e3, 1),
+                     "forward_TOPS": round(ops / t1 / 1e9, 1), "fused_producer_TOPS": round(ops / t2 / 1e9, 1),
+                     "fused_over_forward": round(t2 / t1, 3), "bit_identical": same}
+        del x, nw, pw, y1, y2
+    return {"workload": "one BitLinear per call at M=16384, Qwen3-0.6B shapes: bitlinear_forward "
+                        "(quantization launch + product) against bitlinear_forward_prefill_fused "
+                        "(statistics launch + product whose producer quantizes fp32 rows)",
+            "per_shape": res}
+
+
 def bench_ffn_glue(torch, bl, args):
     """The Qwen3 FFN down projection fed by the glue act(gate) * up at the
     prefill size (M = 16384, K = 3072 -> N = 1024, SiLU): the fused glue +
@@ -1052,6 +1089,12 @@ def main():
                 lc["projs"], lambda p: lc["xs_host"][p["xkey"]][lc["rows"]], len(lc["rows"]),
                 args.cpu_seconds, "sampled token rows")
         del lc
+
+        pq = bench_prefill_fused(torch, bl, args)
+        log("prefill, quantization in the product's producer (one call, M=16384): " + ", ".join(
+            f"{k} {v['fused_producer_us']:.0f} us vs {v['forward_us']:.0f} us"
+            + ("" if v["bit_identical"] else " (OUTPUTS DIFFER)") for k, v in pq["per_shape"].items()))
+        out["prefill_fused_producer"] = pq
 
         glue = bench_ffn_glue(torch, bl, args)
         log(f"ffn glue: glue+quant {glue['glue_quant_us']:.1f} us ({glue['roofline']['achieved']:.0f} GB/s), "

@@ -192,6 +192,27 @@ bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* 
                             void* stream);
 
 /*
+ * bitlinear_forward_prefill_fused — bitlinear_forward with the activation
+ * quantization inside the product's producer for prefill sizes (the pages'
+ * RMSNorm, norm-weight multiply and quantization ops, "BitNet Embeddings GGUF
+ * Conversion Implementation" s4.5, folded into the matrix product instead of
+ * a separate pass that stores int8 codes).  Same arguments, same results bit
+ * for bit.  For M > 16: a statistics pass writes per row the factor, the code
+ * sum and max|x*norm_w| (12 bytes per row of workspace instead of K codes),
+ * then the tiled MFMA kernel loads the fp32 rows and the norm weight itself
+ * and codes them with the quantization kernel's arithmetic while it streams
+ * the weights.  M <= 16 runs exactly as bitlinear_forward (its decode kernel
+ * already quantizes inside itself where the rows fit).  Needs K <= 4096 and
+ * M*K*4 < 2^31, else BL_ERR_UNSUPPORTED.  It reads the fp32 rows once per
+ * 256-column tile of the output, so at prefill sizes it is slower than
+ * bitlinear_forward; it exists to measure that trade.  Workspace rules as
+ * for bitlinear_forward.
+ */
+bl_status bitlinear_forward_prefill_fused(const float* x, const float* norm_w,
+                                          const uint8_t* packed_w, float w_scale, int64_t M,
+                                          int64_t K, int64_t N, float eps, float* y, void* stream);
+
+/*
  * bitlinear_quant — the first stage of bitlinear_forward alone (same kernel):
  * fused RMSNorm + per-token absmax int8 quantization.
  *   xq       device [M][K] int8 output, codes in [-127, 127].
@@ -251,6 +272,10 @@ bl_status bitlinear_glu_forward(const float* gate, const float* up, int32_t act,
 bl_status bitlinear_forward_nwf16(const float* x, const uint16_t* norm_w, const uint8_t* packed_w,
                                   float w_scale, int64_t M, int64_t K, int64_t N, float eps,
                                   float* y, void* stream);
+bl_status bitlinear_forward_prefill_fused_nwf16(const float* x, const uint16_t* norm_w,
+                                                const uint8_t* packed_w, float w_scale, int64_t M,
+                                                int64_t K, int64_t N, float eps, float* y,
+                                                void* stream);
 bl_status bitlinear_quant_nwf16(const float* x, const uint16_t* norm_w, int64_t M, int64_t K,
                                 float eps, int8_t* xq, float* x_factor, void* stream);
 bl_status bitlinear_glu_quant_nwf16(const float* gate, const float* up, int32_t act,

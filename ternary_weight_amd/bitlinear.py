@@ -68,6 +68,8 @@ _SIGS = {
     "bl_gguf_find_tensor": ([_p, ctypes.c_size_t, ctypes.c_char_p, ctypes.POINTER(GgufTensor)], _i32),
     "i2s_pack_device": ([_p, _i64, _i64, _p, ctypes.c_size_t, _p, _p], _i32),
     "bitlinear_forward": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
+    "bitlinear_forward_prefill_fused": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
+    "bitlinear_forward_prefill_fused_nwf16": ([_p, _p, _p, _f32, _i64, _i64, _i64, _f32, _p, _p], _i32),
     "bitlinear_quant": ([_p, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
     "bitlinear_matmul_i32": ([_p, _p, _i64, _i64, _i64, _p, _p], _i32),
     "bitlinear_glu_quant": ([_p, _p, _i32, _p, _i64, _i64, _f32, _p, _p, _p], _i32),
@@ -266,6 +268,23 @@ def bitlinear_forward(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y
         _dev(x, torch.float32, "x"), nw,
         _dev(packed_w, torch.uint8, "packed_w"), w_scale, M, K, N, eps,
         _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)), "bitlinear_forward")
+    return y
+
+
+def bitlinear_forward_prefill_fused(x, norm_w, packed_w, w_scale: float, N: int, eps: float, y=None,
+                                    stream=None):
+    """bitlinear_forward with the quantization inside the prefill product's
+    producer (same results); returns y."""
+    torch = _torch()
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    nw, f16 = _norm(norm_w, K)
+    fn = _lib.bitlinear_forward_prefill_fused_nwf16 if f16 else _lib.bitlinear_forward_prefill_fused
+    _check(fn(
+        _dev(x, torch.float32, "x"), nw,
+        _dev(packed_w, torch.uint8, "packed_w"), w_scale, M, K, N, eps,
+        _dev(y, torch.float32, "y", (M, N)), _stream_handle(stream)), "bitlinear_forward_prefill_fused")
     return y
 
 

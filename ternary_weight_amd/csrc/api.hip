@@ -246,6 +246,46 @@ bl_status forward_impl(const float* x, const void* norm_w, bool nw_f16, const ui
   }
 }
 
+// Prefill with the quantization inside the product's producer: a statistics
+// pass (factor, row sum and max|u| per row; no codes) and the prefill kernel
+// that codes the fp32 rows itself.  Decode sizes take bitlinear_forward's
+// path, which already quantizes inside its kernel when the rows fit.
+bl_status forward_pq_impl(const float* x, const void* norm_w, bool nw_f16, const uint8_t* packed_w,
+                          float w_scale, int64_t M, int64_t K, int64_t N, float eps, float* y,
+                          void* stream) {
+  try {
+    bl_status st = check_forward(x, norm_w, packed_w, w_scale, M, K, N, eps, y);
+    if (st != BL_OK || M == 0) return st;
+    if (M <= kGemvMaxM) return forward_impl(x, norm_w, nw_f16, packed_w, w_scale, M, K, N, eps, y, stream);
+    if (K > kGemmPqMaxK || M * K * 4 >= (int64_t{1} << 31)) return BL_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Prob p{};
+    p.x = x;
+    p.norm_w = static_cast<const float*>(norm_w);
+    p.nw_f16 = nw_f16 ? 1 : 0;
+    p.w = packed_w;
+    p.y = y;
+    p.acc = nullptr;
+    p.xq = nullptr;
+    p.w_scale = w_scale;
+    p.eps = eps;
+    p.M = static_cast<int>(M);
+    p.K = static_cast<int>(K);
+    p.N = static_cast<int>(N);
+    // factor, row sums and max|u|: 12 bytes per row instead of K codes
+    const size_t part = round_up(static_cast<size_t>(M) * 4, 256);
+    uint8_t* ws = nullptr;
+    if ((st = acquire_ws(s, 3 * part, &ws)) != BL_OK) return st;
+    p.factor = reinterpret_cast<float*>(ws);
+    p.rowsum = reinterpret_cast<int32_t*>(ws + part);
+    p.amax = reinterpret_cast<float*>(ws + 2 * part);
+    if ((st = from_hip(launch_quant_stats(single_set(p, quant_units(p.M)), p.K, s))) != BL_OK) return st;
+    return from_hip(launch_gemm_pq(p, s));
+  } catch (...) {
+    return BL_ERR_INTERNAL;
+  }
+}
+
 bl_status quant_impl(const float* x, const void* norm_w, bool nw_f16, int64_t M, int64_t K,
                      float eps, int8_t* xq, float* x_factor, void* stream) {
   try {
@@ -389,6 +429,17 @@ bl_status bitlinear_forward(const float* x, const float* norm_w, const uint8_t* 
                             float w_scale, int64_t M, int64_t K, int64_t N, float eps, float* y,
                             void* stream) {
   return forward_impl(x, norm_w, false, packed_w, w_scale, M, K, N, eps, y, stream);
+}
+bl_status bitlinear_forward_prefill_fused(const float* x, const float* norm_w, const uint8_t* packed_w,
+                                          float w_scale, int64_t M, int64_t K, int64_t N, float eps,
+                                          float* y, void* stream) {
+  return forward_pq_impl(x, norm_w, false, packed_w, w_scale, M, K, N, eps, y, stream);
+}
+bl_status bitlinear_forward_prefill_fused_nwf16(const float* x, const uint16_t* norm_w,
+                                                const uint8_t* packed_w, float w_scale, int64_t M,
+                                                int64_t K, int64_t N, float eps, float* y,
+                                                void* stream) {
+  return forward_pq_impl(x, norm_w, true, packed_w, w_scale, M, K, N, eps, y, stream);
 }
 bl_status bitlinear_forward_nwf16(const float* x, const uint16_t* norm_w, const uint8_t* packed_w,
                                   float w_scale, int64_t M, int64_t K, int64_t N, float eps,

@@ -58,6 +58,10 @@ struct Prob {
   int ksplit;
   int32_t* part;
   unsigned* tile_cnt;
+  // Prefill with quantization in the product's producer: [M] max|x*norm_w|
+  // per row, written by the statistics pass and read by the prefill kernel
+  // that codes fp32 rows itself (null elsewhere).
+  float* amax;
 };
 
 constexpr int kActNone = 0, kActSilu = 1, kActGeluTanh = 2;

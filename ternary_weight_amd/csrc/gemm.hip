@@ -74,6 +74,7 @@ constexpr int kWLoads = kWStage / 4 / 1024;  // 2
 constexpr int kLoadsPerStage = kXLoads + kWLoads;
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int xs_slot(int row, int slot) {
   return slot ^ (row & 7) ^ ((row >> 3) & 1);
@@ -104,8 +105,21 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* ldst) {
 // SPLIT: the launch holds problems with K splits (the split bookkeeping is
 // compiled only into this instance; launches without splits keep the plain
 // kernel's registers).
-template <bool RAW, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
+//
+// PQ: one problem whose activation producer quantizes (the pages' norm,
+// multiply and quantization ops, "BitNet Embeddings GGUF Conversion
+// Implementation" s4.5, folded into the product's producer): instead of
+// direct loads of int8 codes, each thread loads fp32 rows of the stage into
+// registers two stages ahead (lane l of wave w: 16-byte chunk c = l % 32 of
+// rows 32w + 2i + l/32, i = 0..15, so each instruction reads two rows' 512
+// bytes), multiplies by the norm weight chunk, and codes them with the
+// quantization kernel's arithmetic (codes4) against the row's max|u| from the
+// statistics pass, writing the codes into the same swizzled LDS slots the
+// direct loads fill.  Codes, accumulators and outputs are therefore those of
+// the quantization launch + plain kernel, bit for bit.  The two register sets
+// of 64 values per thread need one workgroup per CU.
+template <bool RAW, bool SPLIT, bool PQ = false>
+__global__ __launch_bounds__(256, PQ ? 1 : 2) void gemm_kernel(ProbSet set) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
 
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
@@ -146,13 +160,71 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   }
   auto issue = [&](int kb, int slot_off) {
     uint8_t* st = smem + slot_off;
+    if constexpr (!PQ) {
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i)
-      dma16(P.xq + xoff[i] + kb * kBlockK, st + (kXLoads * wave + i) * 1024);
+      for (int i = 0; i < kXLoads; ++i)
+        dma16(P.xq + xoff[i] + kb * kBlockK, st + (kXLoads * wave + i) * 1024);
+    }
 #pragma unroll
     for (int i = 0; i < kWLoads; ++i)
       dma16(P.w + woff[i] + kb * (kBlockK / 4), st + kXStage + (kWLoads * wave + i) * 1024);
   };
+  // Loads per stage counted by vmcnt: the direct loads, and for PQ the 16
+  // activation chunks and one norm-weight chunk per thread instead of the
+  // activation direct loads.
+  constexpr int kPqRows = 16;
+  constexpr int kLps = PQ ? kWLoads + kPqRows + 1 : kLoadsPerStage;
+
+  // PQ producer state: this thread's rows, their max|u| and byte offsets in
+  // x (stage kb adds 512*kb), two register sets of loaded fp32 chunks and
+  // norm-weight chunks (a binary16 chunk in the low 8 bytes).
+  const int pc = lane & 31;  // 16-byte chunk of the stage's 128 positions
+  int xro[PQ ? kPqRows : 1];
+  float ramax[PQ ? kPqRows : 1];
+  v4i xs[PQ ? 2 : 1][PQ ? kPqRows : 1];
+  v4i nwraw[PQ ? 2 : 1];
+  const __amdgpu_buffer_rsrc_t xrs32 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(P.x), 0, PQ ? M * K * 4 : 0, kBufferDword3);
+  const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(P.norm_w), 0, PQ && P.norm_w ? K * (P.nw_f16 ? 2 : 4) : 0, kBufferDword3);
+  if constexpr (PQ) {
+#pragma unroll
+    for (int i = 0; i < kPqRows; ++i) {
+      const int m = min(m0 + 32 * wave + 2 * i + (lane >> 5), M - 1);
+      xro[i] = m * K * 4 + pc * 16;
+      ramax[i] = gptr<float>(P.amax)[m];
+    }
+  }
+  auto load_x32 = [&](int kb, auto set_c) {
+    constexpr int q = decltype(set_c)::value;
+#pragma unroll
+    for (int i = 0; i < kPqRows; ++i)
+      xs[q][i] = __builtin_amdgcn_raw_buffer_load_b128(xrs32, xro[i], __builtin_amdgcn_readfirstlane(kb * 512), 0);
+    if (P.nw_f16) {
+      const v2i h = __builtin_amdgcn_raw_buffer_load_b64(nrs, pc * 8, __builtin_amdgcn_readfirstlane(kb * 256), 0);
+      nwraw[q] = v4i{h[0], h[1], 0, 0};
+    } else {
+      nwraw[q] = __builtin_amdgcn_raw_buffer_load_b128(nrs, pc * 16, __builtin_amdgcn_readfirstlane(kb * 512), 0);
+    }
+  };
+  // Codes of the stage held in register set q, written to the ring slot at
+  // slot_off: chunk pc of row r at physical slot xs_slot(r, pc / 4).
+  auto code_x = [&](auto set_c, int slot_off) {
+    constexpr int q = decltype(set_c)::value;
+    const f4 nwv = P.nw_f16 ? half4(u2{static_cast<uint32_t>(nwraw[q][0]), static_cast<uint32_t>(nwraw[q][1])})
+                            : __builtin_bit_cast(f4, nwraw[q]);
+    const bool norm = P.norm_w != nullptr;
+#pragma unroll
+    for (int i = 0; i < kPqRows; ++i) {
+      const int r = 32 * wave + 2 * i + (lane >> 5);
+      const f4 xv = __builtin_bit_cast(f4, xs[q][i]);
+      int sum = 0;
+      const uint32_t code = codes4(norm ? xv * nwv : xv, ramax[i], &sum);
+      *reinterpret_cast<uint32_t*>(smem + slot_off + r * kBlockK + xs_slot(r, pc >> 2) * 16 + (pc & 3) * 4) = code;
+    }
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
 
   v16i acc[4][2];
 #pragma unroll
@@ -212,13 +284,34 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   // for stage kb + 1's loads, barrier, refill this slot with stage kb + 3,
   // and read stage kb + 1's packed weights and first activation fragments
   // into the other register set while the k-step 3 MFMAs run.
-  issue(0, 0);
-  if (nblk > 1) issue(1, kStageBytes);
-  if (nblk > 2) issue(2, 2 * kStageBytes);
-  if (nblk > 2) wait_vmcnt<2 * kLoadsPerStage>();
-  else if (nblk > 1) wait_vmcnt<kLoadsPerStage>();
-  else wait_vmcnt<0>();
-  block_sync();
+  if constexpr (PQ) {
+    // Stages 0 and 1 load into register sets 0 and 1; stage 0 is coded into
+    // its slot before stage 2 loads into set 0.
+    issue(0, 0);
+    load_x32(0, Set0{});
+    if (nblk > 1) {
+      issue(1, kStageBytes);
+      load_x32(1, Set1{});
+      wait_vmcnt<kLps>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    code_x(Set0{}, 0);
+    if (nblk > 2) {
+      issue(2, 2 * kStageBytes);
+      load_x32(2, Set0{});
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_sync();
+  } else {
+    issue(0, 0);
+    if (nblk > 1) issue(1, kStageBytes);
+    if (nblk > 2) issue(2, 2 * kStageBytes);
+    if (nblk > 2) wait_vmcnt<2 * kLoadsPerStage>();
+    else if (nblk > 1) wait_vmcnt<kLoadsPerStage>();
+    else wait_vmcnt<0>();
+    block_sync();
+  }
 
   v4i wp[4];     // packed weight half-rows of the current stage
   v4i bx[4][2];  // activation fragments of k-steps 0..3
@@ -232,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   // waits for them).  MID: a later stage exists and the middle-of-stage
   // hand-over runs: the k-step 3 operands are decoded first, which frees the
   // packed weight registers for the next stage's reads.
-  auto stage = [&](auto mid, int kb) {
+  auto stage = [&](auto mid, auto set_c, int kb) {
     constexpr bool kMid = decltype(mid)::value;
     const uint8_t* st = smem + slot;
 #pragma unroll
@@ -255,14 +348,23 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
         for (int i = 0; i < 4; ++i) a3[fn][i] = field_codes(static_cast<uint32_t>(wp[fn][i]), 3);
         asm volatile("" : "+v"(a3[fn]));
       }
-      if (kb + 2 < nblk) wait_lgkm0_vmcnt<kLoadsPerStage>();
+      if (kb + 2 < nblk) wait_lgkm0_vmcnt<kLps>();
       else wait_lgkm0_vmcnt<0>();
-      block_sync();
       const int next = slot == 2 * kStageBytes ? 0 : slot + kStageBytes;
+      if constexpr (PQ) {
+        // stage kb + 1's codes (its fp32 chunks are in set (kb + 1) & 1),
+        // written before the barrier that publishes the stage
+        code_x(set_c, next);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+      block_sync();
       read_w(wp, smem + next);
       read_x(bx[0], smem + next, 0);
       read_x(bx[1], smem + next, 1);
-      if (kb + 3 < nblk) issue(kb + 3, slot);
+      if (kb + 3 < nblk) {
+        issue(kb + 3, slot);
+        if constexpr (PQ) load_x32(kb + 3, set_c);  // (kb + 3) & 1 == (kb + 1) & 1
+      }
       slot = next;
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn)
@@ -277,8 +379,23 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
   int kb = 0;
-  for (; kb + 1 < nblk; ++kb) stage(Yes{}, kb);
-  stage(No{}, kb);
+  if constexpr (PQ) {
+    // Unrolled by two so that each stage's register set is a compile-time
+    // index: stage kb codes set (kb + 1) & 1.
+    for (; kb + 2 < nblk; kb += 2) {
+      stage(Yes{}, Set1{}, kb);
+      stage(Yes{}, Set0{}, kb + 1);
+    }
+    if (kb + 1 < nblk) {
+      stage(Yes{}, Set1{}, kb);
+      stage(No{}, Set0{}, kb + 1);
+    } else {
+      stage(No{}, Set1{}, kb);
+    }
+  } else {
+    for (; kb + 1 < nblk; ++kb) stage(Yes{}, Set0{}, kb);
+    stage(No{}, Set0{}, kb);
+  }
 
   if (SPLIT && ks > 1) {
     // Split tiles.  Each split stores its accumulators, counts itself in,
@@ -421,6 +538,19 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(ProbSet set) {
 
 int gemm_units(int M, int N) {
   return ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
+}
+
+hipError_t launch_gemm_pq(const Prob& p, hipStream_t stream) {
+  if (p.M <= 0) return hipSuccess;
+  if (!p.amax || !p.factor || !p.rowsum || !p.y || p.K > kGemmPqMaxK ||
+      static_cast<int64_t>(p.M) * p.K * 4 >= (int64_t{1} << 31))
+    return hipErrorInvalidValue;
+  ProbSet set{};
+  set.single = p;
+  set.single.ksplit = 0;
+  set.total = gemm_units(p.M, p.N);
+  hipLaunchKernelGGL((gemm_kernel<false, false, true>), dim3(set.total), dim3(256), 0, stream, set);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const ProbSet& set, bool raw, hipStream_t stream) {

@@ -70,6 +70,10 @@ hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hip
 // launch time, not their work.
 constexpr int kQuantMergeMaxUnits = 2048;
 hipError_t launch_quant_merged(const ProbSet& set, hipStream_t stream);
+// The statistics pass of the prefill path that quantizes in the product's
+// producer: per row the factor, the code sum and max|u| (Prob::amax), no
+// codes stored; register-resident rows only (quant_chunks(max_k) > 0).
+hipError_t launch_quant_stats(const ProbSet& set, int max_k, hipStream_t stream);
 // Row sums of caller-supplied int8 activations (for the raw-integer hook).
 hipError_t launch_rowsum(const Prob& p, hipStream_t stream);
 // Stage 2, M <= kGemvMaxM: weight-streaming MFMA decode kernel for one
@@ -115,5 +119,11 @@ hipError_t launch_i2s_pack_device(const float* w, int64_t K, int64_t N, uint8_t*
                                   double* partial, float* scale_dev, hipStream_t stream);
 // Stage 2, M > kGemvMaxM: LDS-tiled MFMA kernel.
 hipError_t launch_gemm(const ProbSet& set, bool raw, hipStream_t stream);
+// The same product for one problem whose activation producer quantizes:
+// it reads the fp32 rows (x, norm_w) and codes them itself from the
+// statistics pass's max|u| (Prob::amax), factor and row sums; forward
+// epilogue only.  Rows of at most kGemmPqMaxK values, M*K*4 < 2^31.
+constexpr int kGemmPqMaxK = 4096;
+hipError_t launch_gemm_pq(const Prob& p, hipStream_t stream);
 
 }  // namespace bl

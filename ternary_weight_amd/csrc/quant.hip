@@ -53,7 +53,10 @@ __device__ __forceinline__ f4 nw_chunk(const Prob& P, int c) {
 // owns kQuantRows consecutive rows of one problem, kQuantRowsPerWave per wave.
 // ACT: the row is act(x) * up (FFN glue) instead of x.  NW: the kind of norm
 // weight (each kind keeps its loads in one block, no per-element branch).
-template <int NC, int ACT, int NW>
+// STATS: the row statistics alone (factor, row sum and max|u| into P.amax),
+// the codes computed for their sum but not stored: the prefill kernel whose
+// producer quantizes recomputes them from x with the same arithmetic.
+template <int NC, int ACT, int NW, bool STATS = false>
 __device__ __forceinline__ void quant_reg_rows(const Prob& P, int m_begin, int lane) {
   const int nch = P.K >> 2;
   for (int r = 0; r < kQuantRowsPerWave; ++r) {
@@ -78,14 +81,34 @@ __device__ __forceinline__ void quant_reg_rows(const Prob& P, int m_begin, int l
     }
     const double ssd = wave_sum(static_cast<double>(ss));
     amax = wave_max(amax);
-    BL_GLOBAL uint32_t* qrow = gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
+    BL_GLOBAL uint32_t* qrow = STATS ? nullptr : gptr_out<uint32_t>(P.xq + static_cast<int64_t>(m) * P.K);
     int rs = 0;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = lane + kWave * i;
-      if (c < nch) __builtin_nontemporal_store(codes4(u[i], amax, &rs), qrow + c);
+      if (c < nch) {
+        const uint32_t q = codes4(u[i], amax, &rs);
+        if (!STATS) __builtin_nontemporal_store(q, qrow + c);
+      }
     }
     finish_row(P, m, ssd, amax, rs, lane);
+    if (STATS && lane == 0) gptr_out<float>(P.amax)[m] = amax;
+  }
+}
+
+// The statistics pass of the prefill path whose product quantizes in its
+// producer (register-resident rows only, no FFN glue).
+template <int NC>
+__global__ __launch_bounds__(256) void quant_stats_kernel(ProbSet set) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int local;
+  const int pi = find_prob(set, blockIdx.x, &local);
+  const Prob P = prob_at(set, pi);
+  const int m_begin = local * kQuantRows + wave_id() * kQuantRowsPerWave;
+  switch (nw_kind(P)) {
+    case kNwF32: quant_reg_rows<NC, kActNone, kNwF32, true>(P, m_begin, lane); break;
+    case kNwF16: quant_reg_rows<NC, kActNone, kNwF16, true>(P, m_begin, lane); break;
+    default: quant_reg_rows<NC, kActNone, kNwNone, true>(P, m_begin, lane);
   }
 }
 
@@ -386,6 +409,22 @@ hipError_t launch_quant(const ProbSet& set, int max_k, bool shared, int act, hip
     BL_QUANT_SWITCH(quant_reg_kernel, , kActNone)
   }
 #undef BL_QUANT_SWITCH
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_stats(const ProbSet& set, int max_k, hipStream_t stream) {
+  if (set.total <= 0) return hipSuccess;
+  const int nc = quant_chunks(max_k);
+  if (nc <= 0) return hipErrorInvalidValue;  // rows too long for registers
+  const dim3 grid(set.total), block(256);
+  switch (nc) {
+#define BL_QUANT_STATS(n) \
+  case n: hipLaunchKernelGGL((quant_stats_kernel<n>), grid, block, 0, stream, set); break;
+    BL_QUANT_STATS(1) BL_QUANT_STATS(2) BL_QUANT_STATS(3) BL_QUANT_STATS(4) BL_QUANT_STATS(6)
+    BL_QUANT_STATS(8) BL_QUANT_STATS(12) BL_QUANT_STATS(16)
+#undef BL_QUANT_STATS
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -290,6 +290,43 @@ def test_forward_matches_hooks_bitwise(M, K):
         assert torch.equal(it["y"], y2)
 
 
+# bitlinear_forward_prefill_fused: the quantization inside the prefill
+# product's producer (a statistics pass, then the tiled kernel codes the fp32
+# rows itself).  Bit-identical to bitlinear_forward (pinned to the oracle
+# above) on full and ragged tiles, K up to 4096, every norm-weight kind, an
+# all-zero row and a tiny row (the double-precision code path); decode sizes
+# run bitlinear_forward's own path.
+PQ_CASES = [(8, 1024, 3072), (17, 128, 1), (40, 1024, 72), (200, 1280, 333), (255, 2048, 640),
+            (257, 640, 2048), (512, 3072, 1024), (130, 4096, 129), (1024, 1024, 3072)]
+
+
+@pytest.mark.parametrize("norm", ["f32", "f16", "none"])
+@pytest.mark.parametrize("M,K,N", PQ_CASES)
+def test_prefill_fused_matches_forward(M, K, N, norm):
+    x, nw, packed, scale = proj_inputs(19, M, K, M, K, N, heavy=True)
+    x[M // 2] = 0.0
+    x[1] *= 1e-36
+    dx, dp = dev(x), dev(packed)
+    dn = {"f32": dev(nw), "f16": torch.from_numpy(nw.astype(np.float16)).to(DEV), "none": None}[norm]
+    y = bl.bitlinear_forward(dx, dn, dp, scale, N, EPS)
+    y2 = torch.full((M, N), float("nan"), device=DEV)
+    bl.bitlinear_forward_prefill_fused(dx, dn, dp, scale, N, EPS, y=y2)
+    assert torch.equal(y, y2)
+    if norm == "f32":
+        assert rel_l2(host(y2), oracle.bitlinear(x, nw, packed, N, EPS)) <= 1e-3
+
+
+def test_prefill_fused_full_size():
+    # One Qwen3-0.6B down projection at the stack's M = 16384 (K = 3072).
+    M, K, N = 16384, 3072, 1024
+    x, nw, packed, scale = proj_inputs(4, 0, 6, M, K, N)
+    dx, dn, dp = dev(x), dev(nw), dev(packed)
+    y = bl.bitlinear_forward(dx, dn, dp, scale, N, EPS)
+    y2 = torch.full((M, N), float("nan"), device=DEV)
+    bl.bitlinear_forward_prefill_fused(dx, dn, dp, scale, N, EPS, y=y2)
+    assert torch.equal(y, y2)
+
+
 def test_group_forward_launch_kinds_and_order():
     # The forward as launches: quantization of the problems not fused (K 1024
     # -> 4 chunks, 4096 -> 16: two classes, so one merged launch for this

@@ -183,6 +183,18 @@ def test_glu_validation():
     assert gf(A, A, S, A, A, 1.0, 0, 128, 8, 1e-6, A, None) == bl.BL_OK
 
 
+def test_prefill_fused_validation():
+    lib = bl.lib
+    f = lib.bitlinear_forward_prefill_fused
+    # rows longer than the register-resident statistics pass: refused before any HIP call
+    assert f(A, A, A, 1.0, 32, 4224, 8, 1e-6, A, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, A, A, 1.0, 32, 100, 8, 1e-6, A, None) == bl.BL_ERR_UNSUPPORTED  # K % 128
+    assert f(A, A, A, 0.0, 32, 128, 8, 1e-6, A, None) == bl.BL_ERR_INVALID_ARGUMENT
+    assert f(A, MIS, A, 1.0, 32, 128, 8, 1e-6, A, None) == bl.BL_ERR_MISALIGNED
+    assert f(A, A, A, 1.0, 0, 128, 8, 1e-6, A, None) == bl.BL_OK
+    assert lib.bitlinear_forward_prefill_fused_nwf16(A, A, A, 1.0, 32, 4224, 8, 1e-6, A, None) == bl.BL_ERR_UNSUPPORTED
+
+
 def test_probe_validation():
     lib = bl.lib
     assert lib.bl_probe_read(None, 64, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT
