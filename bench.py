@@ -589,12 +589,19 @@ def bench_prefill_fused(torch, bl, args):
         ops = 2 * M * N * K
         res[name] = {"K": K, "N": N, "forward_us": round(t1 * 1e3, 1), "fused_producer_us": round(t2 * 1e3, 1),
                      "forward_TOPS": round(ops / t1 / 1e9, 1), "fused_producer_TOPS": round(ops / t2 / 1e9, 1),
+                     "forward_frac": round(ops / t1 / 1e9 / INT8_PEAK_TOPS, 4),
+                     "fused_producer_frac": round(ops / t2 / 1e9 / INT8_PEAK_TOPS, 4),
                      "fused_over_forward": round(t2 / t1, 3), "bit_identical": same}
         del x, nw, pw, y1, y2
     return {"workload": "one BitLinear per call at M=16384, Qwen3-0.6B shapes: bitlinear_forward "
                         "(quantization launch + product) against bitlinear_forward_prefill_fused "
                         "(statistics launch + product whose producer quantizes fp32 rows)",
-            "per_shape": res}
+            "per_shape": res,
+            "roofline": {"bound": "mfma", "kernel": "quant_stats_kernel + gemm_kernel<PQ> (one call per shape)",
+                         "achieved": round(max(v["fused_producer_TOPS"] for v in res.values()), 1),
+                         "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                         "frac": round(max(v["fused_producer_frac"] for v in res.values()), 4),
+                         "note": "best shape; whole calls (statistics launch + product), per shape in per_shape"}}
 
 
 def bench_ffn_glue(torch, bl, args):
