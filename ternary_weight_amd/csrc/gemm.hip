@@ -50,6 +50,14 @@
 // in the workspace, and the last to arrive (a per-tile count) adds the others
 // and runs the epilogue: no workgroup ever waits for another.
 //
+// Epilogue: full output tiles store through a buffer resource at the tile's
+// corner (three VALU operations and one store per element); ragged tiles use
+// a bounds-checked path.
+//
+// Producer quantization (the PQ instance, one problem per launch): the
+// activation side loads fp32 rows and codes them itself instead of loading
+// int8 codes, see gemm_kernel.
+//
 // Bound: int8 MFMA for K >= 2048; for K <= 1024 the fp32 output (4*M*N bytes)
 // weighs as much as the MFMA time.
 #include <type_traits>
