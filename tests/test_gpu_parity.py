@@ -195,6 +195,56 @@ def test_decode_long_rows_from_global(M, K, N):
         assert torch.equal(other["y"], bl.bitlinear_forward(other["x"], dn, dp, scale, N, EPS))
 
 
+def _valid_i2s_bytes(rng, n: int) -> np.ndarray:
+    """n random packed bytes whose four 2-bit fields are codes 0, 1 or 2."""
+    valid = np.array([(a << 6) | (b << 4) | (c << 2) | d for a in range(3) for b in range(3)
+                      for c in range(3) for d in range(3)], dtype=np.uint8)
+    return valid[rng.integers(0, valid.size, size=n, dtype=np.uint8)]
+
+
+def _rows_with_tail(packed: np.ndarray, K: int, n0: int, n1: int) -> np.ndarray:
+    """Weight rows n0..n1-1 of a packed buffer, with its scale tail appended."""
+    rb = K // 4
+    return np.concatenate([packed[n0 * rb:n1 * rb], packed[-4:]])
+
+
+@pytest.mark.parametrize("M,K,N", [(20, 128, (1 << 22) + 300), (40, 65536, 70)])
+def test_prefill_extreme_shapes(M, K, N):
+    # Prefill paths that the workloads never reach: an output wider than the
+    # full-tile store path allows (more than 2^22 columns: every tile takes
+    # the bounds-checked stores, the last one ragged), and the longest K the
+    # library accepts (512 K blocks per tile; its quantization streams the
+    # row).  Raw int32 products against the oracle on column ranges at both
+    # ends and around 2^22, the forward bit-identical to the hooks'
+    # composition everywhere and within 1e-3 of the oracle on those ranges.
+    rng = inputs.rng(31, M, K, 1)
+    rb = K // 4
+    packed = np.concatenate([_valid_i2s_bytes(rng, N * rb),
+                             np.frombuffer(np.float32(41.5).tobytes(), np.uint8)])
+    scale = 41.5
+    xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    x = inputs.activations(31, 0, M, M, K)
+    nw = inputs.norm_weight(31, 0, M, K)
+    dp = dev(packed)
+    ranges = [(0, min(N, 256)), (max(0, N - 300), N)]
+    if N > (1 << 22):
+        ranges.append(((1 << 22) - 128, (1 << 22) + 256))
+    acc = bl.bitlinear_matmul_i32(dev(xq), dp, N)
+    for n0, n1 in ranges:
+        ref = oracle.matmul_i32(xq, _rows_with_tail(packed, K, n0, n1), K, n1 - n0)
+        assert np.array_equal(host(acc[:, n0:n1]), ref), f"int32 columns {n0}..{n1}"
+    del acc
+    dx, dn = dev(x), dev(nw)
+    y = bl.bitlinear_forward(dx, dn, dp, scale, N, EPS)
+    q, f = bl.bitlinear_quant(dx, dn, EPS)
+    acc = bl.bitlinear_matmul_i32(q, dp, N)
+    assert torch.equal(y, _hooks_epilogue(acc, f, scale))
+    del acc
+    for n0, n1 in ranges:
+        y_ref = oracle.bitlinear(x, nw, _rows_with_tail(packed, K, n0, n1), n1 - n0, EPS)
+        assert rel_l2(host(y[:, n0:n1]), y_ref) <= 1e-3, f"forward columns {n0}..{n1}"
+
+
 def _hooks_epilogue(acc, f, scale):
     """The forward's fp32 epilogue applied to the hooks' results: float(acc)
     times (factor / w_scale), each step one fp32 rounding."""
