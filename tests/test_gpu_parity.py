@@ -208,15 +208,23 @@ def _rows_with_tail(packed: np.ndarray, K: int, n0: int, n1: int) -> np.ndarray:
     return np.concatenate([packed[n0 * rb:n1 * rb], packed[-4:]])
 
 
-@pytest.mark.parametrize("M,K,N", [(20, 128, (1 << 22) + 300), (40, 65536, 70)])
-def test_prefill_extreme_shapes(M, K, N):
-    # Prefill paths that the workloads never reach: an output wider than the
-    # full-tile store path allows (more than 2^22 columns: every tile takes
-    # the bounds-checked stores, the last one ragged), and the longest K the
-    # library accepts (512 K blocks per tile; its quantization streams the
-    # row).  Raw int32 products against the oracle on column ranges at both
-    # ends and around 2^22, the forward bit-identical to the hooks'
-    # composition everywhere and within 1e-3 of the oracle on those ranges.
+# The widest weight the library accepts: N*K/4 packed bytes exactly at the
+# 32-bit offset limit (2^31 - 4096), for the decode and the prefill kernel.
+N_AT_OFFSET_LIMIT = ((1 << 31) - 4096) // 32
+
+
+@pytest.mark.parametrize("M,K,N", [(20, 128, (1 << 22) + 300), (40, 65536, 70),
+                                   (1, 128, N_AT_OFFSET_LIMIT), (20, 128, N_AT_OFFSET_LIMIT)])
+def test_extreme_shapes(M, K, N):
+    # Paths that the workloads never reach: an output wider than the
+    # prefill kernel's full-tile store path allows (more than 2^22 columns:
+    # every tile takes the bounds-checked stores, the last one ragged), the
+    # longest K the library accepts (512 K blocks per tile; its quantization
+    # streams the row), and the widest weight it accepts (N*K/4 bytes at the
+    # 32-bit offset limit) through the decode and the prefill kernel.  Raw
+    # int32 products against the oracle on column ranges at both ends and
+    # around 2^22, the forward bit-identical to the hooks' composition
+    # everywhere and within 1e-3 of the oracle on those ranges.
     rng = inputs.rng(31, M, K, 1)
     rb = K // 4
     packed = np.concatenate([_valid_i2s_bytes(rng, N * rb),
