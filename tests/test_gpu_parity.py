@@ -253,6 +253,37 @@ def test_extreme_shapes(M, K, N):
         assert rel_l2(host(y[:, n0:n1]), y_ref) <= 1e-3, f"forward columns {n0}..{n1}"
 
 
+def test_activation_offset_limit():
+    # The most activation codes the library accepts: M*K just below the
+    # 32-bit offset limit (M = 32767 rows of K = 65536: 2.1 G codes from 8.6 GB
+    # of fp32 rows), through the streaming quantization and the prefill
+    # kernel, into a NaN-filled output.  The forward equals the fp32 epilogue
+    # of the hooks everywhere; one row in every 128-row tile is checked
+    # against the oracle (codes and factor, the int32 product of the GPU's
+    # codes bit-exactly, the forward within 1e-3).
+    K, N = 65536, 8
+    M = ((1 << 31) - 4096) // K
+    x = inputs.activations_device(torch, 32, 0, 0, M, K, DEV)
+    nw = inputs.norm_weight(32, 0, 0, K)
+    packed, scale = oracle.i2s_pack(inputs.weight(32, 0, 0, N, K))
+    dn, dp = dev(nw), dev(packed)
+    y = torch.full((M, N), float("nan"), device=DEV)
+    bl.bitlinear_forward(x, dn, dp, scale, N, EPS, y=y)
+    assert bool(torch.isfinite(y).all())
+    xq, f = bl.bitlinear_quant(x, dn, EPS)
+    acc = bl.bitlinear_matmul_i32(xq, dp, N)
+    assert torch.equal(y, _hooks_epilogue(acc, f, scale))
+    rows = inputs.tile_rows(M, 128, seed=32)
+    idx = torch.as_tensor(rows, device=DEV)
+    xr = host(x[idx])
+    q_gpu = host(xq[idx])
+    q_ref, f_ref = oracle.quant(xr, nw, EPS)
+    check_codes(q_gpu, q_ref, xr, nw)
+    check_factor(host(f[idx]), f_ref)
+    assert np.array_equal(host(acc[idx]), oracle.matmul_i32(q_gpu, packed, K, N))
+    assert rel_l2(host(y[idx]), oracle.bitlinear(xr, nw, packed, N, EPS)) <= 1e-3
+
+
 def _hooks_epilogue(acc, f, scale):
     """The forward's fp32 epilogue applied to the hooks' results: float(acc)
     times (factor / w_scale), each step one fp32 rounding."""
