@@ -1347,3 +1347,51 @@ def test_forward_from_gguf_image():
     assert rel_l2(host(y), oracle.bitlinear(x, nw32, packed, N, EPS)) <= 1e-3
     y32 = bl.bitlinear_forward(dev(x), dev(nw32), dev(packed), scale, N, EPS)
     assert torch.equal(y, y32)
+
+
+# ------------------------------------------------------- seeded shape sweep ---
+
+def _sweep_shapes(seed: int, count: int, max_work: float = 2.5e8):
+    """count seeded (M, K, N): decode rows (M <= 16) and tiled rows, K any
+    multiple of 128 up to 4096 (odd superblock counts and ragged K blocks of a
+    split included), N up to 1300, cut down where M*K*N exceeds max_work so
+    that the oracle finishes each case in well under a second."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        M = int(g.integers(1, 17)) if g.random() < 0.4 else int(g.integers(17, 1100))
+        K = 128 * int(g.integers(1, 33))
+        N = min(int(g.integers(1, 1301)), max(1, int(max_work // (M * K))))
+        out.append((M, K, N))
+    return out
+
+
+SWEEP = _sweep_shapes(4242, 40)
+
+
+def test_random_shape_sweep():
+    # Each shape on its own: the raw product bit-exact against the oracle on
+    # random codes, the forward equal to the fp32 epilogue of the two hooks
+    # and within 1e-3 of the oracle.  Then every shape in one stateless
+    # batched call (merged decode, shared planning, K splits where the plan
+    # makes them), bit-identical to the single calls.
+    items, singles = [], []
+    for i, (M, K, N) in enumerate(SWEEP):
+        log(f"sweep case {i}: M={M} K={K} N={N}")
+        x, nw, packed, scale = proj_inputs(43, i, 0, M, K, N)
+        dx, dn, dp = dev(x), dev(nw), dev(packed)
+        codes = inputs.rng(43, i, 1, 7).integers(-127, 128, size=(M, K)).astype(np.int8)
+        acc = bl.bitlinear_matmul_i32(dev(codes), dp, N)
+        assert np.array_equal(host(acc), oracle.matmul_i32(codes, packed, K, N)), (M, K, N)
+        y = bl.bitlinear_forward(dx, dn, dp, scale, N, EPS)
+        xq, f = bl.bitlinear_quant(dx, dn, EPS)
+        assert torch.equal(y, _hooks_epilogue(bl.bitlinear_matmul_i32(xq, dp, N), f, scale)), (M, K, N)
+        assert rel_l2(host(y), oracle.bitlinear(x, nw, packed, N, EPS)) <= 1e-3, (M, K, N)
+        items.append(dict(x=dx, norm_w=dn, packed_w=dp, w_scale=scale, eps=EPS, N=N,
+                          y=torch.full((M, N), float("nan"), device=DEV)))
+        singles.append(y)
+    bl.bitlinear_forward_batched(items)
+    torch.cuda.synchronize()
+    for (M, K, N), it, y in zip(SWEEP, items, singles):
+        assert torch.equal(it["y"], y), (M, K, N)
+    log(f"sweep: {len(SWEEP)} shapes, batched call bit-identical to single calls")
