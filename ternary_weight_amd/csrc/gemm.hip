@@ -54,6 +54,15 @@
 // corner (three VALU operations and one store per element); ragged tiles use
 // a bounds-checked path.
 //
+// Successor prefetch.  A tile's activation rows are first read from HBM by
+// its own direct loads, which then wait behind the output stores that the
+// other workgroups keep the memory system busy with.  So each workgroup, at
+// the start of its epilogue, touches a share of the activation rows of the
+// tile that will most likely take its slot next (workgroup id + 512: two
+// workgroups per CU on 256 CUs, and the ids dealt to the 8 XCDs in turn keep
+// it on this XCD), so that those rows are in the XCD's L2 when that tile
+// starts.  The touches are direct loads into an idle part of the ring.
+//
 // Producer quantization (the PQ instance, one problem per launch): the
 // activation side loads fp32 rows and codes them itself instead of loading
 // int8 codes, see gemm_kernel.
@@ -80,6 +89,10 @@ constexpr int kStageBytes = kXStage + kWStage;
 constexpr int kXLoads = kXStage / 4 / 1024;  // 4
 constexpr int kWLoads = kWStage / 4 / 1024;  // 2
 constexpr int kLoadsPerStage = kXLoads + kWLoads;
+// Successor prefetch: the workgroup that most likely follows on this slot,
+// and how many leading K blocks of its activation rows are touched in all.
+constexpr int kSlotsAhead = 512;
+constexpr int kPrefetchBlocks = 16;
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -147,6 +160,35 @@ __global__ __launch_bounds__(256, PQ ? 1 : 2) void gemm_kernel(ProbSet set) {
   const int n0 = (tile % tiles_n) * kTileN;
   const int kb0 = (K / kBlockK) * split / ks;
   const int nblk = (K / kBlockK) * (split + 1) / ks - kb0;
+
+  // The successor tile's activation rows [pf_m, pf_m + 128) and the K blocks
+  // [pf_b0, pf_b1) this workgroup touches for it.  The successors of one row
+  // block are its consecutive column tiles: successor n of the row block
+  // takes the n-th share of its first kPrefetchBlocks blocks, so each line is
+  // requested once.  Scalar loads, issued here so their latency is long over
+  // by the epilogue.
+  const int8_t* pf_x = nullptr;
+  int pf_k = 0, pf_m = 0, pf_mlast = 0, pf_b0 = 0, pf_b1 = 0;
+  if constexpr (!PQ) {
+    const int b2 = blockIdx.x + kSlotsAhead;
+    if (b2 < set.total) {
+      int local2;
+      const Prob P2 = prob_at(set, find_prob(set, xcd_remap(b2, set.total), &local2));
+      const int ks2 = SPLIT && P2.ksplit > 1 ? P2.ksplit : 1;
+      const int tn2 = (P2.N + kTileN - 1) / kTileN;
+      const int tile2 = local2 / ks2;
+      const int nb = min(kPrefetchBlocks, P2.K / kBlockK);
+      const int n2 = tile2 % tn2, parts = min(tn2, nb);
+      if (local2 % ks2 == 0 && n2 < parts) {
+        pf_x = P2.xq;
+        pf_k = P2.K;
+        pf_m = (tile2 / tn2) * kTileM;
+        pf_mlast = P2.M - 1;
+        pf_b0 = nb * n2 / parts;
+        pf_b1 = nb * (n2 + 1) / parts;
+      }
+    }
+  }
 
   // This lane's direct-load sources (32-bit offsets from the problem's
   // bases): for activation instruction i the lane fills LDS row
@@ -483,6 +525,19 @@ __global__ __launch_bounds__(256, PQ ? 1 : 2) void gemm_kernel(ProbSet set) {
   }
   asm volatile("" ::: "memory");
   __syncthreads();
+  // Successor prefetch, ahead of this tile's stores in the memory pipeline:
+  // per K block 128 rows x 128 bytes, 32 rows of eight 16-byte chunks per
+  // workgroup instruction, into a dummy 1 KB per wave past the row tables.
+  // Being direct loads into LDS, they are awaited before the workgroup ends.
+  if (pf_x) {
+    uint8_t* dummy = smem + 4096 + wave * 1024;
+    for (int b = pf_b0; b < pf_b1; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = min(pf_m + 32 * i + (static_cast<int>(threadIdx.x) >> 3), pf_mlast);
+        dma16(pf_x + m * pf_k + b * kBlockK + (threadIdx.x & 7) * 16, dummy);
+      }
+  }
   if (m0 + kTileM <= M && n0 + kTileN <= N && N <= kGemmFullTileMaxN) {
     // Full tile (the common case): buffer stores against the tile's corner
     // with no bounds checks.  The lane's column (wn*128 + l%32) and row 4g
@@ -516,6 +571,7 @@ __global__ __launch_bounds__(256, PQ ? 1 : 2) void gemm_kernel(ProbSet set) {
           }
         }
       }
+    if (pf_x) wait_vmcnt<0>();
     return;
   }
   const int ncol = n0 + wn * 128 + r32;  // this lane's column in fragment fn = 0
@@ -542,6 +598,7 @@ __global__ __launch_bounds__(256, PQ ? 1 : 2) void gemm_kernel(ProbSet set) {
         }
       }
     }
+  if (pf_x) wait_vmcnt<0>();
 }
 
 int gemm_units(int M, int N) {
