@@ -778,39 +778,45 @@ std::map<QuantKey, StageHost> build_quant_stages(const std::vector<Prob>& probs)
   return out;
 }
 
-// Prefill work order.  Problems are taken in windows of consecutive problems
-// whose packed weights together fit kGemmWindowBytes (a share of one XCD's
-// L2, so the window's weights stay cached while its tiles run); inside a
-// window the problems' tile lists are merged in proportion to their progress,
-// so output-heavy tiles (small K) run beside compute-heavy ones (large K)
-// instead of after them.  Each problem keeps its own tile order.
+// Prefill work order.  Each problem keeps its own tile order (row block
+// major, so a row block's column tiles, which share activation rows, are
+// consecutive).  A launch that runs in successive generations of workgroups
+// (more tiles than two per CU) takes the problems one after another: the
+// kernel's successor prefetch looks one generation ahead in this order.  A
+// launch whose tiles all fit at once merges the tile lists of consecutive
+// problems whose packed weights fit kGemmWindowBytes in proportion to their
+// progress, so that each XCD's share mixes short-K and long-K tiles in the
+// same proportions throughout.  Measured: the plain order is 3% faster on
+// the 196-problem prefill launch and 11% on the Gemma3-270M layer at M =
+// 4096 (it was 2% slower there at M = 512, where every tile fits at once).
 //
-// Then the tiles are dealt to the XCDs.  Consecutive workgroup ids go to the
+// The tiles are then dealt to the XCDs.  Consecutive workgroup ids go to the
 // 8 XCDs in turn, and every XCD receives the same number of workgroups, but
 // tiles of different K take different times: a plain split of the list into
 // 8 contiguous ranges gave a launch of three problems (two at K = 1024, one
 // at K = 3072) XCDs with only the long tiles, which finished last.  So each
-// window's merged sequence is cut into 8 contiguous slices and XCD x takes
-// slice x of every window, in window order: every XCD gets the same mix of
-// tiles, and a slice still holds consecutive tiles of each problem (shared
-// activation rows stay in that XCD's L2).  The kernel reads the table entry
-// xcd_remap(b, total) for workgroup b (XCD b % 8, its (b / 8)-th workgroup),
-// so XCD x's k-th tile is stored at entry x*q + min(x, r) + k.
+// sequence (a problem, or a merged window) is cut into 8 contiguous slices
+// and XCD x takes slice x of every sequence, in order: every XCD gets the
+// same mix of tiles, and a slice still holds consecutive tiles of each
+// problem (shared activation rows and weights stay in that XCD's L2).  The
+// kernel reads the table entry xcd_remap(b, total) for workgroup b (XCD
+// b % 8, its (b / 8)-th workgroup), so XCD x's k-th tile is stored at entry
+// x*q + min(x, r) + k.
 constexpr size_t kGemmWindowBytes = size_t{2} << 20;
 constexpr int kXcds = 8;
 
-void interleave_gemm_units(StageHost& h) {
+void deal_gemm_units(StageHost& h, int cus) {
   if (h.units.empty()) return;
   std::vector<int> tiles(h.probs.size(), 0);
   for (const int2& u : h.units) ++tiles[u.x];
-  std::vector<std::vector<int2>> windows;
+  const bool fits = cus > 0 && h.units.size() <= static_cast<size_t>(2 * cus);
+  std::vector<std::vector<int2>> seqs;
   size_t p0 = 0;
   while (p0 < h.probs.size()) {
-    size_t p1 = p0, bytes = 0;
-    while (p1 < h.probs.size()) {
-      const Prob& q = h.probs[p1];
-      const size_t wb = static_cast<size_t>(q.N) * static_cast<size_t>(q.K / 4);
-      if (p1 > p0 && bytes + wb > kGemmWindowBytes) break;
+    size_t p1 = p0 + 1, bytes = static_cast<size_t>(h.probs[p0].N) * static_cast<size_t>(h.probs[p0].K / 4);
+    while (fits && p1 < h.probs.size()) {
+      const size_t wb = static_cast<size_t>(h.probs[p1].N) * static_cast<size_t>(h.probs[p1].K / 4);
+      if (bytes + wb > kGemmWindowBytes) break;
       bytes += wb;
       ++p1;
     }
@@ -833,12 +839,12 @@ void interleave_gemm_units(StageHost& h) {
       if (best < 0) break;
       seq.push_back(int2{static_cast<int>(p0) + best, next[best]++});
     }
-    windows.push_back(std::move(seq));
+    seqs.push_back(std::move(seq));
     p0 = p1;
   }
-  // Deal: slice x of every window to XCD x.
+  // Deal: slice x of every sequence to XCD x.
   std::vector<std::vector<int2>> xcd(kXcds);
-  for (const auto& seq : windows) {
+  for (const auto& seq : seqs) {
     const size_t L = seq.size();
     for (int x = 0; x < kXcds; ++x)
       xcd[x].insert(xcd[x].end(), seq.begin() + L * x / kXcds, seq.begin() + L * (x + 1) / kXcds);
@@ -1068,7 +1074,7 @@ void plan_build(const bl_desc* descs, int32_t count, int cus, uint8_t* ws, Plan&
     auto it = pl.hv.find({0, true, false});
     if (it != pl.hv.end()) order_merged_units(it->second.fat_units);
   }
-  interleave_gemm_units(pl.hm);
+  deal_gemm_units(pl.hm, cus);
 
   // Table image, stage order: prefill, quantization stages, decode stages.
   std::vector<const StageHost*> hosts{&pl.hm};
