@@ -747,6 +747,12 @@ def measure_peaks(torch, bl):
     for rd in (64, 16):
         moved = msrc.numel() * (1 + 1 / rd)
         mixed[rd] = max(moved / timed(lambda: bl.probe_mixed(msrc, mdst, rd, sink, b)) / 1e9 for b in (1024, 2048))
+    # one write per 4, 2 or 1 reads (20%, 33%, 50% of the bytes written): the
+    # quantization launches' mixes (fp32 rows in, int8 codes out: 20-43%)
+    msrc, mdst = buf[: nbytes // 4], buf[nbytes // 2: 3 * nbytes // 4]
+    for rd in (4, 2, 1):
+        moved = msrc.numel() * (1 + 1 / rd)
+        mixed[rd] = max(moved / timed(lambda: bl.probe_mixed(msrc, mdst, rd, sink, b)) / 1e9 for b in (1024, 2048))
     del buf, src, dst, msrc, mdst
     # Launch floor: back-to-back launches of a one-workgroup kernel that
     # writes 16 bytes (what any launch costs on this stream).
@@ -771,8 +777,7 @@ def measure_peaks(torch, bl):
             "copy_GBps_read_plus_write": round(copy, 1),
             "hbm_write_GBps": round(max(write.values()), 1),
             "hbm_write_by_kind": {"plain": round(write[False], 1), "nontemporal": round(write[True], 1)},
-            "hbm_mixed_GBps": {"1_write_per_64_reads": round(mixed[64], 1),
-                               "1_write_per_16_reads": round(mixed[16], 1)},
+            "hbm_mixed_GBps": {f"1_write_per_{rd}_reads": round(mixed[rd], 1) for rd in (64, 16, 4, 2, 1)},
             "launch_floor_us": round(floor_us, 2),
             "mfma_i8_TOPS": round(max(mfma.values()), 1),
             "mfma_i8_TOPS_by_shape": {f"{k}x{k}": round(v, 1) for k, v in mfma.items()}}

@@ -38,8 +38,9 @@ bl_status bl_probe_write(void* dst, size_t bytes, int32_t blocks, int32_t nontem
  * 16-byte word of src once (non-temporal) and, per 256 * reads_per_write
  * words read, write 256 words of dst (non-temporal, values independent of
  * the reads): src_bytes / reads_per_write bytes written in all.
- * reads_per_write is 16 or 64 (a write share of 6% or 1.5% of the bytes,
- * near a decode launch's output share); src_bytes is a nonzero multiple of
+ * reads_per_write is 1, 2, 4, 16 or 64: a write share of 50%, 33%, 20%, 6%
+ * or 1.5% of the bytes (the quantization launches write 20-43% of theirs,
+ * a decode launch about 1.2%); src_bytes is a nonzero multiple of
  * 4096 * reads_per_write, dst holds at least src_bytes / reads_per_write
  * bytes, both 16-byte aligned.  sink: as for bl_probe_read. */
 bl_status bl_probe_mixed(const void* src, size_t src_bytes, void* dst, size_t dst_bytes,

@@ -151,7 +151,10 @@ bl_status bl_probe_write(void* dst, size_t bytes, int32_t blocks, int32_t nontem
 
 bl_status bl_probe_mixed(const void* src, size_t src_bytes, void* dst, size_t dst_bytes,
                          int32_t reads_per_write, uint32_t* sink, int32_t blocks, void* stream) {
-  if (!src || !dst || !sink || blocks <= 0 || (reads_per_write != 16 && reads_per_write != 64))
+  if (!src || !dst || !sink || blocks <= 0)
+    return BL_ERR_INVALID_ARGUMENT;
+  if (reads_per_write != 1 && reads_per_write != 2 && reads_per_write != 4 && reads_per_write != 16 &&
+      reads_per_write != 64)
     return BL_ERR_INVALID_ARGUMENT;
   const size_t unit = static_cast<size_t>(16) * 256 * static_cast<size_t>(reads_per_write);
   if (src_bytes == 0 || src_bytes % unit != 0 || dst_bytes < src_bytes / static_cast<size_t>(reads_per_write))
@@ -159,12 +162,16 @@ bl_status bl_probe_mixed(const void* src, size_t src_bytes, void* dst, size_t ds
   if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0)
     return BL_ERR_MISALIGNED;
   const int64_t units = static_cast<int64_t>(src_bytes / unit);
-  if (reads_per_write == 16)
-    hipLaunchKernelGGL(bl::probe_mixed_kernel<16>, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const bl::v4i*>(src), static_cast<bl::v4i*>(dst), units, sink);
-  else
-    hipLaunchKernelGGL(bl::probe_mixed_kernel<64>, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const bl::v4i*>(src), static_cast<bl::v4i*>(dst), units, sink);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bl::v4i* in = static_cast<const bl::v4i*>(src);
+  bl::v4i* out = static_cast<bl::v4i*>(dst);
+  switch (reads_per_write) {
+    case 1: hipLaunchKernelGGL(bl::probe_mixed_kernel<1>, dim3(blocks), dim3(256), 0, s, in, out, units, sink); break;
+    case 2: hipLaunchKernelGGL(bl::probe_mixed_kernel<2>, dim3(blocks), dim3(256), 0, s, in, out, units, sink); break;
+    case 4: hipLaunchKernelGGL(bl::probe_mixed_kernel<4>, dim3(blocks), dim3(256), 0, s, in, out, units, sink); break;
+    case 16: hipLaunchKernelGGL(bl::probe_mixed_kernel<16>, dim3(blocks), dim3(256), 0, s, in, out, units, sink); break;
+    default: hipLaunchKernelGGL(bl::probe_mixed_kernel<64>, dim3(blocks), dim3(256), 0, s, in, out, units, sink); break;
+  }
   return bl::hip_status(hipGetLastError());
 }
 

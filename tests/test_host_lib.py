@@ -208,6 +208,8 @@ def test_probe_validation():
     U = 4096 * 16
     assert lib.bl_probe_mixed(None, U, A, U, 16, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT
     assert lib.bl_probe_mixed(A, U, A, U, 8, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT   # ratio
+    assert lib.bl_probe_mixed(A, U, A, U, 3, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT   # ratio
+    assert lib.bl_probe_mixed(A, U, A, U - 16, 1, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT  # dst short
     assert lib.bl_probe_mixed(A, U + 16, A, U, 16, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT  # not whole units
     assert lib.bl_probe_mixed(A, U, A, U // 16 - 16, 16, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT  # dst short
     assert lib.bl_probe_mixed(A, 0, A, U, 16, A, 1, None) == bl.BL_ERR_INVALID_ARGUMENT
