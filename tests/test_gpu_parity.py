@@ -1395,3 +1395,41 @@ def test_random_shape_sweep():
     for (M, K, N), it, y in zip(SWEEP, items, singles):
         assert torch.equal(it["y"], y), (M, K, N)
     log(f"sweep: {len(SWEEP)} shapes, batched call bit-identical to single calls")
+
+
+def test_prefill_group_many_generations():
+    # A prefill launch with more tiles than fit on the GPU at once (here 735
+    # tiles of mixed K, ragged M and N, against 512 resident workgroups): a
+    # workgroup whose successor exists then also touches that tile's
+    # activation rows before it stores.  The outputs must equal the single
+    # calls (launches of at most 96 tiles, which fit at once) bit for bit over
+    # two forwards into NaN-filled outputs, and the oracle on sampled rows.
+    specs = [(1000, 3200, 3000), (700, 640, 2900), (1000, 128, 3072), (300, 4096, 1000),
+             (1000, 2176, 2600), (129, 1152, 257), (1000, 1024, 3072), (513, 3072, 1024),
+             (1000, 2048, 2048), (900, 384, 3000), (1000, 1152, 2816), (257, 640, 33)]
+    tiles = sum(-(-M // 128) * -(-N // 256) for M, K, N in specs)
+    assert tiles > 2 * 256
+    items, refs = [], []
+    for i, (M, K, N) in enumerate(specs):
+        x, nw, packed, scale = proj_inputs(44, i, 0, M, K, N, heavy=(i % 3 == 1))
+        it = dict(x=dev(x), norm_w=dev(nw), packed_w=dev(packed), w_scale=scale, eps=EPS, N=N,
+                  y=torch.full((M, N), float("nan"), device=DEV))
+        items.append(it)
+        refs.append((x, nw, packed))
+    singles = [bl.bitlinear_forward(it["x"], it["norm_w"], it["packed_w"], it["w_scale"], it["N"], EPS)
+               for it in items]
+    with bl.Group(items) as g:
+        assert [d["kind"] for d in g.forward_launches()][-1] == "prefill"
+        for rep in range(2):
+            for it in items:
+                it["y"].fill_(float("nan"))
+            g.forward()
+            torch.cuda.synchronize()
+            for (M, K, N), it, ys in zip(specs, items, singles):
+                assert torch.equal(it["y"], ys), (rep, M, K, N)
+    log(f"prefill group of {len(specs)} problems, {tiles} tiles: identical to single calls")
+    for i in (0, 3, 7, 11):
+        (M, K, N), (x, nw, packed) = specs[i], refs[i]
+        rows = inputs.sample_rows(M, 8, seed=44 + i)
+        ref = oracle.bitlinear(np.ascontiguousarray(x[rows]), nw, packed, N, EPS)
+        assert rel_l2(host(singles[i])[rows], ref) <= 1e-3, (M, K, N)
